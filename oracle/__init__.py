@@ -1,0 +1,39 @@
+"""CPU oracle for sparse MLA forward over fp8_ds_mla records (fp64, NumPy).
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+link this package: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code, table or
+constant generator with the HIP library; both sides read the same bytes made
+by ``synth`` and decode them independently.
+
+Sources (cited by page title and section, never by line):
+  [FlyDSL page]  vLLM API page "vllm.models.kimi_k3.amd.ops.flydsl_sparse_mla_gfx950"
+                 (FlyDSL sparse MLA forward over fp8_ds_mla records, gfx950):
+                 module docstring (record layout, masking rules, tiles),
+                 section "Preconditions the host cannot check", and the kernel
+                 epilogue of ``build_sparse_mla_fp8ds_module`` (natural-log LSE,
+                 empty rows).
+  [K2-back page] vLLM API page "vllm.models.deepseek_v41.amd.mono.attention.back":
+                 module docstring (split / combine stages) and ``stage_combine``
+                 (merge of chunk partials by their max and sum).
+  [OCP FP8]      OCP 8-bit floating point specification, E4M3 encoding
+                 (the format the FlyDSL page's writer rule with its 448 bound
+                 implies).
+
+Every function is pinned by CPU tests in ``tests/test_oracle.py`` against
+closed forms, library routines, brute force or invariants; no oracle function
+is "parity unpinned".
+"""
+
+from .codec import (  # noqa: F401
+    E4M3_TABLE,
+    e4m3_value,
+    bf16_bits_to_f64,
+    decode_records,
+    RECORD_BYTES,
+)
+from .attention import (  # noqa: F401
+    row_attention,
+    sparse_mla_fwd,
+    lse_merge,
+)

@@ -1,0 +1,384 @@
+"""Pins for the CPU oracle (no GPU).
+
+Each pin ties the oracle to something other than itself: the OCP E4M3 table
+and torch's float8/bfloat16 casts (library), hand-decoded records, the
+FlyDSL page's writer bound, pure-Python brute force on tiny inputs, torch's
+scaled_dot_product_attention on the dense special case, and closed-form
+invariants.  ``test_planted_mistakes`` plants plausible errors in the oracle
+(on the CPU) and checks that some pin catches every one of them.
+"""
+
+import math
+import struct
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import oracle.attention as oatt
+import oracle.codec as ocodec
+import synth
+
+SIGMA = float(np.float32(1.0 / math.sqrt(576)))
+
+
+# ----------------------------------------------------------------- helpers
+
+def random_records(rng, n, scale_exp=(-22, 7)):
+    """Random but valid records: any non-NaN e4m3 code, pow2 scales, finite bf16 rope."""
+    rec = np.zeros((n, 656), np.uint8)
+    codes = rng.integers(0, 256, size=(n, 512))
+    codes[(codes & 0x7F) == 0x7F] = 0x38
+    rec[:, :512] = codes
+    e = rng.integers(scale_exp[0], scale_exp[1] + 1, size=(n, 4))
+    rec[:, 512:528] = np.ldexp(1.0, e).astype("<f4").view(np.uint8).reshape(n, 16)
+    rope = rng.standard_normal((n, 64)).astype(np.float32)
+    rec[:, 528:] = torch.from_numpy(rope).to(torch.bfloat16).view(torch.int16).numpy() \
+        .view(np.uint8).reshape(n, 128)
+    return rec
+
+
+def random_q(rng, T, H, std=1.0):
+    x = torch.from_numpy(rng.standard_normal((T, H, 576)) * std).to(torch.bfloat16)
+    return x.view(torch.int16).numpy().view(np.uint16)
+
+
+def torch_decode(rec):
+    """Independent record decode through torch's own float8 / bfloat16 casts."""
+    rec = np.ascontiguousarray(rec)
+    n = rec.shape[0]
+    lat = torch.from_numpy(rec[:, :512].copy()).view(torch.float8_e4m3fn).double().numpy()
+    sc = np.frombuffer(rec[:, 512:528].tobytes(), dtype="<f4").reshape(n, 4).astype(np.float64)
+    rope = torch.from_numpy(rec[:, 528:].copy()).view(torch.bfloat16).double().numpy()
+    return np.concatenate([lat * np.repeat(sc, 128, axis=1), rope], axis=1)
+
+
+def torch_q(q_bits):
+    return torch.from_numpy(np.ascontiguousarray(q_bits).view(np.int16)).view(torch.bfloat16).double().numpy()
+
+
+def brute_force(q_bits, kv, indptr, indices, sigma):
+    """Pure-Python loops (math.fsum / math.exp) over torch-decoded inputs."""
+    T, H, _ = q_bits.shape
+    Q = torch_q(q_bits)
+    out = np.zeros((T, H, 512))
+    lse = np.full((T, H), -np.inf)
+    for r in range(T):
+        keys = [int(i) for i in indices[indptr[r]:indptr[r + 1]] if i >= 0] \
+            if indptr[r + 1] > indptr[r] else []
+        if not keys:
+            continue
+        K = torch_decode(kv[keys])
+        for h in range(H):
+            s = [sigma * math.fsum(float(a) * float(b) for a, b in zip(Q[r, h], K[j]))
+                 for j in range(len(keys))]
+            m = max(s)
+            p = [math.exp(x - m) for x in s]
+            l = math.fsum(p)
+            for d in range(512):
+                out[r, h, d] = math.fsum(p[j] * K[j, d] for j in range(len(keys))) / l
+            lse[r, h] = m + math.log(l)
+    return out, lse
+
+
+def tiny_case(seed):
+    rng = np.random.default_rng(seed)
+    T = int(rng.integers(1, 5))
+    H = int(rng.integers(1, 4))
+    N = int(rng.integers(1, 17))
+    kv = random_records(rng, N)
+    q = random_q(rng, T, H, std=float(rng.choice([0.5, 1.0, 3.0])))
+    slices = []
+    for _ in range(T):
+        L = int(rng.integers(0, 11))
+        s = rng.integers(-1, N, size=L)  # -1 entries and duplicates allowed
+        slices.append(s)
+    indptr = np.zeros(T + 1, np.int64)
+    indptr[1:] = np.cumsum([s.size for s in slices])
+    idx = np.concatenate(slices).astype(np.int64) if slices else np.zeros(0, np.int64)
+    return q, kv, indptr, idx
+
+
+def assert_close(a, b, tol):
+    a, b = np.asarray(a), np.asarray(b)
+    fin = np.isfinite(b)
+    assert np.array_equal(np.isfinite(a), fin)
+    assert np.array_equal(a[~fin], b[~fin])
+    if fin.any():
+        assert np.max(np.abs(a[fin] - b[fin])) <= tol * max(1.0, np.max(np.abs(b[fin])))
+
+
+# ----------------------------------------------------------------- codec pins
+
+def test_e4m3_table_matches_torch():
+    want = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    got = ocodec.E4M3_TABLE
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert nan.sum() == 2
+    assert np.array_equal(got[~nan], want[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(want[~nan]))
+
+
+def test_e4m3_spec_points(golden):
+    for code, val in golden("e4m3_points.txt"):
+        c = int(code, 16)
+        v = float(val)
+        got = ocodec.e4m3_value(c)
+        if math.isnan(v):
+            assert math.isnan(got)
+        else:
+            assert got == v and math.copysign(1, got) == math.copysign(1, v), (code, got, v)
+
+
+def test_bf16_decode_all_patterns():
+    bits = np.arange(65536, dtype=np.uint32)
+    got = ocodec.bf16_bits_to_f64(bits)
+    want = torch.from_numpy(bits.astype(np.uint16).view(np.int16)).view(torch.bfloat16).double().numpy()
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], want[~nan])
+
+
+def test_handbuilt_record(golden):
+    rec = np.zeros((1, 656), np.uint8)
+    rec[0, 512:528] = np.frombuffer(struct.pack("<4f", 2.0 ** -3, 2.0 ** 5, 1.0, 4.0), np.uint8)
+    want = {}
+    for pos, byte, blk, val in golden("handbuilt_record.txt"):
+        pos, b = int(pos), int(byte, 16)
+        if blk == "rope":
+            off = 528 + 2 * (pos - 512)
+            rec[0, off], rec[0, off + 1] = b & 0xFF, b >> 8
+        else:
+            assert int(blk) == pos // 128
+            rec[0, pos] = b
+        want[pos] = float(val)
+    K = oracle.decode_records(rec)[0]
+    for pos, val in want.items():
+        assert K[pos] == val, (pos, K[pos], val)
+    zero = [i for i in range(576) if i not in want]
+    assert np.all(K[zero] == 0.0)
+
+
+def test_record_decode_matches_torch():
+    rec = random_records(np.random.default_rng(1), 64)
+    assert np.array_equal(oracle.decode_records(rec), torch_decode(rec))
+
+
+def test_writer_bound(golden):
+    """The generator's writer meets the page's bound: scale 2^7 iff |latent| <= 57344."""
+    for amax, scale in golden("writer_bound.txt"):
+        amax, scale = float(amax), float(scale)
+        lat = torch.zeros(1, 512)
+        lat[0, :128] = amax
+        rec = synth.encode_records(lat, torch.zeros(1, 64)).numpy()
+        K = oracle.decode_records(rec)[0]
+        assert np.frombuffer(rec[0, 512:516].tobytes(), "<f4")[0] == scale
+        assert K[0] == amax  # exactly representable at that scale
+    lat = torch.zeros(1, 512)
+    lat[0, 0] = 57345.0
+    rec = synth.encode_records(lat, torch.zeros(1, 64)).numpy()
+    assert np.frombuffer(rec[0, 512:516].tobytes(), "<f4")[0] == 256.0
+
+
+# ----------------------------------------------------------------- attention pins
+
+@pytest.mark.parametrize("seed", range(12))
+def test_bruteforce_tiny(seed):
+    q, kv, ip, ix = tiny_case(seed)
+    out, lse = oracle.sparse_mla_fwd(q, kv, ip, ix, SIGMA)
+    bo, bl = brute_force(q, kv, ip, ix, SIGMA)
+    assert_close(out, bo, 1e-12)
+    assert_close(lse, bl, 1e-12)
+
+
+def test_dense_case_matches_sdpa():
+    """Every row attends to every record: multi-query attention, one KV head."""
+    rng = np.random.default_rng(7)
+    T, H, N = 3, 5, 40
+    kv = random_records(rng, N, scale_exp=(-8, 0))
+    q = random_q(rng, T, H, std=2.0)
+    ip = np.arange(T + 1) * N
+    ix = np.tile(np.arange(N), T)
+    out, lse = oracle.sparse_mla_fwd(q, kv, ip, ix, SIGMA)
+    K = torch.from_numpy(torch_decode(kv))
+    Q = torch.from_numpy(torch_q(q))
+    qq = Q[:, :, None, :]
+    kk = K[None, None].expand(T, H, N, 576)
+    vv = K[None, None, :, :512].expand(T, H, N, 512)
+    ref = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv, scale=SIGMA)[:, :, 0]
+    scores = torch.matmul(Q, K.T) * SIGMA
+    assert np.max(np.abs(out - ref.numpy())) <= 1e-10
+    assert np.max(np.abs(lse - torch.logsumexp(scores, dim=-1).numpy())) <= 1e-10
+
+
+def test_single_index_returns_row():
+    rng = np.random.default_rng(3)
+    kv = random_records(rng, 9)
+    q = random_q(rng, 9, 4)
+    ip = np.arange(10)
+    ix = np.arange(9)[::-1].copy()
+    out, lse = oracle.sparse_mla_fwd(q, kv, ip, ix, SIGMA)
+    K = torch_decode(kv)
+    Q = torch_q(q)
+    for r in range(9):
+        k = K[ix[r]]
+        assert np.array_equal(out[r], np.broadcast_to(k[:512], (4, 512)))
+        for h in range(4):
+            want = SIGMA * math.fsum(float(a) * float(b) for a, b in zip(Q[r, h], k))
+            assert abs(lse[r, h] - want) <= 1e-12 * max(1.0, abs(want))
+
+
+def test_equal_scores_give_mean():
+    rng = np.random.default_rng(4)
+    kv = random_records(rng, 30)
+    q = np.zeros((1, 2, 576), np.uint16)  # q = 0: every score is 0
+    ix = rng.integers(0, 30, size=17)
+    out, lse = oracle.sparse_mla_fwd(q, kv, [0, 17], ix, SIGMA)
+    mean = torch_decode(kv[ix])[:, :512].mean(axis=0)
+    assert np.max(np.abs(out[0] - mean)) <= 1e-12 * max(1, np.abs(mean).max())
+    assert np.allclose(lse, math.log(17), rtol=0, atol=1e-14)
+
+
+def test_permutation_invariance():
+    q, kv, ip, ix = tiny_case(100)
+    rng = np.random.default_rng(5)
+    ix2 = ix.copy()
+    for r in range(len(ip) - 1):
+        b, e = ip[r], ip[r + 1]
+        ix2[b:e] = rng.permutation(ix[b:e])
+    o1, l1 = oracle.sparse_mla_fwd(q, kv, ip, ix, SIGMA)
+    o2, l2 = oracle.sparse_mla_fwd(q, kv, ip, ix2, SIGMA)
+    assert_close(o2, o1, 1e-12)
+    assert_close(l2, l1, 1e-12)
+
+
+def test_negative_entries_ignored():
+    rng = np.random.default_rng(6)
+    kv = random_records(rng, 12)
+    q = random_q(rng, 1, 3)
+    base = np.array([3, 7, 0, 11, 5])
+    withneg = np.array([-1, 3, -1, -1, 7, 0, -7, 11, 5, -1])
+    o1, l1 = oracle.sparse_mla_fwd(q, kv, [0, 5], base, SIGMA)
+    o2, l2 = oracle.sparse_mla_fwd(q, kv, [0, 10], withneg, SIGMA)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_duplicates_raise_lse_by_ln2():
+    rng = np.random.default_rng(8)
+    kv = random_records(rng, 12)
+    q = random_q(rng, 1, 3)
+    base = np.array([3, 7, 0, 11, 5])
+    o1, l1 = oracle.sparse_mla_fwd(q, kv, [0, 5], base, SIGMA)
+    o2, l2 = oracle.sparse_mla_fwd(q, kv, [0, 10], np.repeat(base, 2), SIGMA)
+    assert np.max(np.abs(o1 - o2)) <= 1e-12 * max(1, np.abs(o1).max())
+    assert np.max(np.abs(l2 - (l1 + math.log(2)))) <= 1e-12
+
+
+def test_empty_rows():
+    rng = np.random.default_rng(9)
+    kv = random_records(rng, 4)
+    q = random_q(rng, 4, 2)
+    ip = np.array([0, 0, 3, 1, 4])  # row0 empty, row1 all -1, row2 negative length
+    ix = np.array([-1, -1, -1, 2])
+    out, lse = oracle.sparse_mla_fwd(q, kv, ip, ix, SIGMA)
+    assert np.all(out[:3] == 0.0) and np.all(np.isneginf(lse[:3]))
+    assert np.all(np.isfinite(lse[3]))
+
+
+def test_index_out_of_range_raises():
+    rng = np.random.default_rng(10)
+    kv = random_records(rng, 4)
+    with pytest.raises(IndexError):
+        oracle.sparse_mla_fwd(random_q(rng, 1, 1), kv, [0, 2], [1, 4], SIGMA)
+
+
+def test_lse_merge_equals_unsplit():
+    rng = np.random.default_rng(11)
+    kv = random_records(rng, 50, scale_exp=(-8, 2))
+    q = random_q(rng, 1, 4, std=2.0)
+    ix = rng.integers(-1, 50, size=37)
+    whole = oracle.sparse_mla_fwd(q, kv, [0, 37], ix, SIGMA)
+    for cuts in ([10, 20], [1, 2, 3, 36], [0, 0, 37], [5]):
+        edges = [0] + list(cuts) + [37]
+        parts = [oracle.sparse_mla_fwd(q, kv, [0, e - b], ix[b:e], SIGMA)
+                 for b, e in zip(edges[:-1], edges[1:])]
+        out, lse = oracle.lse_merge([(o[0], s[0]) for o, s in parts])
+        assert np.max(np.abs(out - whole[0][0])) <= 1e-12 * max(1, np.abs(whole[0]).max())
+        assert np.max(np.abs(lse - whole[1][0])) <= 1e-12
+
+
+def test_lse_merge_all_empty():
+    out, lse = oracle.lse_merge([(np.full((2, 512), np.nan), np.full(2, -np.inf))] * 3)
+    assert np.all(out == 0) and np.all(np.isneginf(lse))
+
+
+# ----------------------------------------------------------------- planted mistakes
+
+def _pins_pass():
+    """Run the attention pins; return the names of those that fail."""
+    failed = []
+    checks = [
+        ("bruteforce", lambda: [test_bruteforce_tiny(s) for s in (0, 3, 5)]),
+        ("sdpa", test_dense_case_matches_sdpa),
+        ("single", test_single_index_returns_row),
+        ("mean", test_equal_scores_give_mean),
+        ("negative", test_negative_entries_ignored),
+        ("dups", test_duplicates_raise_lse_by_ln2),
+        ("empty", test_empty_rows),
+        ("merge", test_lse_merge_equals_unsplit),
+    ]
+    for name, fn in checks:
+        try:
+            fn()
+        except Exception:  # noqa: BLE001 - any failure counts as caught
+            failed.append(name)
+    return failed
+
+
+def _mut_decode(fn):
+    real = ocodec.decode_records
+
+    def wrapped(rec):
+        return fn(real(rec), rec)
+    return wrapped
+
+
+def _row_attention_variant(kind):
+    def f(Q, K, sigma):
+        H = Q.shape[0]
+        if K.shape[0] == 0:
+            return np.zeros((H, 512)), np.full(H, -np.inf)
+        s = (Q @ K.T) * (1.0 if kind == "no_sigma" else sigma)
+        m = s.max(axis=1, keepdims=True)
+        p = np.exp(m - s) if kind == "sign" else np.exp(s - m)
+        l = p.sum(axis=1)
+        V = K[::-1, :512] if kind == "transposed_v" else K[:, :512]
+        out = (p @ V) / l[:, None]
+        lse = m[:, 0] + (np.log2(l) if kind == "log2" else np.log(l))
+        return out, lse
+    return f
+
+
+MUTANTS = {
+    "rope_dropped": ("decode_records", _mut_decode(lambda K, rec: np.concatenate(
+        [K[:, :512], np.zeros_like(K[:, 512:])], axis=1))),
+    "scale_block_shift": ("decode_records", _mut_decode(lambda K, rec: np.concatenate(
+        [K[:, :128], 2 * K[:, 128:256], K[:, 256:]], axis=1))),
+    "no_sigma": ("row_attention", _row_attention_variant("no_sigma")),
+    "sign": ("row_attention", _row_attention_variant("sign")),
+    "log2_lse": ("row_attention", _row_attention_variant("log2")),
+    "transposed_v": ("row_attention", _row_attention_variant("transposed_v")),
+    "negatives_kept": ("_row_keys", lambda kv, sl: ocodec.decode_records(kv[sl])),
+}
+
+
+@pytest.mark.filterwarnings("ignore::RuntimeWarning")
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistakes(monkeypatch, name):
+    assert _pins_pass() == []
+    attr, fn = MUTANTS[name]
+    monkeypatch.setattr(oatt, attr, fn)
+    failed = _pins_pass()
+    assert failed, f"planted mistake {name!r} went unnoticed by every pin"
