@@ -1,0 +1,163 @@
+/*
+ * smla.h -- C ABI of the sparse MLA forward library (libsmla.so) for MI355X
+ * (gfx950, CDNA4).
+ *
+ * The operation (vLLM API page "vllm.models.kimi_k3.amd.ops.flydsl_sparse_mla_gfx950",
+ * module docstring and the epilogue of build_sparse_mla_fp8ds_module): for each
+ * query row r and head h, softmax attention of q[r, h, 0:576] over the KV
+ * records listed in the row's CSR slice indices[indptr[r] .. indptr[r+1]),
+ * where a record is decoded to K (576 values) and V (its first 512), logits are
+ * scaled by sm_scale, out[r, h, 0:512] is the attention output and lse[r, h] the
+ * natural-log log-sum-exp of the scaled logits.
+ *
+ * KV record, 656 bytes (same page, module docstring, "Record (656 B)"):
+ *   bytes   0..511  512 e4m3 (OCP E4M3FN) latent codes
+ *   bytes 512..527  4 little-endian f32 power-of-two scales; scale b applies to
+ *                   latent values 128b .. 128b+127
+ *   bytes 528..655  64 bf16 rope values
+ *   K = [latent * scale, rope], V = latent * scale.
+ *
+ * Conventions for every entry point:
+ *   - Pointers marked "device" are device memory the caller owns and keeps
+ *     alive until the work queued on `stream` has finished; the library never
+ *     frees or retains them.  `stream` is a hipStream_t (NULL = the null
+ *     stream).  Work is queued asynchronously; no entry point synchronises
+ *     the host unless stated.
+ *   - Every entry point returns SMLA_OK (0) or a negative smla_status.  On a
+ *     negative status nothing was queued, and sparse_mla_last_error() returns
+ *     a message for the calling thread.
+ *   - Element strides are in elements of the tensor's own type.
+ */
+#ifndef SMLA_H
+#define SMLA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SMLA_OK = 0,
+  SMLA_EINVAL = -1,          /* malformed argument (null pointer, negative size, alignment, overflow) */
+  SMLA_EUNSUPPORTED = -2,    /* well formed but outside what the kernels implement (e.g. heads > 64) */
+  SMLA_EWORKSPACE = -3,      /* workspace missing or smaller than sparse_mla_workspace_bytes() */
+  SMLA_EHIP = -4             /* a HIP runtime call failed; the message carries hipGetErrorString */
+} smla_status;
+
+/* Largest head count the kernels implement (they tile heads by 16). */
+#define SMLA_MAX_HEADS 64
+
+/*
+ * sparse_mla_supported -- 1 if a forward with `num_heads` heads is implemented,
+ * else 0.  The FlyDSL page rejects head counts outside [1, 16]
+ * (build_sparse_mla_fp8ds_module); this library accepts [1, SMLA_MAX_HEADS].
+ */
+int sparse_mla_supported(int32_t num_heads);
+
+/*
+ * sparse_mla_workspace_bytes -- device workspace a forward of T query rows,
+ * H heads and nnz CSR entries needs on the current device (per-row plan,
+ * longest-first order and, when rows are split, chunk partials).  Returns
+ * the byte count (>= 256), or a negative smla_status for invalid arguments.
+ * The first 256 bytes hold a ticket counter that must be zero the first time
+ * a workspace is used (e.g. hipMemset once); every completed forward leaves it
+ * zero again.  A workspace must not be shared by forwards that may run
+ * concurrently.
+ */
+int64_t sparse_mla_workspace_bytes(int32_t T, int32_t H, int64_t nnz);
+
+/*
+ * sparse_mla_fwd -- sparse MLA forward over fp8_ds_mla records.
+ *
+ *   q          device, bf16 [T, H, 576]: element (r, h, d) at
+ *              q + r*q_stride_t + h*q_stride_h + d.  Dims 0..511 meet the
+ *              latent, 512..575 the rope.  16-byte aligned, strides multiples of 8.
+ *   kv         device, uint8 [n_kv, 656], rows contiguous, 16-byte aligned.
+ *              Rows are addressed with 64-bit offsets, so the cache may exceed
+ *              4 GiB.  Not bounds-checked (see preconditions).
+ *   indptr     device, int32 [T + 1].  Row r's slice is
+ *              indices[indptr[r] .. indptr[r+1]); a negative length is empty.
+ *   indices    device, int32 [nnz] (may be NULL when nnz == 0).  Entries < 0
+ *              mean "no key" and are ignored whatever has_invalid says.
+ *              Index reads are bounded by nnz: a malformed indptr cannot read
+ *              past the buffer (such positions read as index 0).
+ *   sm_scale   logit scale (e.g. 1/sqrt(576)).
+ *   has_invalid  nonzero: the caller pads slices with trailing entries < 0;
+ *              tiles after the last entry >= 0 of a row are skipped (found by a
+ *              scan of the slice).  Zero: every slice position is scheduled.
+ *              The result is the same either way.
+ *   out        device, bf16 [T, H, 512] at out + r*o_stride_t + h*o_stride_h + d;
+ *              16-byte aligned, strides multiples of 8.
+ *   lse        device, f32 [T, H] contiguous, or NULL to skip it.  Natural log;
+ *              -inf for a row with no key (whose out is all zero).
+ *   workspace  device, >= sparse_mla_workspace_bytes(T, H, nnz) bytes,
+ *              256-byte aligned, ticket zero (see above).
+ *
+ * Preconditions the library cannot check (undefined results if broken, as on
+ * the FlyDSL page, section "Preconditions the host cannot check"):
+ *   - every per-128 scale is a positive power of two: the QK stage applies
+ *     only the scale's exponent field (a mantissa or sign is dropped, and a
+ *     zero scale acts as 2^-127, i.e. as a zero latent in practice), while the
+ *     P.V stage uses the stored value;
+ *   - every per-128 scale is <= 2^7: a larger one is clamped to 2^7 in the P.V
+ *     product, which keeps the output finite but inexact;
+ *   - every consumed index i satisfies 0 <= i < n_kv;
+ *   - indptr is non-decreasing within [0, nnz] (violations are memory-safe but
+ *     give unspecified rows).
+ *
+ * Returns SMLA_OK, or SMLA_EINVAL / SMLA_EUNSUPPORTED / SMLA_EWORKSPACE /
+ * SMLA_EHIP with nothing queued.  Queues 2 or 3 kernels on `stream`
+ * (plan, forward, and a combine when rows are split), no host sync, no
+ * allocation.  Deterministic for a fixed device and arguments.
+ */
+int sparse_mla_fwd(const void* q, int64_t q_stride_t, int64_t q_stride_h,
+                   const void* kv, int64_t n_kv,
+                   const int32_t* indptr, const int32_t* indices, int64_t nnz,
+                   int32_t T, int32_t H, float sm_scale, int32_t has_invalid,
+                   void* out, int64_t o_stride_t, int64_t o_stride_h,
+                   float* lse,
+                   void* workspace, int64_t workspace_bytes,
+                   void* stream);
+
+/*
+ * sparse_mla_decode_rows -- test hook: decode records rows[0..n) of kv to f32
+ * out[n, 576] (latent * scale, then rope) exactly as the forward's QK stage
+ * sees them (scale applied through its exponent field), cross-checked on the
+ * device against the P.V stage's conversion for positive power-of-two scales
+ * (a disagreement yields NaN).  A row index outside [0, n_kv) yields a row of
+ * NaN.
+ *   kv device uint8 [n_kv, 656]; rows device int32 [n]; out device f32 [n, 576].
+ */
+int sparse_mla_decode_rows(const void* kv, int64_t n_kv, const int32_t* rows, int64_t n,
+                           float* out, void* stream);
+
+/* Message for the calling thread's last non-OK status ("" if none). */
+const char* sparse_mla_last_error(void);
+
+/*
+ * sparse_mla_set_option -- tuning / test knobs, process-wide, not thread-safe
+ * against concurrent forwards.  Names:
+ *   "split"  chunks per row when rows are split (0 = automatic, 1 = never,
+ *            2..SMLA_MAX_SPLIT forced); the workspace size accounts for it.
+ * Returns SMLA_OK or SMLA_EINVAL for an unknown name or value.
+ */
+#define SMLA_MAX_SPLIT 32
+int sparse_mla_set_option(const char* name, int64_t value);
+
+/*
+ * Kernel timing for benchmarks.  sparse_mla_profile_begin(max_calls) makes the
+ * following forwards (up to max_calls of them, on any stream) record HIP
+ * events around each kernel they queue; sparse_mla_profile_end() waits for
+ * those events, writes the summed device time in milliseconds and the launch
+ * count of each kernel kind (0 plan, 1 forward, 2 combine) to ms[3] and
+ * launches[3], and stops recording.  Creates and destroys events on the host
+ * only; no device memory is allocated.
+ */
+int sparse_mla_profile_begin(int32_t max_calls);
+int sparse_mla_profile_end(double* ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SMLA_H */

@@ -1,0 +1,204 @@
+"""ctypes binding of libsmla.so (C ABI in include/smla.h).
+
+Argument marshalling only: every step of the forward runs in the library's
+HIP kernels.  PyTorch supplies device memory and the current stream.  If the
+library is missing this module raises at import; there is no fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libsmla.so")
+
+SMLA_OK = 0
+SMLA_EINVAL = -1
+SMLA_EUNSUPPORTED = -2
+SMLA_EWORKSPACE = -3
+SMLA_EHIP = -4
+MAX_HEADS = 64
+MAX_SPLIT = 32
+RECORD_BYTES = 656
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is not built; run `python -m sparse_mla_decode_fp8_amd.build` "
+        "(or __graft_entry__.build()) first")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+_vp, _i32, _i64, _f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+_lib.sparse_mla_supported.argtypes = [_i32]
+_lib.sparse_mla_supported.restype = ctypes.c_int
+_lib.sparse_mla_workspace_bytes.argtypes = [_i32, _i32, _i64]
+_lib.sparse_mla_workspace_bytes.restype = _i64
+_lib.sparse_mla_fwd.argtypes = [
+    _vp, _i64, _i64,        # q, strides
+    _vp, _i64,              # kv, n_kv
+    _vp, _vp, _i64,         # indptr, indices, nnz
+    _i32, _i32, _f32, _i32,  # T, H, sm_scale, has_invalid
+    _vp, _i64, _i64,        # out, strides
+    _vp,                    # lse
+    _vp, _i64,              # workspace, bytes
+    _vp,                    # stream
+]
+_lib.sparse_mla_fwd.restype = ctypes.c_int
+_lib.sparse_mla_decode_rows.argtypes = [_vp, _i64, _vp, _i64, _vp, _vp]
+_lib.sparse_mla_decode_rows.restype = ctypes.c_int
+_lib.sparse_mla_last_error.argtypes = []
+_lib.sparse_mla_last_error.restype = ctypes.c_char_p
+_lib.sparse_mla_set_option.argtypes = [ctypes.c_char_p, _i64]
+_lib.sparse_mla_set_option.restype = ctypes.c_int
+_lib.sparse_mla_profile_begin.argtypes = [_i32]
+_lib.sparse_mla_profile_begin.restype = ctypes.c_int
+_lib.sparse_mla_profile_end.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i64)]
+_lib.sparse_mla_profile_end.restype = ctypes.c_int
+
+EXPORTED = (
+    "sparse_mla_supported", "sparse_mla_workspace_bytes", "sparse_mla_fwd",
+    "sparse_mla_decode_rows", "sparse_mla_last_error", "sparse_mla_set_option",
+    "sparse_mla_profile_begin", "sparse_mla_profile_end",
+)
+
+
+class SmlaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"smla status {status}: {msg}")
+        self.status = status
+
+
+def _check(rc: int) -> None:
+    if rc != SMLA_OK:
+        raise SmlaError(rc, _lib.sparse_mla_last_error().decode(errors="replace"))
+
+
+def lib() -> ctypes.CDLL:
+    return _lib
+
+
+def supported(num_heads: int) -> bool:
+    return bool(_lib.sparse_mla_supported(int(num_heads)))
+
+
+def workspace_bytes(T: int, H: int, nnz: int) -> int:
+    n = _lib.sparse_mla_workspace_bytes(int(T), int(H), int(nnz))
+    if n < 0:
+        _check(int(n))
+    return int(n)
+
+
+def set_option(name: str, value: int) -> None:
+    _check(_lib.sparse_mla_set_option(name.encode(), int(value)))
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+_ws_cache = {}
+
+
+def workspace(device: torch.device, nbytes: int) -> torch.Tensor:
+    """A zeroed device workspace of at least nbytes, reused per device.
+
+    The library keeps its first 256 bytes (a ticket) zero between calls, so a
+    cached workspace stays valid; calls on one device share it and must not
+    overlap in time (they are ordered on one stream in normal use)."""
+    key = (device.type, device.index)
+    ws = _ws_cache.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _ws_cache[key] = ws
+    return ws
+
+
+def fwd(q: torch.Tensor, kv: torch.Tensor, indptr: torch.Tensor, indices: torch.Tensor,
+        sm_scale: float, has_invalid: bool = False, return_lse: bool = True,
+        out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+        ws: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Sparse MLA forward: q bf16 [T, H, 576], kv uint8 [N, 656], indptr int32 [T+1],
+    indices int32 [nnz] -> (out bf16 [T, H, 512], lse f32 [T, H] or None)."""
+    if q.dtype != torch.bfloat16 or q.dim() != 3 or q.shape[2] != 576:
+        raise ValueError("q must be bf16 [T, H, 576]")
+    if kv.dtype != torch.uint8 or kv.dim() != 2 or kv.shape[1] != RECORD_BYTES:
+        raise ValueError(f"kv must be uint8 [N, {RECORD_BYTES}]")
+    if not kv.is_contiguous():
+        raise ValueError("kv rows must be contiguous")
+    if indptr.dtype != torch.int32 or indices.dtype != torch.int32:
+        raise ValueError("indptr and indices must be int32")
+    if q.stride(2) != 1:
+        raise ValueError("q's last dimension must be contiguous")
+    dev = q.device
+    for t in (kv, indptr, indices):
+        if t.device != dev:
+            raise ValueError("all tensors must be on q's device")
+    T, H, _ = q.shape
+    indptr = indptr.contiguous()
+    indices = indices.contiguous()
+    nnz = indices.numel()
+    if indptr.numel() != T + 1:
+        raise ValueError("indptr must have T + 1 entries")
+    if out is None:
+        out = torch.empty(T, H, 512, dtype=torch.bfloat16, device=dev)
+    if return_lse and lse is None:
+        lse = torch.empty(T, H, dtype=torch.float32, device=dev)
+    if not return_lse:
+        lse = None
+    nbytes = workspace_bytes(T, H, nnz)
+    if ws is None:
+        ws = workspace(dev, nbytes)
+    rc = _lib.sparse_mla_fwd(
+        _ptr(q), q.stride(0), q.stride(1),
+        _ptr(kv), kv.shape[0],
+        _ptr(indptr), _ptr(indices) if nnz else None, nnz,
+        T, H, float(sm_scale), 1 if has_invalid else 0,
+        _ptr(out), out.stride(0), out.stride(1),
+        _ptr(lse),
+        _ptr(ws), ws.numel(),
+        _stream(dev))
+    _check(rc)
+    return out, lse
+
+
+def decode_rows(kv: torch.Tensor, rows: torch.Tensor) -> torch.Tensor:
+    """Decode records kv[rows] to f32 [n, 576] on the device (test hook)."""
+    if kv.dtype != torch.uint8 or kv.dim() != 2 or kv.shape[1] != RECORD_BYTES or not kv.is_contiguous():
+        raise ValueError(f"kv must be contiguous uint8 [N, {RECORD_BYTES}]")
+    rows = rows.to(torch.int32).contiguous()
+    out = torch.empty(rows.numel(), 576, dtype=torch.float32, device=kv.device)
+    _check(_lib.sparse_mla_decode_rows(_ptr(kv), kv.shape[0], _ptr(rows), rows.numel(),
+                                       _ptr(out), _stream(kv.device)))
+    return out
+
+
+class KernelTimer:
+    """HIP-event timing of the library's kernels over the calls made inside
+    the ``with`` block: ``.ms`` and ``.launches`` per kind (plan, fwd, combine)."""
+
+    KINDS = ("plan", "fwd", "combine")
+
+    def __init__(self, max_calls: int):
+        self.max_calls = max_calls
+        self.ms = {}
+        self.launches = {}
+
+    def __enter__(self):
+        _check(_lib.sparse_mla_profile_begin(int(self.max_calls)))
+        return self
+
+    def __exit__(self, *exc):
+        ms = (ctypes.c_double * 3)()
+        n = (_i64 * 3)()
+        _check(_lib.sparse_mla_profile_end(ms, n))
+        self.ms = {k: ms[i] for i, k in enumerate(self.KINDS)}
+        self.launches = {k: int(n[i]) for i, k in enumerate(self.KINDS)}
+        return False

@@ -1,0 +1,285 @@
+// C ABI of libsmla.so (declared in include/smla.h): argument validation,
+// work planning (split factor, workspace layout) and kernel launches on the
+// caller's stream.  No allocation and no host synchronisation on the forward
+// path.
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "smla.h"
+#include "smla_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(SMLA_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int64_t g_split_override = 0;  // 0 = automatic
+
+int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return 256;
+  return cus;
+}
+
+// Chunks per row.  Rows are independent, so split only when there are too few
+// rows to give every CU a unit; never split below one tile per chunk.
+int choose_split(int32_t T, int32_t H, int64_t nnz) {
+  if (g_split_override > 0) return (int)g_split_override;
+  if (T <= 0) return 1;
+  const int tile = smla::tile_tokens(H);
+  const int64_t avg_tiles = (nnz / T + tile - 1) / tile;
+  const int cus = device_cus();
+  if (T >= cus) return 1;
+  int64_t s = (cus + T - 1) / T;
+  if (s > avg_tiles) s = avg_tiles;
+  if (s > SMLA_MAX_SPLIT) s = SMLA_MAX_SPLIT;
+  return s < 1 ? 1 : (int)s;
+}
+
+struct Layout {
+  int S;
+  size_t ticket, row_tiles, order, part_lse, part_o, total;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+Layout layout(int32_t T, int32_t H, int64_t nnz) {
+  Layout L{};
+  L.S = choose_split(T, H, nnz);
+  size_t off = 0;
+  L.ticket = off;
+  off += 256;
+  L.row_tiles = off;
+  off = align256(off + sizeof(int32_t) * (size_t)T);
+  L.order = off;
+  off = align256(off + sizeof(int32_t) * (size_t)T);
+  L.part_lse = off;
+  L.part_o = off;
+  if (L.S > 1) {
+    off = align256(off + sizeof(float) * (size_t)T * L.S * H);
+    L.part_o = off;
+    off = align256(off + sizeof(float) * (size_t)T * L.S * H * 512);
+  }
+  L.total = off;
+  return L;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// ---- kernel timing (benchmarks)
+struct Prof {
+  std::mutex mu;
+  bool active = false;
+  int cap = 0;
+  int used = 0;  // event pairs used
+  std::vector<hipEvent_t> ev;  // 2 per pair
+  std::vector<int> kind;       // per pair
+} g_prof;
+
+template <class F>
+hipError_t timed(int kind, hipStream_t s, F&& launch) {
+  int slot = -1;
+  {
+    std::lock_guard<std::mutex> lk(g_prof.mu);
+    if (g_prof.active && g_prof.used < g_prof.cap) {
+      slot = g_prof.used++;
+      g_prof.kind[slot] = kind;
+    }
+  }
+  if (slot >= 0) {
+    hipError_t e = hipEventRecord(g_prof.ev[2 * slot], s);
+    if (e != hipSuccess) return e;
+  }
+  hipError_t e = launch();
+  if (e != hipSuccess) return e;
+  if (slot >= 0) return hipEventRecord(g_prof.ev[2 * slot + 1], s);
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sparse_mla_supported(int32_t num_heads) { return num_heads >= 1 && num_heads <= SMLA_MAX_HEADS; }
+
+int64_t sparse_mla_workspace_bytes(int32_t T, int32_t H, int64_t nnz) {
+  if (T < 0 || nnz < 0) return fail(SMLA_EINVAL, "T and nnz must be >= 0 (T=%d nnz=%lld)", T, (long long)nnz);
+  if (!sparse_mla_supported(H)) return fail(SMLA_EUNSUPPORTED, "num_heads must be in [1, %d], got %d", SMLA_MAX_HEADS, H);
+  return (int64_t)layout(T, H, nnz).total;
+}
+
+int sparse_mla_fwd(const void* q, int64_t q_stride_t, int64_t q_stride_h,
+                   const void* kv, int64_t n_kv,
+                   const int32_t* indptr, const int32_t* indices, int64_t nnz,
+                   int32_t T, int32_t H, float sm_scale, int32_t has_invalid,
+                   void* out, int64_t o_stride_t, int64_t o_stride_h,
+                   float* lse,
+                   void* workspace, int64_t workspace_bytes,
+                   void* stream) {
+  g_err.clear();
+  if (!sparse_mla_supported(H)) return fail(SMLA_EUNSUPPORTED, "num_heads must be in [1, %d], got %d", SMLA_MAX_HEADS, H);
+  if (T < 0) return fail(SMLA_EINVAL, "T must be >= 0, got %d", T);
+  if (nnz < 0) return fail(SMLA_EINVAL, "nnz must be >= 0, got %lld", (long long)nnz);
+  if (nnz >= (int64_t(1) << 30)) return fail(SMLA_EINVAL, "nnz must be < 2^30 (32-bit bounded index reads), got %lld", (long long)nnz);
+  if (n_kv < 0 || n_kv > INT64_MAX / smla::kRecordBytes) return fail(SMLA_EINVAL, "n_kv out of range: %lld", (long long)n_kv);
+  if (!isfinite(sm_scale)) return fail(SMLA_EINVAL, "sm_scale must be finite");
+  if (T == 0) return SMLA_OK;
+  if (!q || !kv || !indptr || !out || !workspace) return fail(SMLA_EINVAL, "null pointer (q, kv, indptr, out and workspace are required)");
+  if (nnz > 0 && !indices) return fail(SMLA_EINVAL, "indices is null but nnz > 0");
+  if (!aligned(q, 16) || !aligned(out, 16) || !aligned(kv, 16)) return fail(SMLA_EINVAL, "q, out and kv must be 16-byte aligned");
+  if (!aligned(workspace, 256)) return fail(SMLA_EINVAL, "workspace must be 256-byte aligned");
+  if (q_stride_t < 0 || q_stride_h < 0 || o_stride_t < 0 || o_stride_h < 0 ||
+      (q_stride_t | q_stride_h | o_stride_t | o_stride_h) % 8 != 0)
+    return fail(SMLA_EINVAL, "strides must be non-negative multiples of 8 elements");
+  const Layout L = layout(T, H, nnz);
+  if (workspace_bytes < (int64_t)L.total)
+    return fail(SMLA_EWORKSPACE, "workspace has %lld bytes, needs %lld", (long long)workspace_bytes, (long long)L.total);
+
+  hipStream_t s = (hipStream_t)stream;
+  uint8_t* ws = (uint8_t*)workspace;
+  int32_t* row_tiles = (int32_t*)(ws + L.row_tiles);
+  int32_t* order = (int32_t*)(ws + L.order);
+  const uint32_t idx_bytes = (uint32_t)(nnz * 4);
+
+  smla::PlanParams pp{indptr, indices, idx_bytes, T, smla::tile_tokens(H), has_invalid ? 1 : 0,
+                      row_tiles, order, (uint32_t*)(ws + L.ticket)};
+  hipError_t e = timed(0, s, [&] { return smla::launch_plan(pp, s); });
+  if (e != hipSuccess) return hip_fail(e, "plan kernel launch");
+
+  smla::FwdParams fp{};
+  fp.q = (const uint16_t*)q;
+  fp.q_st = q_stride_t;
+  fp.q_sh = q_stride_h;
+  fp.kv = (const uint8_t*)kv;
+  fp.indptr = indptr;
+  fp.indices = indices;
+  fp.idx_bytes = idx_bytes;
+  fp.T = T;
+  fp.H = H;
+  fp.S = L.S;
+  fp.c_log2 = (float)((double)sm_scale * 1.4426950408889634074);
+  fp.out = (uint16_t*)out;
+  fp.o_st = o_stride_t;
+  fp.o_sh = o_stride_h;
+  fp.lse = lse;
+  fp.row_tiles = row_tiles;
+  fp.order = order;
+  fp.part_o = (float*)(ws + L.part_o);
+  fp.part_lse = (float*)(ws + L.part_lse);
+  e = timed(1, s, [&] { return smla::launch_fwd(fp, s); });
+  if (e != hipSuccess) return hip_fail(e, "forward kernel launch");
+
+  if (L.S > 1) {
+    smla::CombineParams cp{T, H, L.S, order, fp.part_o, fp.part_lse, fp.out, o_stride_t, o_stride_h, lse};
+    e = timed(2, s, [&] { return smla::launch_combine(cp, s); });
+    if (e != hipSuccess) return hip_fail(e, "combine kernel launch");
+  }
+  return SMLA_OK;
+}
+
+int sparse_mla_decode_rows(const void* kv, int64_t n_kv, const int32_t* rows, int64_t n,
+                           float* out, void* stream) {
+  g_err.clear();
+  if (n < 0 || n_kv < 0) return fail(SMLA_EINVAL, "n and n_kv must be >= 0");
+  if (n > 0x7fffffff) return fail(SMLA_EINVAL, "n too large for one launch");
+  if (n == 0) return SMLA_OK;
+  if (!kv || !rows || !out) return fail(SMLA_EINVAL, "null pointer");
+  if (!aligned(kv, 16)) return fail(SMLA_EINVAL, "kv must be 16-byte aligned");
+  hipError_t e = smla::launch_decode_rows((const uint8_t*)kv, n_kv, rows, n, out, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
+  return SMLA_OK;
+}
+
+const char* sparse_mla_last_error(void) { return g_err.c_str(); }
+
+int sparse_mla_set_option(const char* name, int64_t value) {
+  g_err.clear();
+  if (!name) return fail(SMLA_EINVAL, "null option name");
+  if (!strcmp(name, "split")) {
+    if (value < 0 || value > SMLA_MAX_SPLIT) return fail(SMLA_EINVAL, "split must be in [0, %d]", SMLA_MAX_SPLIT);
+    g_split_override = value;
+    return SMLA_OK;
+  }
+  return fail(SMLA_EINVAL, "unknown option '%s'", name);
+}
+
+int sparse_mla_profile_begin(int32_t max_calls) {
+  g_err.clear();
+  if (max_calls <= 0) return fail(SMLA_EINVAL, "max_calls must be > 0");
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  if (g_prof.active) return fail(SMLA_EINVAL, "profiling already active");
+  const int pairs = 3 * max_calls;
+  g_prof.ev.assign(2 * pairs, nullptr);
+  g_prof.kind.assign(pairs, -1);
+  for (auto& ev : g_prof.ev) {
+    hipError_t e = hipEventCreate(&ev);
+    if (e != hipSuccess) {
+      for (auto& x : g_prof.ev)
+        if (x) (void)hipEventDestroy(x);
+      g_prof.ev.clear();
+      return hip_fail(e, "hipEventCreate");
+    }
+  }
+  g_prof.cap = pairs;
+  g_prof.used = 0;
+  g_prof.active = true;
+  return SMLA_OK;
+}
+
+int sparse_mla_profile_end(double* ms, int64_t* launches) {
+  g_err.clear();
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  if (!g_prof.active) return fail(SMLA_EINVAL, "profiling not active");
+  double acc[3] = {0, 0, 0};
+  int64_t cnt[3] = {0, 0, 0};
+  int rc = SMLA_OK;
+  for (int i = 0; i < g_prof.used; ++i) {
+    hipError_t e = hipEventSynchronize(g_prof.ev[2 * i + 1]);
+    float t = 0.0f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&t, g_prof.ev[2 * i], g_prof.ev[2 * i + 1]);
+    if (e != hipSuccess) {
+      rc = hip_fail(e, "event timing");
+      break;
+    }
+    const int k = g_prof.kind[i];
+    acc[k] += t;
+    cnt[k] += 1;
+  }
+  for (auto& x : g_prof.ev) (void)hipEventDestroy(x);
+  g_prof.ev.clear();
+  g_prof.kind.clear();
+  g_prof.active = false;
+  g_prof.cap = g_prof.used = 0;
+  if (rc != SMLA_OK) return rc;
+  for (int k = 0; k < 3; ++k) {
+    if (ms) ms[k] = acc[k];
+    if (launches) launches[k] = cnt[k];
+  }
+  return SMLA_OK;
+}
+
+}  // extern "C"

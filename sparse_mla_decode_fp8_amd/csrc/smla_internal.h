@@ -1,0 +1,68 @@
+// Internal interface between the C ABI (smla_api.cpp) and the HIP kernels
+// (smla_kernels.hip).  Not installed; the public ABI is include/smla.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace smla {
+
+constexpr int kRecordBytes = 656;  // 512 e4m3 | 4 x f32 scale | 64 x bf16 rope
+constexpr int kTokensPerWave = 32;  // tokens one wave owns in a tile
+constexpr int kPlanBuckets = 256;   // longest-first counting-sort buckets (tiles, capped)
+
+struct PlanParams {
+  const int32_t* indptr;
+  const int32_t* indices;
+  uint32_t idx_bytes;  // bytes of `indices` readable (bounded index reads)
+  int32_t T;
+  int32_t tile;        // tokens per tile
+  int32_t has_invalid;
+  int32_t* row_tiles;  // [T] out: tiles of each row
+  int32_t* order;      // [T] out: rows, longest first
+  uint32_t* ticket;    // zero on entry; zero again on exit
+};
+
+struct FwdParams {
+  const uint16_t* q;   // bf16 bits
+  int64_t q_st, q_sh;
+  const uint8_t* kv;
+  const int32_t* indptr;
+  const int32_t* indices;
+  uint32_t idx_bytes;
+  int32_t T, H, S;     // rows, heads, chunks per row
+  float c_log2;        // sm_scale * log2(e)
+  uint16_t* out;       // bf16 bits
+  int64_t o_st, o_sh;
+  float* lse;          // nullable
+  const int32_t* row_tiles;
+  const int32_t* order;
+  float* part_o;       // [T*S, H, 512] when S > 1
+  float* part_lse;     // [T*S, H]  (log2 units) when S > 1
+};
+
+struct CombineParams {
+  int32_t T, H, S;
+  const int32_t* order;
+  const float* part_o;
+  const float* part_lse;
+  uint16_t* out;
+  int64_t o_st, o_sh;
+  float* lse;
+};
+
+// Head tiling: HT tiles of 16 heads; TG token groups of 32 tokens per tile.
+inline int head_tiles(int H) { return (H + 15) / 16; }
+inline int token_groups(int H) { int ht = head_tiles(H); return ht >= 3 ? 1 : 4 / ht; }
+inline int tile_tokens(int H) { return kTokensPerWave * token_groups(H); }
+
+hipError_t launch_plan(const PlanParams& p, hipStream_t s);
+hipError_t launch_fwd(const FwdParams& p, hipStream_t s);
+hipError_t launch_combine(const CombineParams& p, hipStream_t s);
+hipError_t launch_decode_rows(const uint8_t* kv, int64_t n_kv, const int32_t* rows, int64_t n,
+                              float* out, hipStream_t s);
+
+// Blocks a launch of T rows x `per_row` blocks uses with the XCD-aware mapping.
+inline int64_t xcd_grid(int32_t T, int32_t per_row) { return 8LL * ((T + 7) / 8) * per_row; }
+
+}  // namespace smla

@@ -15,4 +15,5 @@ from .workloads import (  # noqa: F401
     make_config,
     make_workload,
     distinct_uniform,
+    build_workload,
 )

@@ -1,0 +1,84 @@
+"""Shared helpers of the GPU parity tests: run the HIP path through the C ABI
+and the fp64 oracle on the same seeded inputs, and compare them.
+
+Tolerances (stated for this method): out relative L2 <= 1e-2 and max abs
+<= 3e-2 per element, lse max abs <= 1e-3 over rows that have a key, the -inf
+lse positions identical and rows without a key exactly zero.  Where |out| is
+large (the +-1000 outlier workload) a bf16 output cannot carry 3e-2 absolute
+accuracy, so the per-element bound there is 3e-2 + 2^-8 |ref| (the storage
+bound of a bf16 result); the literal max abs is still reported.
+"""
+
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+
+OUT_REL_L2 = 1e-2
+OUT_ABS = 3e-2
+LSE_ABS = 1e-3
+BF16_REL = 2.0 ** -8
+
+
+def q_bits(w) -> np.ndarray:
+    return w.q.detach().cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def run_gpu(w, *, has_invalid=None, return_lse=True, q=None, out=None):
+    import sparse_mla_decode_fp8_amd as smla
+    dev = torch.device("cuda", 0)
+    q = (w.q if q is None else q).to(dev)
+    kv, ip, ix = w.kv.to(dev), w.indptr.to(dev), w.indices.to(dev)
+    hi = w.has_invalid if has_invalid is None else has_invalid
+    o, l = smla.fwd(q, kv, ip, ix, w.sm_scale, has_invalid=bool(hi), return_lse=return_lse, out=out)
+    torch.cuda.synchronize()
+    return o, l
+
+
+def run_oracle(w, rows=None):
+    kv = w.kv.cpu().numpy()
+    return oracle.sparse_mla_fwd(q_bits(w), kv, w.indptr.cpu().numpy(), w.indices.cpu().numpy(),
+                                 w.sm_scale, rows=rows)
+
+
+def compare(out_gpu, lse_gpu, out_ref, lse_ref, rows=None, large_values=False, label=""):
+    """Assert the tolerances; return the measured error figures."""
+    o = out_gpu.detach().float().cpu().numpy().astype(np.float64)
+    rows = np.arange(o.shape[0]) if rows is None else np.asarray(rows)
+    o, r = o[rows], out_ref[rows]
+    lr = lse_ref[rows]
+    live = np.isfinite(lr)  # [rows, H]
+    stats = {}
+    # rows / heads with no key: exactly zero output, -inf lse
+    assert np.all(o[~live] == 0.0), f"{label}: nonzero output where no key"
+    if lse_gpu is not None:
+        lg = lse_gpu.detach().cpu().numpy().astype(np.float64)[rows]
+        assert np.array_equal(np.isneginf(lg), ~live), f"{label}: -inf lse positions differ"
+        if live.any():
+            stats["lse_max_abs"] = float(np.max(np.abs(lg[live] - lr[live])))
+            assert stats["lse_max_abs"] <= LSE_ABS, f"{label}: lse err {stats['lse_max_abs']}"
+    if live.any():
+        d = o[live] - r[live]
+        nr = np.linalg.norm(r[live])
+        stats["out_rel_l2"] = float(np.linalg.norm(d) / nr) if nr > 0 else float(np.linalg.norm(d))
+        stats["out_max_abs"] = float(np.max(np.abs(d)))
+        bound = OUT_ABS + (BF16_REL * np.abs(r[live]) if large_values else 0.0)
+        worst = float(np.max(np.abs(d) - bound))
+        assert stats["out_rel_l2"] <= OUT_REL_L2, f"{label}: rel L2 {stats['out_rel_l2']}"
+        assert worst <= 0.0, f"{label}: max abs {stats['out_max_abs']} over bound by {worst}"
+    print(f"[parity] {label} {stats}", file=sys.stderr, flush=True)
+    return stats
+
+
+def sample_rows(T: int, n: int, seed: int = 0) -> np.ndarray:
+    """Up to n rows: the first, the last and a seeded uniform sample between."""
+    if T <= n:
+        return np.arange(T)
+    rng = np.random.default_rng(seed)
+    mid = rng.choice(np.arange(1, T - 1), size=n - 2, replace=False)
+    return np.sort(np.concatenate([[0, T - 1], mid]))

@@ -1,0 +1,106 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/smla.h declares, and rejects malformed arguments on the host with the
+documented status before any kernel is queued."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "smla.h")
+
+
+@pytest.fixture(scope="module")
+def b():
+    from sparse_mla_decode_fp8_amd import binding
+    return binding
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sparse_mla_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(b):
+    decl = declared_functions()
+    assert len(decl) >= 8
+    lib = b.lib()
+    for name in decl:
+        assert hasattr(lib, name), f"{name} declared in smla.h but not exported"
+    assert sorted(b.EXPORTED) == decl
+
+
+def test_supported_range(b):
+    assert not b.supported(0)
+    assert b.supported(1) and b.supported(16) and b.supported(64)
+    assert not b.supported(65)
+
+
+def test_workspace_bytes(b):
+    assert b.workspace_bytes(0, 16, 0) >= 256
+    small = b.workspace_bytes(4096, 64, 4096 * 2048)   # many rows: no split partials
+    assert small < 1 << 20
+    with pytest.raises(b.SmlaError) as e:
+        b.workspace_bytes(1, 65, 10)
+    assert e.value.status == b.SMLA_EUNSUPPORTED
+    with pytest.raises(b.SmlaError) as e:
+        b.workspace_bytes(-1, 16, 10)
+    assert e.value.status == b.SMLA_EINVAL
+
+
+FAKE = 0x10000  # a 256-aligned non-null address; never dereferenced by the failing calls
+
+
+def call(b, **over):
+    a = dict(q=FAKE, qst=576 * 16, qsh=576, kv=FAKE, n_kv=10, indptr=FAKE, indices=FAKE, nnz=4,
+             T=1, H=16, scale=0.04, inv=0, out=FAKE, ost=512 * 16, osh=512, lse=None,
+             ws=FAKE, wsb=1 << 40, stream=None)
+    a.update(over)
+    return b.lib().sparse_mla_fwd(a["q"], a["qst"], a["qsh"], a["kv"], a["n_kv"], a["indptr"],
+                                  a["indices"], a["nnz"], a["T"], a["H"], a["scale"], a["inv"],
+                                  a["out"], a["ost"], a["osh"], a["lse"], a["ws"], a["wsb"],
+                                  a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(H=0), -2), (dict(H=65), -2), (dict(T=-1), -1), (dict(nnz=-1), -1),
+    (dict(nnz=1 << 30), -1), (dict(n_kv=-1), -1), (dict(scale=float("inf")), -1),
+    (dict(q=None), -1), (dict(kv=None), -1), (dict(indptr=None), -1), (dict(out=None), -1),
+    (dict(ws=None), -1), (dict(indices=None), -1), (dict(q=FAKE + 8), -1),
+    (dict(out=FAKE + 4), -1), (dict(kv=FAKE + 2), -1), (dict(ws=FAKE + 16), -1),
+    (dict(qsh=577), -1), (dict(ost=-512), -1), (dict(wsb=100), -3),
+])
+def test_host_validation(b, over, status):
+    assert call(b, **over) == status
+    assert b.lib().sparse_mla_last_error()  # a message for the failing call
+
+
+def test_zero_rows_is_a_noop(b):
+    assert call(b, T=0, q=None, out=None, ws=None) == 0
+
+
+def test_options(b):
+    assert b.lib().sparse_mla_set_option(b"split", 4) == 0
+    assert b.lib().sparse_mla_set_option(b"split", 0) == 0
+    assert b.lib().sparse_mla_set_option(b"split", 33) == -1
+    assert b.lib().sparse_mla_set_option(b"nope", 1) == -1
+
+
+def test_decode_rows_validation(b):
+    lib = b.lib()
+    assert lib.sparse_mla_decode_rows(FAKE, 10, FAKE, -1, FAKE, None) == -1
+    assert lib.sparse_mla_decode_rows(None, 10, FAKE, 3, FAKE, None) == -1
+    assert lib.sparse_mla_decode_rows(FAKE + 4, 10, FAKE, 3, FAKE, None) == -1
+    assert lib.sparse_mla_decode_rows(FAKE, 10, FAKE, 0, FAKE, None) == 0
+
+
+def test_profile_state_machine(b):
+    lib = b.lib()
+    ms = (ctypes.c_double * 3)()
+    n = (ctypes.c_int64 * 3)()
+    assert lib.sparse_mla_profile_end(ms, n) == -1      # not active
+    assert lib.sparse_mla_profile_begin(0) == -1

@@ -1,0 +1,267 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Every case prints its name and shape before touching the GPU and its error
+figures after.  Inputs are seeded and synthetic (synth/); the oracle never
+sees anything the HIP path produced.
+"""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from parity import compare, q_bits, run_gpu, run_oracle, sample_rows
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda", 0)
+
+
+def note(msg):
+    print(f"[case] {msg}", file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module")
+def smla():
+    import sparse_mla_decode_fp8_amd as m
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return m
+
+
+@pytest.fixture(autouse=True)
+def _reset_split(smla):
+    smla.set_option("split", 0)
+    yield
+    smla.set_option("split", 0)
+
+
+def custom(name, H, N, slices, seed=11, device="cuda", **kw):
+    slices = [np.asarray(s, dtype=np.int64) for s in slices]
+    return synth.build_workload(name, len(slices), H, N, lambda g, r, m: slices[r],
+                                seed=seed, device=device, **kw)
+
+
+# ------------------------------------------------------------------ decode hook
+
+def test_decode_rows_bitexact(smla):
+    rng = np.random.default_rng(5)
+    n = 512
+    rec = np.zeros((n, 656), np.uint8)
+    codes = np.tile(np.arange(256, dtype=np.uint8), (n, 2))
+    codes = np.stack([rng.permutation(c) for c in codes])
+    codes[(codes & 0x7F) == 0x7F] = 0x00  # the two NaN codes are covered separately
+    rec[:, :512] = codes
+    e = rng.integers(-22, 8, size=(n, 4)).astype(np.float64)
+    sc = np.ldexp(1.0, e.astype(int)).astype("<f4")
+    sc[::17, 2] = 0.0  # zero-scale blocks
+    rec[:, 512:528] = sc.view(np.uint8).reshape(n, 16)
+    rec[:, 528:] = rng.integers(0, 256, size=(n, 128), dtype=np.uint8)
+    rec[:, 529::2] &= 0x7F ^ 0x40  # keep rope exponents finite
+    kv = torch.from_numpy(rec).to(DEV)
+    rows = torch.from_numpy(np.concatenate([rng.permutation(n), [-1, n]]).astype(np.int32)).to(DEV)
+    note(f"decode_rows n={n}")
+    got = smla.decode_rows(kv, rows).cpu().numpy()
+    ref = oracle.decode_records(rec[rows.cpu().numpy()[:n]]).astype(np.float32)
+    # zero-scale blocks: the QK conversion applies the scale's exponent field,
+    # so they decode to code * 2^-127 (a zero latent for attention purposes)
+    zmask = np.zeros((n, 576), bool)
+    zrow = np.isin(rows.cpu().numpy()[:n], np.arange(0, n, 17))
+    zmask[np.ix_(zrow, np.arange(256, 384))] = True
+    assert np.all(np.abs(got[:n][zmask]) <= 2.0 ** -118)
+    gb, rb = got[:n].view(np.uint32), ref.view(np.uint32)
+    bad = np.argwhere((gb != rb) & ~zmask)
+    detail = [(int(i), int(j), float(got[i, j]), float(ref[i, j]), hex(int(rec[rows.cpu().numpy()[i], j])) if j < 512 else "rope")
+              for i, j in bad[:12]]
+    assert bad.size == 0, f"{len(bad)} mismatching values, first: {detail}"
+    assert np.all(np.isnan(got[n:]))
+
+
+# ------------------------------------------------------------------ the five workloads
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_config_parity(smla, cfg):
+    c = synth.make_config(cfg)
+    note(f"config {cfg} {c['name']} T={c['T']} H={c['H']} N={c['N']}")
+    w = synth.make_workload(cfg, device="cuda")
+    out, lse = run_gpu(w)
+    rows = None if cfg != 5 else sample_rows(w.T, 48, seed=cfg)
+    ro, rl = run_oracle(w, rows=rows)
+    compare(out, lse, ro, rl, rows=rows, large_values=(cfg == 3), label=f"config{cfg}")
+
+
+# ------------------------------------------------------------------ edge cases
+
+def edge_slices(N, rng):
+    s = [
+        [],                                   # empty
+        [-1, -1, -1],                          # all invalid
+        [int(rng.integers(N))],                # single key
+        rng.integers(0, N, 31).tolist(),       # < one wave's 32
+        rng.integers(0, N, 33).tolist(),       # crosses a wave boundary
+        rng.integers(0, N, 127).tolist(),      # ragged tail
+        rng.integers(0, N, 129).tolist(),      # one past a 128-token tile
+        rng.integers(0, N, 300).tolist() + [-1] * 70,            # trailing padding
+        [-1] * 40 + rng.integers(0, N, 50).tolist() + [-1] * 9,  # leading and trailing -1
+        (rng.integers(0, N, 200) * (rng.random(200) < 0.7) - (rng.random(200) >= 0.7)).tolist(),
+        rng.integers(0, N, 1000).tolist(),
+        [int(N - 1)] * 5,                      # duplicates of the last row
+    ]
+    return s
+
+
+@pytest.mark.parametrize("has_invalid", [0, 1])
+def test_edge_rows(smla, has_invalid):
+    rng = np.random.default_rng(21)
+    N = 5000
+    w = custom("edges", 16, N, edge_slices(N, rng), has_invalid=has_invalid)
+    note(f"edge rows has_invalid={has_invalid} T={w.T}")
+    out, lse = run_gpu(w)
+    ro, rl = run_oracle(w)
+    compare(out, lse, ro, rl, label=f"edges_inv{has_invalid}")
+
+
+def test_negative_length_rows(smla):
+    rng = np.random.default_rng(22)
+    w = custom("neglen", 16, 600, [rng.integers(0, 600, 50), rng.integers(0, 600, 70), rng.integers(0, 600, 40)])
+    ip = w.indptr.cpu().numpy()
+    ip[1] = ip[2] + 5  # row 0 grows past row 1's end, row 1 gets a negative length
+    w.indptr = torch.from_numpy(ip).to(DEV)
+    note("negative length")
+    out, lse = run_gpu(w)
+    ro, rl = run_oracle(w)
+    assert np.isneginf(rl[1]).all()
+    compare(out, lse, ro, rl, label="neglen")
+
+
+@pytest.mark.parametrize("H", [1, 7, 16, 17, 32, 33, 48, 64])
+def test_head_counts(smla, H):
+    rng = np.random.default_rng(100 + H)
+    N = 3000
+    sl = [rng.integers(0, N, int(L)) for L in rng.integers(0, 400, 9)]
+    w = custom(f"heads{H}", H, N, sl, seed=H)
+    note(f"H={H} T={w.T}")
+    out, lse = run_gpu(w)
+    ro, rl = run_oracle(w)
+    compare(out, lse, ro, rl, label=f"H{H}")
+
+
+@pytest.mark.parametrize("split", [1, 2, 3, 7, 32])
+def test_forced_split(smla, split):
+    rng = np.random.default_rng(7)
+    N = 20000
+    sl = [rng.integers(0, N, int(L)) for L in (2048, 1, 700, 0, 1500, 129)]
+    w = custom("split", 16, N, sl)
+    smla.set_option("split", split)
+    note(f"split={split}")
+    out, lse = run_gpu(w)
+    ro, rl = run_oracle(w)
+    compare(out, lse, ro, rl, label=f"split{split}")
+
+
+def test_single_index_is_exact(smla):
+    rng = np.random.default_rng(8)
+    N = 700
+    w = custom("single", 16, N, [[int(i)] for i in rng.integers(0, N, 40)])
+    note("single index per row")
+    out, lse = run_gpu(w)
+    K = oracle.decode_records(w.kv.cpu().numpy()[w.indices.cpu().numpy()])
+    want = torch.from_numpy(K[:, :512]).float().to(torch.bfloat16)[:, None, :].expand(-1, 16, -1)
+    assert torch.equal(out.cpu(), want), "one key must return that record's latent exactly"
+    Q = oracle.bf16_bits_to_f64(q_bits(w))
+    s = w.sm_scale * np.einsum("thd,td->th", Q, K)
+    assert np.max(np.abs(lse.cpu().numpy() - s)) <= 1e-3
+
+
+def test_strided_q_out_and_no_lse(smla):
+    rng = np.random.default_rng(9)
+    N = 4000
+    sl = [rng.integers(0, N, int(L)) for L in (300, 5, 640)]
+    w = custom("strided", 16, N, sl)
+    qbig = torch.zeros(w.T, 19, 584, dtype=torch.bfloat16, device=DEV)
+    qbig[:, 2:18, :576] = w.q.to(DEV)
+    obig = torch.full((w.T, 20, 520), 7.0, dtype=torch.bfloat16, device=DEV)
+    note("strided q/out, no lse")
+    out, lse = run_gpu(w, q=qbig[:, 2:18, :576], out=obig[:, 3:19, :512], return_lse=False)
+    assert lse is None
+    ro, rl = run_oracle(w)
+    compare(out, None, ro, rl, label="strided")
+    assert torch.all(obig[:, :3] == 7.0) and torch.all(obig[:, 19:] == 7.0)
+    assert torch.all(obig[:, :, 512:] == 7.0)
+
+
+def test_empty_index_stream(smla):
+    w = custom("nnz0", 16, 10, [[], [], []])
+    note("nnz = 0")
+    out, lse = run_gpu(w)
+    assert torch.all(out == 0) and torch.all(torch.isneginf(lse))
+
+
+def test_zero_scale_records(smla):
+    rng = np.random.default_rng(12)
+    N = 300
+    w = custom("zeroscale", 16, N, [rng.integers(0, N, 200), rng.integers(0, N, 33)])
+    kv = w.kv.cpu().numpy()
+    kv[::3, 512:528] = 0  # every third record: all four scales zero
+    kv[1::3, 516:520] = 0  # block 1 zero
+    w.kv = torch.from_numpy(kv).to(DEV)
+    note("zero-scale records")
+    out, lse = run_gpu(w)
+    ro, rl = run_oracle(w)
+    compare(out, lse, ro, rl, label="zeroscale")
+
+
+def test_permutation_duplicates(smla):
+    rng = np.random.default_rng(13)
+    N = 2500
+    base = [rng.integers(0, N, 500), rng.integers(0, N, 77)]
+    w1 = custom("perm_a", 16, N, base, seed=3)
+    w2 = custom("perm_b", 16, N, [rng.permutation(b) for b in base], seed=3)
+    w3 = custom("dups", 16, N, [np.repeat(b, 2) for b in base], seed=3)
+    note("permutation / duplicates")
+    o1, l1 = run_gpu(w1)
+    o2, l2 = run_gpu(w2)
+    o3, l3 = run_gpu(w3)
+    ro, rl = run_oracle(w1)
+    compare(o2, l2, ro, rl, label="permuted")
+    compare(o3, l3 - math.log(2), ro, rl, label="duplicated")
+
+
+def test_causal_ragged_longest_first(smla):
+    """Many ragged rows (row r has min(r + 1, 2048) keys): exercises the
+    longest-first order and has_invalid trimming at scale."""
+    T, N = 600, 32768
+    rng = np.random.default_rng(14)
+    sl = []
+    for r in range(T):
+        L = min(3 * r + 1, 2048)
+        sl.append(np.concatenate([rng.integers(0, N, L), -np.ones(2048 - L, np.int64)]))
+    w = custom("causal", 16, N, sl, has_invalid=1)
+    note(f"causal ragged T={T}")
+    out, lse = run_gpu(w)
+    rows = sample_rows(T, 40, seed=1)
+    ro, rl = run_oracle(w, rows=rows)
+    compare(out, lse, ro, rl, rows=rows, label="causal")
+
+
+def test_repeat_calls_bitwise_identical(smla):
+    w = synth.make_workload(2, device="cuda", T=16)
+    note("repeat determinism")
+    o1, l1 = run_gpu(w)
+    o2, l2 = run_gpu(w)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_scale_above_cap_stays_finite(smla):
+    """A scale above 2^7 breaks a precondition: the result must stay finite."""
+    rng = np.random.default_rng(15)
+    N = 200
+    w = custom("bigscale", 16, N, [rng.integers(0, N, 100)])
+    kv = w.kv.cpu().numpy()
+    kv[:, 512:516] = np.frombuffer(np.float32(2.0 ** 10).tobytes(), np.uint8)
+    w.kv = torch.from_numpy(kv).to(DEV)
+    note("scale above cap")
+    out, lse = run_gpu(w)
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
