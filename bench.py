@@ -1,0 +1,283 @@
+"""Benchmark of the sparse MLA forward (plan + forward + combine) on one GPU.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
+
+One "step" is one call of the whole op on one batch of the workload.  Prints
+one JSON line (the last line of stdout).  Inputs are seeded synthetic tensors
+made on the device before timing.  The workload defaults to the decode batch
+(64 query rows, 16 heads, 65,536 records, 2,048 keys per row).
+
+Figures:
+  value        gathered KV GB/s over the timed steps, warm (back-to-back calls);
+               gathered bytes = 656 B x (CSR entries >= 0), counted once per entry
+  rows_per_s   query rows per second, same timing
+  cold         the same figures with a 1 GiB scratch write between calls (no
+               cache reuse across calls); median of per-call HIP-event times
+  roofline     the forward kernel alone: gathered bytes per launch / its mean
+               launch time (HIP events the library records around each launch
+               on the launch stream) against 8 TB/s HBM peak; `traffic` is the
+               HBM bytes per launch from the committed rocprofv3 counter summary
+               (null if that summary was taken from other kernel source)
+  cpu_baseline the fp64 CPU oracle on the same workload on this host's cores
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "gathered KV GB/s and query-rows/s (sparse MLA fwd, top-k 2048); % HBM peak"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+RECORD_BYTES = 656
+KERNEL_SRC = os.path.join(ROOT, "sparse_mla_decode_fp8_amd", "csrc", "smla_kernels.hip")
+COUNTERS = os.path.join(ROOT, "profiles", "fwd_decode_T64_H16_counters.txt")
+
+
+def kernel_sha() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic(config_name: str):
+    """HBM bytes per forward launch from the committed counter summary, if it
+    was measured on this workload with the current kernel source."""
+    if not os.path.exists(COUNTERS):
+        return None
+    kv = {}
+    with open(COUNTERS) as f:
+        for line in f:
+            m = re.match(r"^(\w+):\s*(\S+)", line.strip())
+            if m:
+                kv[m.group(1)] = m.group(2)
+    if kv.get("kernel_source_sha256_16") != kernel_sha() or kv.get("workload") != config_name:
+        return None
+    try:
+        return int(float(kv["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, budget_s: float, max_workers: int):
+    """Time the fp64 oracle over the workload's rows: whole passes over all rows,
+    repeated until budget_s, in a pool of spawned processes (fresh interpreters
+    that never touch the GPU), one BLAS thread each."""
+    import numpy as np
+    import torch
+    from concurrent.futures import ProcessPoolExecutor
+    import multiprocessing as mp
+    q = w.q.detach().cpu().view(torch.int16).numpy().view(np.uint16)
+    args = (q, w.kv.cpu().numpy(), w.indptr.cpu().numpy(), w.indices.cpu().numpy(), w.sm_scale)
+    workers = max(1, min(max_workers, len(os.sched_getaffinity(0)), w.T))
+    chunks = [list(range(i, w.T, workers)) for i in range(workers)]
+    valid = w.valid_entries()
+    with ProcessPoolExecutor(max_workers=workers, mp_context=mp.get_context("spawn"),
+                             initializer=_cb_init, initargs=args) as ex:
+        list(ex.map(_cb_rows, [[0]] * workers))  # start-up and imports, untimed
+        passes = 0
+        t0 = time.perf_counter()
+        while True:
+            list(ex.map(_cb_rows, chunks))
+            passes += 1
+            dt = time.perf_counter() - t0
+            if dt >= budget_s or passes >= 1000:
+                break
+    return {
+        "value": round(RECORD_BYTES * valid * passes / dt / 1e9, 4),
+        "unit": "GB/s",
+        "rows_per_s": round(w.T * passes / dt, 2),
+        "cores": workers,
+        "kind": "oracle",
+        "sample": f"{passes} full pass(es) over all {w.T} rows of the timed workload "
+                  f"({dt:.1f} s wall, fp64 NumPy oracle, {workers} processes x 1 BLAS thread)",
+        "cpu": _cpu_model(),
+    }
+
+
+_CB_ARGS = None
+
+
+def _cb_init(*args):
+    global _CB_ARGS
+    _CB_ARGS = args
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
+    except Exception:  # noqa: BLE001
+        pass
+
+
+def _cb_rows(rows):
+    import oracle
+    q, kv, ip, ix, sc = _CB_ARGS
+    oracle.sparse_mla_fwd(q, kv, ip, ix, sc, rows=rows)
+    return len(rows)
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--config", type=int, default=2, help="workload number 1..5")
+    ap.add_argument("--cold-steps", type=int, default=50)
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run plain device copies of known size (counter scaling)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        return 2
+
+    import torch
+    import synth
+    import sparse_mla_decode_fp8_amd as smla
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    cfg = synth.make_config(args.config)
+    print(f"[bench] generating {cfg['name']}", file=sys.stderr, flush=True)
+    w = synth.make_workload(args.config, device="cuda")
+    valid = w.valid_entries()
+    gathered = RECORD_BYTES * valid
+    flop = 2.0 * w.H * (576 + 512) * valid
+    out = torch.empty(w.T, w.H, 512, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(w.T, w.H, dtype=torch.float32, device=dev)
+    ws = smla.workspace(dev, smla.workspace_bytes(w.T, w.H, w.nnz))
+
+    def step():
+        smla.fwd(w.q, w.kv, w.indptr, w.indices, w.sm_scale, has_invalid=bool(w.has_invalid),
+                 out=out, lse=lse, ws=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # ---- warm: K back-to-back steps
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+
+    # ---- per-kernel device time (events around each launch, on its stream)
+    with smla.KernelTimer(args.steps) as kt:
+        for _ in range(args.steps):
+            step()
+    torch.cuda.synchronize()
+    fwd_ms = kt.ms["fwd"] / max(kt.launches["fwd"], 1)
+
+    # ---- cold: flush caches between calls
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    cold = []
+    for _ in range(args.cold_steps):
+        scratch.fill_(1)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        step()
+        b.record()
+        torch.cuda.synchronize()
+        cold.append(a.elapsed_time(b))
+    cold_ms = statistics.median(cold)
+    del scratch
+
+    if args.calibrate_copy:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(3)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    s = ms_per_step * 1e-3
+    achieved = gathered / (fwd_ms * 1e-3) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": round(gathered / s / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": cfg["name"], "T": w.T, "H": w.H, "N": w.N, "topk": cfg["topk"],
+            "nnz": w.nnz, "valid_entries": valid, "has_invalid": w.has_invalid,
+            "record_bytes": RECORD_BYTES, "split": _split_of(smla, w),
+        },
+        "rows_per_s": round(w.T / s, 1),
+        "tflops": round(flop / s / 1e12, 2),
+        "pct_hbm_peak": round(100.0 * gathered / s / 1e9 / HBM_PEAK_GBS, 2),
+        "precision": "records e4m3 (exactly dequantised); QK bf16 MFMA, PV f16 MFMA, f32 accumulation and softmax",
+        "cold": {
+            "ms_per_call_median": round(cold_ms, 5),
+            "value": round(gathered / (cold_ms * 1e-3) / 1e9, 2),
+            "rows_per_s": round(w.T / (cold_ms * 1e-3), 1),
+            "pct_hbm_peak": round(100.0 * gathered / (cold_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+            "calls": args.cold_steps,
+        },
+        "kernels_ms_per_call": {k: round(kt.ms[k] / max(kt.launches[k], 1), 5) if kt.launches[k] else 0.0
+                                for k in kt.KINDS},
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": read_traffic(cfg["name"]),
+            "kernel": "smla_fwd_kernel",
+            "bytes_per_launch": gathered,
+            "launch_ms": round(fwd_ms, 5),
+        },
+    }
+    if args.config == 5:
+        tf = flop / (fwd_ms * 1e-3) / 1e12
+        result["roofline"].update({"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS,
+                                   "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
+                                   "flop_per_launch": flop})
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_budget, 16)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def _split_of(smla, w) -> int:
+    from sparse_mla_decode_fp8_amd import binding
+    return binding.split_for(w.T, w.H, w.nnz)
+
+
+if __name__ == "__main__":
+    sys.exit(main())

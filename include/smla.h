@@ -57,15 +57,21 @@ int sparse_mla_supported(int32_t num_heads);
 
 /*
  * sparse_mla_workspace_bytes -- device workspace a forward of T query rows,
- * H heads and nnz CSR entries needs on the current device (per-row plan,
- * longest-first order and, when rows are split, chunk partials).  Returns
- * the byte count (>= 256), or a negative smla_status for invalid arguments.
- * The first 256 bytes hold a ticket counter that must be zero the first time
- * a workspace is used (e.g. hipMemset once); every completed forward leaves it
- * zero again.  A workspace must not be shared by forwards that may run
- * concurrently.
+ * H heads and nnz CSR entries needs on the current device (per-row tile
+ * counts, the longest-first row order and, when rows are split, chunk
+ * partials).  Returns the byte count, or a negative smla_status for invalid
+ * arguments.  The workspace needs no initialisation; it must not be shared by
+ * forwards that may run concurrently.
  */
 int64_t sparse_mla_workspace_bytes(int32_t T, int32_t H, int64_t nnz);
+
+/*
+ * sparse_mla_split_for -- chunks per row (>= 1) a forward of T rows, H heads
+ * and nnz entries uses on the current device: rows are split, and the chunks
+ * merged by their log-sum-exp, only when there are too few rows to give every
+ * compute unit work.  Negative smla_status for invalid arguments.
+ */
+int32_t sparse_mla_split_for(int32_t T, int32_t H, int64_t nnz);
 
 /*
  * sparse_mla_fwd -- sparse MLA forward over fp8_ds_mla records.
@@ -92,7 +98,7 @@ int64_t sparse_mla_workspace_bytes(int32_t T, int32_t H, int64_t nnz);
  *   lse        device, f32 [T, H] contiguous, or NULL to skip it.  Natural log;
  *              -inf for a row with no key (whose out is all zero).
  *   workspace  device, >= sparse_mla_workspace_bytes(T, H, nnz) bytes,
- *              256-byte aligned, ticket zero (see above).
+ *              256-byte aligned.
  *
  * Preconditions the library cannot check (undefined results if broken, as on
  * the FlyDSL page, section "Preconditions the host cannot check"):
@@ -107,9 +113,11 @@ int64_t sparse_mla_workspace_bytes(int32_t T, int32_t H, int64_t nnz);
  *     give unspecified rows).
  *
  * Returns SMLA_OK, or SMLA_EINVAL / SMLA_EUNSUPPORTED / SMLA_EWORKSPACE /
- * SMLA_EHIP with nothing queued.  Queues 2 or 3 kernels on `stream`
- * (plan, forward, and a combine when rows are split), no host sync, no
- * allocation.  Deterministic for a fixed device and arguments.
+ * SMLA_EHIP with nothing queued.  Queues on `stream`: the plan (a slice
+ * scan when has_invalid, then a one-block longest-first sort), the forward,
+ * and a combine when rows are split.  No host sync, no allocation.
+ * Deterministic for a fixed device and arguments.  nnz must be below
+ * 2^30 - 4096 (index reads use 32-bit byte offsets).
  */
 int sparse_mla_fwd(const void* q, int64_t q_stride_t, int64_t q_stride_h,
                    const void* kv, int64_t n_kv,

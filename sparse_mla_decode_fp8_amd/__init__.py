@@ -9,7 +9,7 @@ there is no fallback path.
 
 _PUBLIC = (
     "MAX_HEADS", "MAX_SPLIT", "KernelTimer", "SmlaError", "decode_rows", "fwd",
-    "set_option", "supported", "workspace", "workspace_bytes", "LIB_PATH", "EXPORTED",
+    "set_option", "split_for", "supported", "workspace", "workspace_bytes", "LIB_PATH", "EXPORTED",
 )
 
 __all__ = list(_PUBLIC)

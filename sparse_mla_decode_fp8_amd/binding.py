@@ -37,6 +37,8 @@ _lib.sparse_mla_supported.argtypes = [_i32]
 _lib.sparse_mla_supported.restype = ctypes.c_int
 _lib.sparse_mla_workspace_bytes.argtypes = [_i32, _i32, _i64]
 _lib.sparse_mla_workspace_bytes.restype = _i64
+_lib.sparse_mla_split_for.argtypes = [_i32, _i32, _i64]
+_lib.sparse_mla_split_for.restype = _i32
 _lib.sparse_mla_fwd.argtypes = [
     _vp, _i64, _i64,        # q, strides
     _vp, _i64,              # kv, n_kv
@@ -60,7 +62,7 @@ _lib.sparse_mla_profile_end.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.
 _lib.sparse_mla_profile_end.restype = ctypes.c_int
 
 EXPORTED = (
-    "sparse_mla_supported", "sparse_mla_workspace_bytes", "sparse_mla_fwd",
+    "sparse_mla_supported", "sparse_mla_workspace_bytes", "sparse_mla_split_for", "sparse_mla_fwd",
     "sparse_mla_decode_rows", "sparse_mla_last_error", "sparse_mla_set_option",
     "sparse_mla_profile_begin", "sparse_mla_profile_end",
 )
@@ -92,6 +94,14 @@ def workspace_bytes(T: int, H: int, nnz: int) -> int:
     return int(n)
 
 
+def split_for(T: int, H: int, nnz: int) -> int:
+    """Chunks per row the forward uses for this shape on the current device."""
+    n = _lib.sparse_mla_split_for(int(T), int(H), int(nnz))
+    if n < 0:
+        _check(int(n))
+    return int(n)
+
+
 def set_option(name: str, value: int) -> None:
     _check(_lib.sparse_mla_set_option(name.encode(), int(value)))
 
@@ -108,15 +118,13 @@ _ws_cache = {}
 
 
 def workspace(device: torch.device, nbytes: int) -> torch.Tensor:
-    """A zeroed device workspace of at least nbytes, reused per device.
-
-    The library keeps its first 256 bytes (a ticket) zero between calls, so a
-    cached workspace stays valid; calls on one device share it and must not
-    overlap in time (they are ordered on one stream in normal use)."""
+    """A device workspace of at least nbytes, reused per device.  Calls on one
+    device share it, so they must not overlap in time (they are ordered on one
+    stream in normal use)."""
     key = (device.type, device.index)
     ws = _ws_cache.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
         _ws_cache[key] = ws
     return ws
 

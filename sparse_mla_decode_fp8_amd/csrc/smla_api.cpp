@@ -37,6 +37,28 @@ int hip_fail(hipError_t e, const char* what) {
 
 int64_t g_split_override = 0;  // 0 = automatic
 
+// Index reads use 32-bit byte offsets; the kernels read up to a few tiles past
+// a row's end, so leave headroom below 2^32 bytes.
+constexpr int64_t kMaxNnz = (int64_t(1) << 30) - 4096;
+
+// Device address of the zero record, per device (looked up once per device).
+std::mutex g_zero_mu;
+const uint8_t* g_zero_ptr[64] = {};
+
+hipError_t zero_record(const uint8_t** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_zero_mu);
+  if (!g_zero_ptr[dev]) {
+    e = smla::zero_record_address(&g_zero_ptr[dev]);
+    if (e != hipSuccess) return e;
+  }
+  *out = g_zero_ptr[dev];
+  return hipSuccess;
+}
+
 int device_cus() {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 256;
@@ -62,7 +84,7 @@ int choose_split(int32_t T, int32_t H, int64_t nnz) {
 
 struct Layout {
   int S;
-  size_t ticket, row_tiles, order, part_lse, part_o, total;
+  size_t row_tiles, order, part_lse, part_o, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -71,8 +93,6 @@ Layout layout(int32_t T, int32_t H, int64_t nnz) {
   Layout L{};
   L.S = choose_split(T, H, nnz);
   size_t off = 0;
-  L.ticket = off;
-  off += 256;
   L.row_tiles = off;
   off = align256(off + sizeof(int32_t) * (size_t)T);
   L.order = off;
@@ -132,6 +152,12 @@ int64_t sparse_mla_workspace_bytes(int32_t T, int32_t H, int64_t nnz) {
   return (int64_t)layout(T, H, nnz).total;
 }
 
+int32_t sparse_mla_split_for(int32_t T, int32_t H, int64_t nnz) {
+  if (T < 0 || nnz < 0) return fail(SMLA_EINVAL, "T and nnz must be >= 0 (T=%d nnz=%lld)", T, (long long)nnz);
+  if (!sparse_mla_supported(H)) return fail(SMLA_EUNSUPPORTED, "num_heads must be in [1, %d], got %d", SMLA_MAX_HEADS, H);
+  return choose_split(T, H, nnz);
+}
+
 int sparse_mla_fwd(const void* q, int64_t q_stride_t, int64_t q_stride_h,
                    const void* kv, int64_t n_kv,
                    const int32_t* indptr, const int32_t* indices, int64_t nnz,
@@ -144,7 +170,7 @@ int sparse_mla_fwd(const void* q, int64_t q_stride_t, int64_t q_stride_h,
   if (!sparse_mla_supported(H)) return fail(SMLA_EUNSUPPORTED, "num_heads must be in [1, %d], got %d", SMLA_MAX_HEADS, H);
   if (T < 0) return fail(SMLA_EINVAL, "T must be >= 0, got %d", T);
   if (nnz < 0) return fail(SMLA_EINVAL, "nnz must be >= 0, got %lld", (long long)nnz);
-  if (nnz >= (int64_t(1) << 30)) return fail(SMLA_EINVAL, "nnz must be < 2^30 (32-bit bounded index reads), got %lld", (long long)nnz);
+  if (nnz > kMaxNnz) return fail(SMLA_EINVAL, "nnz must be <= %lld (32-bit bounded index reads), got %lld", (long long)kMaxNnz, (long long)nnz);
   if (n_kv < 0 || n_kv > INT64_MAX / smla::kRecordBytes) return fail(SMLA_EINVAL, "n_kv out of range: %lld", (long long)n_kv);
   if (!isfinite(sm_scale)) return fail(SMLA_EINVAL, "sm_scale must be finite");
   if (T == 0) return SMLA_OK;
@@ -159,6 +185,9 @@ int sparse_mla_fwd(const void* q, int64_t q_stride_t, int64_t q_stride_h,
   if (workspace_bytes < (int64_t)L.total)
     return fail(SMLA_EWORKSPACE, "workspace has %lld bytes, needs %lld", (long long)workspace_bytes, (long long)L.total);
 
+  const uint8_t* zero = nullptr;
+  hipError_t ez = zero_record(&zero);
+  if (ez != hipSuccess) return hip_fail(ez, "zero record lookup");
   hipStream_t s = (hipStream_t)stream;
   uint8_t* ws = (uint8_t*)workspace;
   int32_t* row_tiles = (int32_t*)(ws + L.row_tiles);
@@ -166,7 +195,7 @@ int sparse_mla_fwd(const void* q, int64_t q_stride_t, int64_t q_stride_h,
   const uint32_t idx_bytes = (uint32_t)(nnz * 4);
 
   smla::PlanParams pp{indptr, indices, idx_bytes, T, smla::tile_tokens(H), has_invalid ? 1 : 0,
-                      row_tiles, order, (uint32_t*)(ws + L.ticket)};
+                      row_tiles, order};
   hipError_t e = timed(0, s, [&] { return smla::launch_plan(pp, s); });
   if (e != hipSuccess) return hip_fail(e, "plan kernel launch");
 
@@ -175,6 +204,7 @@ int sparse_mla_fwd(const void* q, int64_t q_stride_t, int64_t q_stride_h,
   fp.q_st = q_stride_t;
   fp.q_sh = q_stride_h;
   fp.kv = (const uint8_t*)kv;
+  fp.zero = zero;
   fp.indptr = indptr;
   fp.indices = indices;
   fp.idx_bytes = idx_bytes;

@@ -20,13 +20,13 @@ struct PlanParams {
   int32_t has_invalid;
   int32_t* row_tiles;  // [T] out: tiles of each row
   int32_t* order;      // [T] out: rows, longest first
-  uint32_t* ticket;    // zero on entry; zero again on exit
 };
 
 struct FwdParams {
   const uint16_t* q;   // bf16 bits
   int64_t q_st, q_sh;
   const uint8_t* kv;
+  const uint8_t* zero; // a record of zeros on this device (masked positions read it)
   const int32_t* indptr;
   const int32_t* indices;
   uint32_t idx_bytes;
@@ -58,6 +58,8 @@ inline int tile_tokens(int H) { return kTokensPerWave * token_groups(H); }
 
 hipError_t launch_plan(const PlanParams& p, hipStream_t s);
 hipError_t launch_fwd(const FwdParams& p, hipStream_t s);
+// Device address of the library's zero record on the current device.
+hipError_t zero_record_address(const uint8_t** out);
 hipError_t launch_combine(const CombineParams& p, hipStream_t s);
 hipError_t launch_decode_rows(const uint8_t* kv, int64_t n_kv, const int32_t* rows, int64_t n,
                               float* out, hipStream_t s);

@@ -42,6 +42,7 @@ namespace smla {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v2i __attribute__((ext_vector_type(2)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v2f __attribute__((ext_vector_type(2)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
@@ -86,6 +87,23 @@ __device__ __forceinline__ void dma16(const uint8_t* src, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                :: "v"(src), "s"(lds_base) : "memory", "m0");
 }
+// 16 bytes per lane from the SGPR address `base` plus a per-lane 32-bit
+// offset into LDS at lds_base + 16*lane (LDS DMA, scalar-base form).
+__device__ __forceinline__ void dma16_s(const uint8_t* base, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(base), "s"(lds_base) : "memory", "m0");
+}
+// 4 bytes per lane from a 64-bit global address into LDS at lds_base + 4*lane.
+__device__ __forceinline__ void dma4(const uint8_t* src, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :: "v"(src), "s"(lds_base) : "memory", "m0");
+}
+// 4 bytes per lane through a bounded buffer descriptor (reads past its size
+// return 0) into LDS at lds_base + 4*lane.
+__device__ __forceinline__ void buf_dma4(__amdgpu_buffer_rsrc_t rsrc, uint32_t voffset, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
+               :: "v"(voffset), "s"(rsrc), "s"(lds_base) : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 // vmcnt(0) only (expcnt, lgkmcnt left at their maxima), through the intrinsic
@@ -127,9 +145,6 @@ __device__ __forceinline__ v8h cvt8_f16(v2i w) {
   return v8h{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
 }
 
-__device__ __forceinline__ const uint8_t* record_ptr(const uint8_t* kv, int ix) {
-  return ix >= 0 ? kv + (int64_t)ix * kRecordBytes : g_zero_record;
-}
 
 // XCD-aware unit mapping: block b runs on XCD b % 8; rows of rank r go to XCD
 // r % 8 and the `per_row` blocks of a row are consecutive on that XCD.
@@ -142,89 +157,125 @@ __device__ __forceinline__ void xcd_unit(int per_row, int& rank, int& sub) {
 
 // ---------------------------------------------------------------- plan
 
-// One wave per row: tile count (after the has_invalid trim); the last block to
-// finish sorts rows by tile count, longest first (FlyDSL page: long rows are
-// issued first so the long tail starts early).
-__global__ __launch_bounds__(256) void smla_plan_kernel(PlanParams p) {
+// Tiles of a row from its effective length.
+__device__ __forceinline__ int tiles_of(int len, int tile) { return (len + tile - 1) / tile; }
+
+// has_invalid only: one wave per row finds 1 + the last slice position whose
+// entry is >= 0 (bounded index reads) and stores the row's tile count.
+__global__ __launch_bounds__(256) void smla_plan_scan_kernel(PlanParams p) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  __shared__ int s_last;
-  __shared__ int s_hist[kPlanBuckets];
-  if (row < p.T) {
-    const int beg = p.indptr[row];
-    const int len = max(p.indptr[row + 1] - beg, 0);
-    int eff = len;
+  if (row >= p.T) return;
+  const int beg = p.indptr[row];
+  const int len = max(p.indptr[row + 1] - beg, 0);
+  const __amdgpu_buffer_rsrc_t r = idx_rsrc(p.indices, p.idx_bytes);
+  int lastp = 0;
+  for (int base = 0; base < len; base += 256) {
+    int v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = load_idx(r, (uint32_t)(beg + base + 4 * lane + j) * 4u);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int pos = base + 4 * lane + j;
+      if (pos < len && v[j] >= 0) lastp = pos + 1;
+    }
+  }
+#pragma unroll
+  for (int sh = 32; sh >= 1; sh >>= 1) lastp = max(lastp, __shfl_xor(lastp, sh));
+  if (lane == 0) p.row_tiles[row] = tiles_of(lastp, p.tile);
+}
+
+// One block: tile counts of every row (from the scan, or from indptr) and a
+// counting sort of the rows by tile count, longest first (the FlyDSL page
+// issues long rows first so the long tail starts early).
+__global__ __launch_bounds__(1024) void smla_plan_sort_kernel(PlanParams p) {
+  __shared__ int s_cnt[kPlanBuckets];
+  __shared__ int s_wsum[kPlanBuckets / 64];
+  const int tid = threadIdx.x;
+  for (int i = tid; i < kPlanBuckets; i += blockDim.x) s_cnt[i] = 0;
+  __syncthreads();
+  for (int r = tid; r < p.T; r += blockDim.x) {
+    int t;
     if (p.has_invalid) {
-      const __amdgpu_buffer_rsrc_t r = idx_rsrc(p.indices, p.idx_bytes);
-      int lastp = 0;
-      for (int base = 0; base < len; base += 256) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int pos = base + 4 * lane + j;
-          const int v = load_idx(r, (uint32_t)(beg + pos) * 4u);
-          if (pos < len && v >= 0) lastp = pos + 1;
-        }
-      }
-#pragma unroll
-      for (int sh = 32; sh >= 1; sh >>= 1) lastp = max(lastp, __shfl_xor(lastp, sh));
-      eff = lastp;
+      t = p.row_tiles[r];
+    } else {
+      t = tiles_of(max(p.indptr[r + 1] - p.indptr[r], 0), p.tile);
+      p.row_tiles[r] = t;
     }
-    if (lane == 0) p.row_tiles[row] = (eff + p.tile - 1) / p.tile;
-  }
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t prev = __hip_atomic_fetch_add(p.ticket, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = (prev == gridDim.x - 1);
+    atomicAdd(&s_cnt[min(t, kPlanBuckets - 1)], 1);
   }
   __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  for (int i = threadIdx.x; i < kPlanBuckets; i += blockDim.x) s_hist[i] = 0;
-  __syncthreads();
-  for (int r = threadIdx.x; r < p.T; r += blockDim.x) {
-    const int t = __hip_atomic_load(p.row_tiles + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    atomicAdd(&s_hist[min(t, kPlanBuckets - 1)], 1);
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {  // exclusive prefix, largest bucket first
-    int acc = 0;
-    for (int b = kPlanBuckets - 1; b >= 0; --b) {
-      const int c = s_hist[b];
-      s_hist[b] = acc;
-      acc += c;
+  // exclusive prefix over buckets in descending order: start[b] = sum_{b' > b} cnt[b'].
+  // Threads < kPlanBuckets (whole waves) scan; every thread meets every barrier.
+  const bool scanner = tid < kPlanBuckets;
+  const int b = kPlanBuckets - 1 - (scanner ? tid : 0);  // position tid in descending order
+  const int c = scanner ? s_cnt[b] : 0;
+  int incl = c;
+  if (scanner) {
+#pragma unroll
+    for (int sh = 1; sh < 64; sh <<= 1) {
+      const int o = __shfl_up(incl, sh);
+      if ((tid & 63) >= sh) incl += o;
     }
+    if ((tid & 63) == 63) s_wsum[tid >> 6] = incl;
   }
   __syncthreads();
-  for (int r = threadIdx.x; r < p.T; r += blockDim.x) {
-    const int t = __hip_atomic_load(p.row_tiles + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    p.order[atomicAdd(&s_hist[min(t, kPlanBuckets - 1)], 1)] = r;
+  if (scanner) {
+    int off = 0;
+    for (int w = 0; w < (tid >> 6); ++w) off += s_wsum[w];
+    s_cnt[b] = off + incl - c;
   }
-  if (threadIdx.x == 0) __hip_atomic_store(p.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  for (int r = tid; r < p.T; r += blockDim.x) {
+    const int t = p.row_tiles[r];
+    p.order[atomicAdd(&s_cnt[min(t, kPlanBuckets - 1)], 1)] = r;
+  }
 }
 
 // ---------------------------------------------------------------- forward
+
+// s_waitcnt immediates (gfx9 layout: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14)
+constexpr int waitcnt_vm(int n) { return (n & 0xF) | (0x7 << 4) | (0xF << 8) | (((n >> 4) & 0x3) << 14); }
+constexpr int kWaitLgkm0 = 0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14);
+
+constexpr int kLatRow = kLat + 16;  // LDS row of a token's latent, padded: QK reads conflict-free
+constexpr int kWaveLatStage = kTokensPerWave * kLatRow;
+constexpr int kSideTok = 144;       // scales (16 B) + rope (128 B) of a record
+constexpr int kSideChunks = 9;
+constexpr int kRing = 8;            // index ring slots (tiles)
+constexpr int kPrefetchInstr = 3;   // 32 tokens x 6 cache lines / 64 lanes
+constexpr int kIdxAhead = 5;        // tile n issues the index load of tile n + 5
+constexpr float kShift = 4.0f;      // P = exp2(x - m_ref + 4)
+constexpr float kTau = 4.0f;        // m_ref moves only when a head's max exceeds it by > 4
 
 template <int HT, int TG>
 struct FwdCfg {
   static constexpr int kWaves = HT * TG;
   static constexpr int kThreads = 64 * kWaves;
   static constexpr int kTile = kTokensPerWave * TG;
-  static constexpr int kLatBytes = 2 * TG * kWaveLatBytes;  // 2 stages
+  static constexpr int kSideStages = TG == 4 ? 1 : 2;  // TG == 4 implies HT == 1 (wave-private)
+  static constexpr int kLatBytes = 2 * TG * kWaveLatStage;
+  static constexpr int kSideBytes = kSideStages * TG * kTokensPerWave * kSideTok;
+  static constexpr int kIdxBytes = kRing * TG * kTokensPerWave * 4;
+  static constexpr int kTabBytes = 2 * kWaves * kTokensPerWave * 8;  // per-wave record-address tables
+  static constexpr int kJunkBytes = kPrefetchInstr * 256;
+  static constexpr int kSideOff = kLatBytes;
+  static constexpr int kIdxOff = kSideOff + kSideBytes;
+  static constexpr int kTabOff = kIdxOff + kIdxBytes;
+  static constexpr int kJunkOff = kTabOff + kTabBytes;
+  static constexpr int kStreamBytes = kJunkOff + kJunkBytes;
   static constexpr int kMergeBytes = TG > 1 ? TG * HT * 16 * kMergeRow * 4 : 0;
-  static constexpr int kBigBytes = kLatBytes > kMergeBytes ? kLatBytes : kMergeBytes;
-};
-
-struct Side {
-  v4f sc[2];     // 4 block scales of tokens t and 16 + t
-  v4i rp[2][2];  // rope A operands: [subtile][rope K-step]
+  static constexpr int kBigBytes = kStreamBytes > kMergeBytes ? kStreamBytes : kMergeBytes;
+  // vector-memory instructions a wave issues after a tile's latent and side
+  // DMA and before the next tile's wait: the L2 prefetch and one index load
+  static constexpr int kTrailingVm = kPrefetchInstr + 1;
 };
 
 template <int HT, int TG>
 __global__ __launch_bounds__(64 * HT * TG, 1) void smla_fwd_kernel(FwdParams p) {
   using C = FwdCfg<HT, TG>;
+  static_assert(C::kBigBytes + 2 * C::kWaves * 16 * 4 <= 160 * 1024, "LDS budget");
   __shared__ __attribute__((aligned(1024))) uint8_t s_big[C::kBigBytes];
-  __shared__ __attribute__((aligned(16))) v4f s_ks[C::kWaves][kTokensPerWave];
   __shared__ float s_m[C::kWaves][16];
   __shared__ float s_l[C::kWaves][16];
 
@@ -266,6 +317,87 @@ __global__ __launch_bounds__(64 * HT * TG, 1) void smla_fwd_kernel(FwdParams p) 
     return;
   }
 
+  // ---- LDS addresses: latent rows and side data of this wave's token group,
+  // the group's index ring, this wave's record-address tables, a junk slot.
+  const uint32_t big = lds_addr(s_big);
+  auto lat_at = [&](int st) -> uint32_t { return big + (st * TG + tg) * kWaveLatStage; };
+  auto side_at = [&](int st) -> uint32_t {
+    return big + C::kSideOff + (st * TG + tg) * kTokensPerWave * kSideTok;
+  };
+  auto ring_at = [&](int n) -> uint32_t {
+    return big + C::kIdxOff + ((n & (kRing - 1)) * TG + tg) * kTokensPerWave * 4;
+  };
+  auto tab_at = [&](int n) -> uint32_t {
+    return big + C::kTabOff + ((n & 1) * C::kWaves + wave) * kTokensPerWave * 8;
+  };
+  const uint32_t junk = big + C::kJunkOff;
+  const __amdgpu_buffer_rsrc_t irs = idx_rsrc(p.indices, p.idx_bytes);
+  const uint8_t* const kv = p.kv;
+  const uint8_t* const zero = p.zero;
+
+  // Index at slice position of token `tau` of this group in tile n (from the
+  // ring), -1 past the row.  Positions past nnz read 0 and are masked here.
+  auto ring_ix = [&](int n, int tau) -> int {
+    const int raw = *LDSP(int, ring_at(n) + 4 * tau);
+    return (n * C::kTile + kTokensPerWave * tg + tau < len) ? raw : -1;
+  };
+  auto rec_of = [&](int ix) -> const uint8_t* { return ix >= 0 ? kv + (int64_t)ix * kRecordBytes : zero; };
+  // C: index DMA of tile n (bounded buffer reads, 32 entries) into its ring slot.
+  auto issue_idx = [&](int n) {
+    const uint32_t base = __builtin_amdgcn_readfirstlane(ring_at(n));
+    if (lane < kTokensPerWave) {
+      const uint32_t off = (uint32_t)(beg + n * C::kTile + kTokensPerWave * tg + lane) * 4u;
+      buf_dma4(irs, off, base);
+    }
+  };
+  // Record addresses of tile n's 32 tokens into this wave's table (lane tau
+  // writes token tau's); tiles at or past t1 get the zero record.
+  auto fill_table = [&](int n) {
+    if (lane < kTokensPerWave) {
+      const int ix = n < t1 ? ring_ix(n, lane) : -1;
+      *LDSP(uint64_t, tab_at(n) + 8 * lane) = (uint64_t)(uintptr_t)rec_of(ix);
+    }
+  };
+  // A: latent DMA of tile n into stage st: one instruction per token, its
+  // record address in SGPRs, lanes 0..31 fetch its 16-byte chunks.
+  auto issue_latent = [&](int n, int st) {
+    const int ix = ring_ix(n, lane & 31);
+    const uint32_t base = lat_at(st);
+    if (lane < kTokensPerWave) {
+#pragma unroll
+      for (int tau = ht; tau < kTokensPerWave; tau += HT) {
+        const int v = __builtin_amdgcn_readlane(ix, tau);
+        dma16_s(rec_of(v), 16 * lane, __builtin_amdgcn_readfirstlane(base + kLatRow * tau));
+      }
+    }
+  };
+  // B: side DMA (scales + rope, 9 chunks per token) of tile n into stage st,
+  // addresses from this wave's table.
+  auto issue_side = [&](int n, int st) {
+    const uint32_t base = __builtin_amdgcn_readfirstlane(side_at(st));
+    const uint32_t tab = tab_at(n);
+#pragma unroll
+    for (int k = ht; k < 5; k += HT) {
+      const int piece = 64 * k + lane;
+      if (piece < kTokensPerWave * kSideChunks) {
+        const int tau = piece / kSideChunks, c = piece % kSideChunks;
+        const uint8_t* rec = (const uint8_t*)(uintptr_t)*LDSP(uint64_t, tab + 8 * tau);
+        dma16(rec + kScaleOff + 16 * c, base + 1024 * k);
+      }
+    }
+  };
+  // D: L2 prefetch of tile n's records (6 lines each) into a junk LDS slot.
+  auto issue_prefetch = [&](int n) {
+    const uint32_t tab = tab_at(n);
+#pragma unroll
+    for (int k = 0; k < kPrefetchInstr; ++k) {
+      const int e = 64 * k + lane;
+      const int tau = e / 6, j = e % 6;
+      const uint8_t* rec = (const uint8_t*)(uintptr_t)*LDSP(uint64_t, tab + 8 * tau);
+      dma4(rec + 128 * j, __builtin_amdgcn_readfirstlane(junk + 256 * k));
+    }
+  };
+
   // ---- q as bf16 B operands.  Latent K-step 2m / 2m+1: dims 64m + 16g + [0..7] / [8..15];
   // rope K-step i: dims 512 + 32i + 8g + [0..7].
   v8bf qlat[16];
@@ -288,104 +420,114 @@ __global__ __launch_bounds__(64 * HT * TG, 1) void smla_fwd_kernel(FwdParams p) 
     }
   }
 
-  const __amdgpu_buffer_rsrc_t irs = idx_rsrc(p.indices, p.idx_bytes);
-  const uint32_t lat0 = lds_addr(s_big) + tg * kWaveLatBytes;  // stage st adds st*TG*16K
-
-  // Index of token (lane & 31) of this wave's 32 positions in tile n.  The raw
-  // (bounded) load and the row-end mask are separate so a prefetched index is
-  // not consumed, and so not waited for, before the next tile.
-  auto pos_of = [&](int n) -> int { return n * C::kTile + kTokensPerWave * tg + (lane & 31); };
-  auto load_raw = [&](int n) -> int { return load_idx(irs, (uint32_t)(beg + pos_of(n)) * 4u); };
-  auto masked = [&](int raw, int n) -> int { return pos_of(n) < len ? raw : -1; };
-  // Latent DMA of the wave's 32 tokens into stage `st`.  LDS holds token tau's
-  // 16-byte chunk c at slot c ^ tau of its 512-byte row; instruction k covers
-  // tokens 2k, 2k+1 (lane -> token 2k + lane/32, slot lane % 32).
-  auto issue_dma = [&](int ix_lane, int st) {
-    const uint32_t base = __builtin_amdgcn_readfirstlane(lat0 + st * TG * kWaveLatBytes);
+  // ---- prologue: indices of the first tiles, then tile t0's data
 #pragma unroll
-    for (int k = ht; k < 16; k += HT) {
-      const int v0 = __builtin_amdgcn_readlane(ix_lane, 2 * k);
-      const int v1 = __builtin_amdgcn_readlane(ix_lane, 2 * k + 1);
-      const int tau = 2 * k + (lane >> 5);
-      const uint8_t* rec = record_ptr(p.kv, (lane >> 5) ? v1 : v0);
-      dma16(rec + 16 * ((lane & 31) ^ tau), base + 1024 * k);
-    }
-  };
-  auto load_side = [&](int ix_lane, Side& sd) {
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const uint8_t* rec = record_ptr(p.kv, __shfl(ix_lane, 16 * s + t));
-      sd.sc[s] = *(const v4f*)(rec + kScaleOff);
-      sd.rp[s][0] = *(const v4i*)(rec + kRopeOff + 16 * g);
-      sd.rp[s][1] = *(const v4i*)(rec + kRopeOff + 64 + 16 * g);
-    }
-  };
+  for (int k = 0; k < kIdxAhead - 1; ++k) issue_idx(t0 + k);
+  wait_vm_all();
+  if (HT > 1) __syncthreads();
+  fill_table(t0);
+  fill_table(t0 + 1);
+  issue_latent(t0, 0);
+  issue_side(t0, 0);
+  issue_prefetch(t0 + 1);
+  issue_idx(t0 + kIdxAhead - 1);
 
-  float m_run = -INFINITY;
-  float l_run = 0.0f;
+  float m_ref = -INFINITY;  // reference max (log2 units) of P and O
+  float l_run = 0.0f;       // this lane's share of sum P
   v4f O[32];
 #pragma unroll
   for (int i = 0; i < 32; ++i) O[i] = v4f{0, 0, 0, 0};
 
-  int raw_cur = load_raw(t0);
-  {
-    const int ix0 = masked(raw_cur, t0);
-    issue_dma(ix0, 0);
-  }
-  Side sd_next;
-  load_side(masked(raw_cur, t0), sd_next);
-  int raw_next = load_raw(t0 + 1);
-
   // PV transposed-read lane address: lane (t, g) reads token row j = t/2,
-  // tau_j = 16(j/4) + 4g + j%4, byte half t%2; the dim chunk dt is XORed in.
+  // tau_j = 16(j/4) + 4g + j%4, byte half t%2; dim chunk dt is an immediate offset.
   const int jrow = t >> 1;
   const int tau_v = 16 * (jrow >> 2) + 4 * g + (jrow & 3);
-  const uint32_t v_off = 512 * tau_v + 16 * tau_v + 8 * (t & 1);
+  const uint32_t v_off = kLatRow * tau_v + 8 * (t & 1);
 
   for (int n = t0; n < t1; ++n) {
     const int st = (n - t0) & 1;
-    wait_vm_all();            // tile n's DMA and side data have landed
-    if (HT > 1) __syncthreads();  // ... for every wave sharing the tile
-    const int ix_n = masked(raw_cur, n);
-    const Side sd = sd_next;
-    if (n + 1 < t1) {         // prefetch tile n+1 into the other stage
-      const int ix1 = masked(raw_next, n + 1);
-      issue_dma(ix1, st ^ 1);
-      load_side(ix1, sd_next);
-      raw_cur = raw_next;
-      raw_next = load_raw(n + 2);  // bounded read; masked when used
-    }
-    const uint32_t lat = lat0 + st * TG * kWaveLatBytes;
+    const int sst = C::kSideStages == 1 ? 0 : st;
+    // tile n's latent and side data have landed (the later prefetch and index
+    // loads may still be in flight); with several head tiles, for every wave
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(C::kTrailingVm));
+    if (HT > 1) __syncthreads();
+    const int ix_n = ring_ix(n, lane & 31);
     const uint32_t vmask = (uint32_t)__ballot(ix_n >= 0);  // bit tau: token tau is a key
+    const bool more = n + 1 < t1;
+    if (more) issue_latent(n + 1, st ^ 1);
+    fill_table(n + 2);
+
+    const uint32_t lat = lat_at(st);
+    const uint32_t side = side_at(sst);
 
     // ---- QK: S^T tiles; lane (t, g) gets head t, tokens 16s + 4g + r.
     v4f S[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const int tau = 16 * s + t;
-      const uint32_t kb = lat + 512 * tau + 16 * tau;
+      const uint32_t kb = lat + kLatRow * tau + 16 * g;
+      const uint32_t sb = side + kSideTok * tau;
+      v4i kr[8];
+#pragma unroll
+      for (int m = 0; m < 8; ++m) kr[m] = *LDSP(v4i, kb + 64 * m);
+      const v4f ksc = *LDSP(v4f, sb);
+      const v4i rp0 = *LDSP(v4i, sb + 16 + 16 * g);
+      const v4i rp1 = *LDSP(v4i, sb + 80 + 16 * g);
       v4f acc = v4f{0, 0, 0, 0};
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
-        const v4i raw = *LDSP(v4i, kb ^ (16 * (4 * m + g)));
-        const float sc = sd.sc[s][m >> 1];
+        const float sc = ksc[m >> 1];
         v2bf a0, a1, a2, a3, b0, b1, b2, b3;
-        cvt4_bf16(raw.x, sc, a0, a1);
-        cvt4_bf16(raw.y, sc, a2, a3);
-        cvt4_bf16(raw.z, sc, b0, b1);
-        cvt4_bf16(raw.w, sc, b2, b3);
+        cvt4_bf16(kr[m].x, sc, a0, a1);
+        cvt4_bf16(kr[m].y, sc, a2, a3);
+        cvt4_bf16(kr[m].z, sc, b0, b1);
+        cvt4_bf16(kr[m].w, sc, b2, b3);
         const v8bf ka = {a0.x, a0.y, a1.x, a1.y, a2.x, a2.y, a3.x, a3.y};
         const v8bf kb8 = {b0.x, b0.y, b1.x, b1.y, b2.x, b2.y, b3.x, b3.y};
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qlat[2 * m], acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb8, qlat[2 * m + 1], acc, 0, 0, 0);
       }
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, sd.rp[s][i]), qrope[i], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, rp0), qrope[0], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, rp1), qrope[1], acc, 0, 0, 0);
       S[s] = acc;
     }
 
-    // ---- online softmax (log2 domain), per head over this wave's tokens
+    // ---- V scales of this lane's C-layout tokens 16s + 4g + r, clamped to
+    // 2^7 and kept as f16 (exact for the power-of-two scales).  psc[b][k/2]
+    // packs tokens k, k+1 of block b.
+    v2h psc[4][4];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int r = 0; r < 4; r += 2) {
+        const v4f a = *LDSP(v4f, side + kSideTok * (16 * s + 4 * g + r));
+        const v4f b = *LDSP(v4f, side + kSideTok * (16 * s + 4 * g + r + 1));
+#pragma unroll
+        for (int blk = 0; blk < 4; ++blk)
+          psc[blk][(4 * s + r) / 2] = v2h{(_Float16)__builtin_fminf(a[blk], kScaleCap),
+                                          (_Float16)__builtin_fminf(b[blk], kScaleCap)};
+      }
+
+    // ---- next tile's side data (its buffer is free once this tile's side
+    // reads are done), L2 prefetch two tiles ahead, index load five ahead
+    __builtin_amdgcn_sched_barrier(0);
+    if (more) {
+      if (C::kSideStages == 1) __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      issue_side(n + 1, C::kSideStages == 1 ? 0 : (sst ^ 1));
+    }
+    issue_prefetch(n + 2);
+    issue_idx(n + kIdxAhead);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- first half of the V^T reads (independent of the softmax)
+    const uint32_t vaddr = lat + v_off;
+    v2i vr[16];
+#pragma unroll
+    for (int dt = 0; dt < 16; ++dt) vr[dt] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(LDSP(v2i, vaddr + 16 * dt));
+
+    // ---- online softmax (log2 domain).  m_ref only moves when some head's
+    // tile max exceeds it by more than kTau, so P = exp2(x - m_ref + kShift)
+    // stays <= 2^(kShift + kTau) = 2^8 and P' = P * scale (<= 2^7) fits f16.
     float x[8];
     float tmax = -INFINITY;
 #pragma unroll
@@ -398,53 +540,52 @@ __global__ __launch_bounds__(64 * HT * TG, 1) void smla_fwd_kernel(FwdParams p) 
         tmax = fmax_(tmax, v);
       }
     tmax = xor_max(tmax);
-    const float m_new = fmax_(m_run, tmax);
-    const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    float P[8];
-    float psum = 0.0f;
+    if (__builtin_amdgcn_ballot_w64(tmax > m_ref + kTau)) {
+      const float m_new = fmax_(m_ref, tmax);
+      const float alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_ref - m_new);
+      if (__builtin_amdgcn_ballot_w64(m_ref != -INFINITY)) {  // O and l are still zero otherwise
+        l_run *= alpha;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      P[k] = __builtin_amdgcn_exp2f(x[k] - m_use + kPShift);
-      psum += P[k];
+        for (int i = 0; i < 32; ++i) O[i] *= alpha;
+      }
+      m_ref = m_new;
     }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
+    const float m_use = (m_ref == -INFINITY) ? 0.0f : m_ref;
+    v2h ph[4];  // P as f16, token pairs
 #pragma unroll
-    for (int i = 0; i < 32; ++i) O[i] *= alpha;
-
-    // ---- V scales of this lane's 8 tokens (wave-local exchange through LDS)
-    if (g == 0) {
-      s_ks[wave][t] = sd.sc[0];
-      s_ks[wave][16 + t] = sd.sc[1];
+    for (int k = 0; k < 8; k += 2) {
+      const float p0 = __builtin_amdgcn_exp2f(x[k] - m_use + kShift);
+      const float p1 = __builtin_amdgcn_exp2f(x[k + 1] - m_use + kShift);
+      l_run += p0 + p1;
+      ph[k / 2] = v2h{(_Float16)p0, (_Float16)p1};
     }
-    v8h pb[4];  // P' B operands, one per V scale block
-    {
-      v4f scv[8];
+    v8h pb[4];  // P' B operands, one per V scale block: f16(P) * scale (a power of two)
 #pragma unroll
-      for (int s = 0; s < 2; ++s)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) scv[4 * s + r] = s_ks[wave][16 * s + 4 * g + r];
-#pragma unroll
-      for (int b = 0; b < 4; ++b)
-#pragma unroll
-        for (int k = 0; k < 8; ++k)
-          pb[b][k] = (_Float16)(P[k] * __builtin_fminf(scv[k][b], kScaleCap));
+    for (int b = 0; b < 4; ++b) {
+      const v2h q0 = ph[0] * psc[b][0], q1 = ph[1] * psc[b][1];
+      const v2h q2 = ph[2] * psc[b][2], q3 = ph[3] * psc[b][3];
+      pb[b] = v8h{q0.x, q0.y, q1.x, q1.y, q2.x, q2.y, q3.x, q3.y};
     }
 
     // ---- PV: O^T[d, h] += V^T[d, tok] P'^T[tok, h] over the wave's 32 tokens
+    v2i vr2[16];
 #pragma unroll
-    for (int dt = 0; dt < 32; ++dt) {
-      const v2i raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(LDSP(v2i, (lat + v_off) ^ (16 * dt)));
-      O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(cvt8_f16(raw), pb[dt >> 3], O[dt], 0, 0, 0);
-    }
+    for (int dt = 0; dt < 16; ++dt)
+      vr2[dt] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(LDSP(v2i, vaddr + 16 * (dt + 16)));
+#pragma unroll
+    for (int dt = 0; dt < 16; ++dt)
+      O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(cvt8_f16(vr[dt]), pb[dt >> 3], O[dt], 0, 0, 0);
+#pragma unroll
+    for (int dt = 0; dt < 16; ++dt)
+      O[16 + dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(cvt8_f16(vr2[dt]), pb[2 + (dt >> 3)], O[16 + dt], 0, 0, 0);
   }
+  wait_vm_all();  // drain the trailing prefetch / index DMA before LDS is reused
 
   // ---- epilogue
   l_run = xor_sum(l_run);  // lane (t, *) now holds head t's sum over this wave's tokens
   if constexpr (TG == 1) {
     const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;
-    const float l2 = l_run > 0.0f ? m_run + __builtin_log2f(l_run) - kPShift : -INFINITY;
+    const float l2 = l_run > 0.0f ? m_ref + __builtin_log2f(l_run) - kShift : -INFINITY;
     if (h_ok) {
       if (split) {
         float* po = p.part_o + ((int64_t)unit * p.H + h) * kLat;
@@ -466,36 +607,41 @@ __global__ __launch_bounds__(64 * HT * TG, 1) void smla_fwd_kernel(FwdParams p) 
   } else {
     // token groups of a head tile merge through LDS: weights 2^(m_own - M)
     if (g == 0) {
-      s_m[wave][t] = m_run;
+      s_m[wave][t] = m_ref;
       s_l[wave][t] = l_run;
     }
-    __syncthreads();  // every wave is done with the stage buffers
+    __syncthreads();  // every wave is done with the stream buffers
+    // statistics of head t over the token groups (every lane, for its head)
     float M = -INFINITY;
 #pragma unroll
     for (int k = 0; k < TG; ++k) M = fmax_(M, s_m[k * HT + ht][t]);
-    const float w_own = (m_run == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run - M);
+    float L = 0.0f;
+#pragma unroll
+    for (int k = 0; k < TG; ++k) {
+      const float mk = s_m[k * HT + ht][t];
+      if (mk != -INFINITY) L += s_l[k * HT + ht][t] * __builtin_amdgcn_exp2f(mk - M);
+    }
+    const float w_own = (m_ref == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_ref - M);
+    const float inv_h = L > 0.0f ? 1.0f / L : 0.0f;
+    const float l2_h = L > 0.0f ? M + __builtin_log2f(L) - kShift : -INFINITY;
     float* mrg = (float*)s_big;
     float* mine = mrg + ((tg * HT + ht) * 16 + t) * kMergeRow;
 #pragma unroll
-    for (int dt = 0; dt < 32; ++dt) *(v4f*)(mine + 16 * dt + 4 * g) = O[dt] * w_own;
+    for (int dt = 0; dt < 32; ++dt) *(v4f*)(mine + 16 * dt + 4 * g) = O[dt] * (w_own * inv_h);
+    // this wave's heads' lse (one token group writes it)
+    if (tg == 0 && g == 0 && h_ok) {
+      if (split) p.part_lse[(int64_t)unit * p.H + h] = l2_h;
+      else if (p.lse) p.lse[(int64_t)row * p.H + h] = l2_h * kLn2;
+    }
     __syncthreads();
-    constexpr int kDpw = kLat / TG;     // dims this wave reduces
-    constexpr int kDpl = kDpw / 64;     // dims per lane (2 or 4)
+    // wave (ht, tg) sums dims [tg * 512/TG, ...) of its 16 heads over the groups
+    constexpr int kDpw = kLat / TG;  // dims this wave reduces
+    constexpr int kDpl = kDpw / 64;  // dims per lane (2 or 4)
     const int d0 = tg * kDpw + lane * kDpl;
-    for (int hh = 0; hh < 16; ++hh) {
+    const int hmax = min(16, p.H - 16 * ht);
+#pragma unroll 4
+    for (int hh = 0; hh < hmax; ++hh) {
       const int hd = 16 * ht + hh;
-      if (hd >= p.H) break;
-      float Mh = -INFINITY;
-#pragma unroll
-      for (int k = 0; k < TG; ++k) Mh = fmax_(Mh, s_m[k * HT + ht][hh]);
-      float L = 0.0f;
-#pragma unroll
-      for (int k = 0; k < TG; ++k) {
-        const float mk = s_m[k * HT + ht][hh];
-        if (mk != -INFINITY) L += s_l[k * HT + ht][hh] * __builtin_amdgcn_exp2f(mk - Mh);
-      }
-      const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-      const float l2 = L > 0.0f ? Mh + __builtin_log2f(L) - kPShift : -INFINITY;
       float acc[kDpl];
 #pragma unroll
       for (int e = 0; e < kDpl; ++e) acc[e] = 0.0f;
@@ -507,17 +653,17 @@ __global__ __launch_bounds__(64 * HT * TG, 1) void smla_fwd_kernel(FwdParams p) 
       }
       if (split) {
         float* po = p.part_o + ((int64_t)unit * p.H + hd) * kLat + d0;
-#pragma unroll
-        for (int e = 0; e < kDpl; ++e) po[e] = acc[e] * inv;
-        if (tg == 0 && lane == 0) p.part_lse[(int64_t)unit * p.H + hd] = l2;
+        if constexpr (kDpl == 2) *(v2f*)po = v2f{acc[0], acc[1]};
+        else *(v4f*)po = v4f{acc[0], acc[1], acc[2], acc[3]};
       } else {
         uint16_t* po = p.out + row * p.o_st + hd * p.o_sh + d0;
-#pragma unroll
-        for (int e = 0; e < kDpl; e += 2) {
-          const uint32_t w = f32_to_bf16_rne(acc[e] * inv) | ((uint32_t)f32_to_bf16_rne(acc[e + 1] * inv) << 16);
-          *(uint32_t*)(po + e) = w;
+        if constexpr (kDpl == 2) {
+          *(uint32_t*)po = f32_to_bf16_rne(acc[0]) | ((uint32_t)f32_to_bf16_rne(acc[1]) << 16);
+        } else {
+          const uint32_t w0 = f32_to_bf16_rne(acc[0]) | ((uint32_t)f32_to_bf16_rne(acc[1]) << 16);
+          const uint32_t w1 = f32_to_bf16_rne(acc[2]) | ((uint32_t)f32_to_bf16_rne(acc[3]) << 16);
+          *(v2i*)po = v2i{(int)w0, (int)w1};
         }
-        if (tg == 0 && lane == 0 && p.lse) p.lse[(int64_t)row * p.H + hd] = l2 * kLn2;
       }
     }
   }
@@ -527,23 +673,33 @@ __global__ __launch_bounds__(64 * HT * TG, 1) void smla_fwd_kernel(FwdParams p) 
 
 // LSE merge of a split row's chunks (K2-back page, stage_combine, without the
 // sink): M = max_c lse2_c, w_c = 2^(lse2_c - M), out = sum w_c o_c / sum w_c.
-__global__ __launch_bounds__(128) void smla_combine_kernel(CombineParams p) {
-  int rank, h;
-  xcd_unit(p.H, rank, h);
-  if (rank >= p.T) return;
-  const int row = p.order[rank];
+// All chunk loads are issued before any is used.
+template <int SMAX>
+__device__ __forceinline__ void combine_row(const CombineParams& p, int row, int h) {
   const int64_t u0 = (int64_t)row * p.S;
+  float lc[SMAX];
+  v4f oc[SMAX];
+#pragma unroll
+  for (int c = 0; c < SMAX; ++c) {
+    if (c < p.S) {
+      lc[c] = p.part_lse[(u0 + c) * p.H + h];
+      oc[c] = *(const v4f*)(p.part_o + ((u0 + c) * p.H + h) * kLat + 4 * threadIdx.x);
+    }
+  }
   float M = -INFINITY;
-  for (int c = 0; c < p.S; ++c) M = fmax_(M, p.part_lse[(u0 + c) * p.H + h]);
+#pragma unroll
+  for (int c = 0; c < SMAX; ++c)
+    if (c < p.S) M = fmax_(M, lc[c]);
   v4f acc = v4f{0, 0, 0, 0};
   float L = 0.0f;
   if (M != -INFINITY) {
-    for (int c = 0; c < p.S; ++c) {
-      const float lc = p.part_lse[(u0 + c) * p.H + h];
-      if (lc == -INFINITY) continue;
-      const float w = __builtin_amdgcn_exp2f(lc - M);
-      L += w;
-      acc += w * *(const v4f*)(p.part_o + ((u0 + c) * p.H + h) * kLat + 4 * threadIdx.x);
+#pragma unroll
+    for (int c = 0; c < SMAX; ++c) {
+      if (c < p.S && lc[c] != -INFINITY) {  // an empty chunk's o_c was never written
+        const float w = __builtin_amdgcn_exp2f(lc[c] - M);
+        L += w;
+        acc += w * oc[c];
+      }
     }
   }
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
@@ -553,6 +709,17 @@ __global__ __launch_bounds__(128) void smla_combine_kernel(CombineParams p) {
   *(v2i*)(p.out + row * p.o_st + h * p.o_sh + 4 * threadIdx.x) = v2i{(int)w0, (int)w1};
   if (threadIdx.x == 0 && p.lse)
     p.lse[(int64_t)row * p.H + h] = L > 0.0f ? (M + __builtin_log2f(L)) * kLn2 : -INFINITY;
+}
+
+__global__ __launch_bounds__(128) void smla_combine_kernel(CombineParams p) {
+  int rank, h;
+  xcd_unit(p.H, rank, h);
+  if (rank >= p.T) return;
+  const int row = p.order[rank];
+  if (p.S <= 4) combine_row<4>(p, row, h);
+  else if (p.S <= 8) combine_row<8>(p, row, h);
+  else if (p.S <= 16) combine_row<16>(p, row, h);
+  else combine_row<32>(p, row, h);
 }
 
 // ---------------------------------------------------------------- decode hook
@@ -599,9 +766,20 @@ __global__ __launch_bounds__(64) void smla_decode_rows_kernel(const uint8_t* kv,
 
 // ---------------------------------------------------------------- launchers
 
+hipError_t zero_record_address(const uint8_t** out) {
+  void* ptr = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(g_zero_record));
+  *out = (const uint8_t*)ptr;
+  return e;
+}
+
 hipError_t launch_plan(const PlanParams& p, hipStream_t s) {
-  const int blocks = (p.T + 3) / 4;
-  hipLaunchKernelGGL(smla_plan_kernel, dim3(blocks), dim3(256), 0, s, p);
+  if (p.has_invalid) {
+    hipLaunchKernelGGL(smla_plan_scan_kernel, dim3((p.T + 3) / 4), dim3(256), 0, s, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(smla_plan_sort_kernel, dim3(1), dim3(1024), 0, s, p);
   return hipGetLastError();
 }
 
