@@ -10,6 +10,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -59,11 +60,16 @@ hipError_t zero_record(const uint8_t** out) {
   return hipSuccess;
 }
 
+// Compute units of the current device (queried once per device).
+std::atomic<int> g_cus[64];
+
 int device_cus() {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (dev >= 0 && dev < 64 && (cus = g_cus[dev].load(std::memory_order_relaxed)) > 0) return cus;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
     return 256;
+  if (dev >= 0 && dev < 64) g_cus[dev].store(cus, std::memory_order_relaxed);
   return cus;
 }
 
@@ -194,10 +200,18 @@ int sparse_mla_fwd(const void* q, int64_t q_stride_t, int64_t q_stride_h,
   int32_t* order = (int32_t*)(ws + L.order);
   const uint32_t idx_bytes = (uint32_t)(nnz * 4);
 
-  smla::PlanParams pp{indptr, indices, idx_bytes, T, smla::tile_tokens(H), has_invalid ? 1 : 0,
-                      row_tiles, order};
-  hipError_t e = timed(0, s, [&] { return smla::launch_plan(pp, s); });
-  if (e != hipSuccess) return hip_fail(e, "plan kernel launch");
+  // Longest-first order only pays when there are more units than CUs (one
+  // forward block fits a CU): otherwise every unit starts at once and the
+  // order cannot shorten the slowest.  Without has_invalid and without an
+  // order there is nothing to plan: the forward reads lengths from indptr.
+  const bool sort = (int64_t)T * L.S > device_cus();
+  hipError_t e = hipSuccess;
+  if (sort || has_invalid) {
+    smla::PlanParams pp{indptr, indices, idx_bytes, T, smla::tile_tokens(H), has_invalid ? 1 : 0,
+                        row_tiles, order};
+    e = timed(0, s, [&] { return smla::launch_plan(pp, sort, s); });
+    if (e != hipSuccess) return hip_fail(e, "plan kernel launch");
+  }
 
   smla::FwdParams fp{};
   fp.q = (const uint16_t*)q;
@@ -216,15 +230,15 @@ int sparse_mla_fwd(const void* q, int64_t q_stride_t, int64_t q_stride_h,
   fp.o_st = o_stride_t;
   fp.o_sh = o_stride_h;
   fp.lse = lse;
-  fp.row_tiles = row_tiles;
-  fp.order = order;
+  fp.row_tiles = (sort || has_invalid) ? row_tiles : nullptr;
+  fp.order = sort ? order : nullptr;
   fp.part_o = (float*)(ws + L.part_o);
   fp.part_lse = (float*)(ws + L.part_lse);
   e = timed(1, s, [&] { return smla::launch_fwd(fp, s); });
   if (e != hipSuccess) return hip_fail(e, "forward kernel launch");
 
   if (L.S > 1) {
-    smla::CombineParams cp{T, H, L.S, order, fp.part_o, fp.part_lse, fp.out, o_stride_t, o_stride_h, lse};
+    smla::CombineParams cp{T, H, L.S, fp.order, fp.part_o, fp.part_lse, fp.out, o_stride_t, o_stride_h, lse};
     e = timed(2, s, [&] { return smla::launch_combine(cp, s); });
     if (e != hipSuccess) return hip_fail(e, "combine kernel launch");
   }

@@ -35,15 +35,15 @@ struct FwdParams {
   uint16_t* out;       // bf16 bits
   int64_t o_st, o_sh;
   float* lse;          // nullable
-  const int32_t* row_tiles;
-  const int32_t* order;
+  const int32_t* row_tiles;  // nullable: tiles from indptr
+  const int32_t* order;      // nullable: rows in their own order
   float* part_o;       // [T*S, H, 512] when S > 1
   float* part_lse;     // [T*S, H]  (log2 units) when S > 1
 };
 
 struct CombineParams {
   int32_t T, H, S;
-  const int32_t* order;
+  const int32_t* order;  // nullable: rows in their own order
   const float* part_o;
   const float* part_lse;
   uint16_t* out;
@@ -56,7 +56,9 @@ inline int head_tiles(int H) { return (H + 15) / 16; }
 inline int token_groups(int H) { int ht = head_tiles(H); return ht >= 3 ? 1 : 4 / ht; }
 inline int tile_tokens(int H) { return kTokensPerWave * token_groups(H); }
 
-hipError_t launch_plan(const PlanParams& p, hipStream_t s);
+// The has_invalid scan (row_tiles) when p.has_invalid; the longest-first sort
+// (order, and row_tiles from indptr when there was no scan) when `sort`.
+hipError_t launch_plan(const PlanParams& p, bool sort, hipStream_t s);
 hipError_t launch_fwd(const FwdParams& p, hipStream_t s);
 // Device address of the library's zero record on the current device.
 hipError_t zero_record_address(const uint8_t** out);

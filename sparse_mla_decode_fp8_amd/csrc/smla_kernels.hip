@@ -93,11 +93,6 @@ __device__ __forceinline__ void dma16_s(const uint8_t* base, uint32_t voff, uint
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :: "v"(voff), "s"(base), "s"(lds_base) : "memory", "m0");
 }
-// 4 bytes per lane from a 64-bit global address into LDS at lds_base + 4*lane.
-__device__ __forceinline__ void dma4(const uint8_t* src, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
-               :: "v"(src), "s"(lds_base) : "memory", "m0");
-}
 // 4 bytes per lane through a bounded buffer descriptor (reads past its size
 // return 0) into LDS at lds_base + 4*lane.
 __device__ __forceinline__ void buf_dma4(__amdgpu_buffer_rsrc_t rsrc, uint32_t voffset, uint32_t lds_base) {
@@ -243,7 +238,6 @@ constexpr int kWaveLatStage = kTokensPerWave * kLatRow;
 constexpr int kSideTok = 144;       // scales (16 B) + rope (128 B) of a record
 constexpr int kSideChunks = 9;
 constexpr int kRing = 8;            // index ring slots (tiles)
-constexpr int kPrefetchInstr = 3;   // 32 tokens x 6 cache lines / 64 lanes
 constexpr int kIdxAhead = 5;        // tile n issues the index load of tile n + 5
 constexpr float kShift = 4.0f;      // P = exp2(x - m_ref + 4)
 constexpr float kTau = 4.0f;        // m_ref moves only when a head's max exceeds it by > 4
@@ -258,17 +252,15 @@ struct FwdCfg {
   static constexpr int kSideBytes = kSideStages * TG * kTokensPerWave * kSideTok;
   static constexpr int kIdxBytes = kRing * TG * kTokensPerWave * 4;
   static constexpr int kTabBytes = 2 * kWaves * kTokensPerWave * 8;  // per-wave record-address tables
-  static constexpr int kJunkBytes = kPrefetchInstr * 256;
   static constexpr int kSideOff = kLatBytes;
   static constexpr int kIdxOff = kSideOff + kSideBytes;
   static constexpr int kTabOff = kIdxOff + kIdxBytes;
-  static constexpr int kJunkOff = kTabOff + kTabBytes;
-  static constexpr int kStreamBytes = kJunkOff + kJunkBytes;
+  static constexpr int kStreamBytes = kTabOff + kTabBytes;
   static constexpr int kMergeBytes = TG > 1 ? TG * HT * 16 * kMergeRow * 4 : 0;
   static constexpr int kBigBytes = kStreamBytes > kMergeBytes ? kStreamBytes : kMergeBytes;
   // vector-memory instructions a wave issues after a tile's latent and side
-  // DMA and before the next tile's wait: the L2 prefetch and one index load
-  static constexpr int kTrailingVm = kPrefetchInstr + 1;
+  // DMA and before the next tile's wait: one index load
+  static constexpr int kTrailingVm = 1;
 };
 
 template <int HT, int TG>
@@ -290,10 +282,13 @@ __global__ __launch_bounds__(64 * HT * TG, 1) void smla_fwd_kernel(FwdParams p) 
   int rank, chunk;
   xcd_unit(p.S, rank, chunk);
   if (rank >= p.T) return;
-  const int row = p.order[rank];
+  // Without a plan the rows run in their own order and a row's tiles follow
+  // from indptr; with one, order[] is longest first and row_tiles[] is the
+  // has_invalid scan's (trailing masked entries trimmed) or indptr's count.
+  const int row = p.order ? p.order[rank] : rank;
   const int beg = p.indptr[row];
   const int len = max(p.indptr[row + 1] - beg, 0);
-  const int tiles = p.row_tiles[row];
+  const int tiles = p.row_tiles ? p.row_tiles[row] : (len + C::kTile - 1) / C::kTile;
   const int ct = (tiles + p.S - 1) / p.S;
   const int t0 = min(chunk * ct, tiles);
   const int t1 = min(t0 + ct, tiles);
@@ -318,7 +313,7 @@ __global__ __launch_bounds__(64 * HT * TG, 1) void smla_fwd_kernel(FwdParams p) 
   }
 
   // ---- LDS addresses: latent rows and side data of this wave's token group,
-  // the group's index ring, this wave's record-address tables, a junk slot.
+  // the group's index ring, this wave's record-address tables.
   const uint32_t big = lds_addr(s_big);
   auto lat_at = [&](int st) -> uint32_t { return big + (st * TG + tg) * kWaveLatStage; };
   auto side_at = [&](int st) -> uint32_t {
@@ -330,7 +325,6 @@ __global__ __launch_bounds__(64 * HT * TG, 1) void smla_fwd_kernel(FwdParams p) 
   auto tab_at = [&](int n) -> uint32_t {
     return big + C::kTabOff + ((n & 1) * C::kWaves + wave) * kTokensPerWave * 8;
   };
-  const uint32_t junk = big + C::kJunkOff;
   const __amdgpu_buffer_rsrc_t irs = idx_rsrc(p.indices, p.idx_bytes);
   const uint8_t* const kv = p.kv;
   const uint8_t* const zero = p.zero;
@@ -386,17 +380,6 @@ __global__ __launch_bounds__(64 * HT * TG, 1) void smla_fwd_kernel(FwdParams p) 
       }
     }
   };
-  // D: L2 prefetch of tile n's records (6 lines each) into a junk LDS slot.
-  auto issue_prefetch = [&](int n) {
-    const uint32_t tab = tab_at(n);
-#pragma unroll
-    for (int k = 0; k < kPrefetchInstr; ++k) {
-      const int e = 64 * k + lane;
-      const int tau = e / 6, j = e % 6;
-      const uint8_t* rec = (const uint8_t*)(uintptr_t)*LDSP(uint64_t, tab + 8 * tau);
-      dma4(rec + 128 * j, __builtin_amdgcn_readfirstlane(junk + 256 * k));
-    }
-  };
 
   // ---- q as bf16 B operands.  Latent K-step 2m / 2m+1: dims 64m + 16g + [0..7] / [8..15];
   // rope K-step i: dims 512 + 32i + 8g + [0..7].
@@ -429,7 +412,6 @@ __global__ __launch_bounds__(64 * HT * TG, 1) void smla_fwd_kernel(FwdParams p) 
   fill_table(t0 + 1);
   issue_latent(t0, 0);
   issue_side(t0, 0);
-  issue_prefetch(t0 + 1);
   issue_idx(t0 + kIdxAhead - 1);
 
   float m_ref = -INFINITY;  // reference max (log2 units) of P and O
@@ -447,8 +429,8 @@ __global__ __launch_bounds__(64 * HT * TG, 1) void smla_fwd_kernel(FwdParams p) 
   for (int n = t0; n < t1; ++n) {
     const int st = (n - t0) & 1;
     const int sst = C::kSideStages == 1 ? 0 : st;
-    // tile n's latent and side data have landed (the later prefetch and index
-    // loads may still be in flight); with several head tiles, for every wave
+    // tile n's latent and side data have landed (the later index load may
+    // still be in flight); with several head tiles, for every wave
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(C::kTrailingVm));
     if (HT > 1) __syncthreads();
     const int ix_n = ring_ix(n, lane & 31);
@@ -509,13 +491,12 @@ __global__ __launch_bounds__(64 * HT * TG, 1) void smla_fwd_kernel(FwdParams p) 
       }
 
     // ---- next tile's side data (its buffer is free once this tile's side
-    // reads are done), L2 prefetch two tiles ahead, index load five ahead
+    // reads are done), index load five ahead
     __builtin_amdgcn_sched_barrier(0);
     if (more) {
       if (C::kSideStages == 1) __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
       issue_side(n + 1, C::kSideStages == 1 ? 0 : (sst ^ 1));
     }
-    issue_prefetch(n + 2);
     issue_idx(n + kIdxAhead);
     __builtin_amdgcn_sched_barrier(0);
 
@@ -579,7 +560,7 @@ __global__ __launch_bounds__(64 * HT * TG, 1) void smla_fwd_kernel(FwdParams p) 
     for (int dt = 0; dt < 16; ++dt)
       O[16 + dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(cvt8_f16(vr2[dt]), pb[2 + (dt >> 3)], O[16 + dt], 0, 0, 0);
   }
-  wait_vm_all();  // drain the trailing prefetch / index DMA before LDS is reused
+  wait_vm_all();  // drain the trailing index DMA before LDS is reused
 
   // ---- epilogue
   l_run = xor_sum(l_run);  // lane (t, *) now holds head t's sum over this wave's tokens
@@ -715,7 +696,7 @@ __global__ __launch_bounds__(128) void smla_combine_kernel(CombineParams p) {
   int rank, h;
   xcd_unit(p.H, rank, h);
   if (rank >= p.T) return;
-  const int row = p.order[rank];
+  const int row = p.order ? p.order[rank] : rank;
   if (p.S <= 4) combine_row<4>(p, row, h);
   else if (p.S <= 8) combine_row<8>(p, row, h);
   else if (p.S <= 16) combine_row<16>(p, row, h);
@@ -773,14 +754,17 @@ hipError_t zero_record_address(const uint8_t** out) {
   return e;
 }
 
-hipError_t launch_plan(const PlanParams& p, hipStream_t s) {
+hipError_t launch_plan(const PlanParams& p, bool sort, hipStream_t s) {
   if (p.has_invalid) {
     hipLaunchKernelGGL(smla_plan_scan_kernel, dim3((p.T + 3) / 4), dim3(256), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(smla_plan_sort_kernel, dim3(1), dim3(1024), 0, s, p);
-  return hipGetLastError();
+  if (sort) {
+    hipLaunchKernelGGL(smla_plan_sort_kernel, dim3(1), dim3(1024), 0, s, p);
+    return hipGetLastError();
+  }
+  return hipSuccess;
 }
 
 template <int HT, int TG>
