@@ -113,9 +113,11 @@ int32_t sparse_mla_split_for(int32_t T, int32_t H, int64_t nnz);
  *     give unspecified rows).
  *
  * Returns SMLA_OK, or SMLA_EINVAL / SMLA_EUNSUPPORTED / SMLA_EWORKSPACE /
- * SMLA_EHIP with nothing queued.  Queues on `stream`: the plan (a slice
- * scan when has_invalid, then a one-block longest-first sort), the forward,
- * and a combine when rows are split.  No host sync, no allocation.
+ * SMLA_EHIP with nothing queued.  Queues on `stream`: a slice scan when
+ * has_invalid; a one-block longest-first sort of the rows when there are
+ * more (row, chunk) units than compute units (otherwise every unit starts at
+ * once and rows run in their own order); the forward; and a combine when
+ * rows are split.  No host sync, no allocation.
  * Deterministic for a fixed device and arguments.  nnz must be below
  * 2^30 - 4096 (index reads use 32-bit byte offsets).
  */
@@ -155,8 +157,11 @@ int sparse_mla_set_option(const char* name, int64_t value);
 
 /*
  * Kernel timing for benchmarks.  sparse_mla_profile_begin(max_calls) makes the
- * following forwards (up to max_calls of them, on any stream) record HIP
- * events around each kernel they queue; sparse_mla_profile_end() waits for
+ * following forwards (up to max_calls of them, on any stream) time each kernel
+ * kind they queue with a HIP event pair attached to the kernel dispatches
+ * themselves (hipExtLaunchKernel: start at the first dispatch's start, stop at
+ * the last one's end, so queueing between launches is not counted);
+ * sparse_mla_profile_end() waits for
  * those events, writes the summed device time in milliseconds and the launch
  * count of each kernel kind (0 plan, 1 forward, 2 combine) to ms[3] and
  * launches[3], and stops recording.  Creates and destroys events on the host

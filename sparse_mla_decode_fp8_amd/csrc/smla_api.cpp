@@ -126,24 +126,22 @@ struct Prof {
   std::vector<int> kind;       // per pair
 } g_prof;
 
+// Runs `launch(ev)`; while profiling, ev carries an event pair that the
+// launch attaches to its kernel dispatches (hipExtLaunchKernel), so the pair
+// brackets the kernels' execution and not the queueing around them.
 template <class F>
-hipError_t timed(int kind, hipStream_t s, F&& launch) {
-  int slot = -1;
+hipError_t timed(int kind, F&& launch) {
+  smla::Events ev;
   {
     std::lock_guard<std::mutex> lk(g_prof.mu);
     if (g_prof.active && g_prof.used < g_prof.cap) {
-      slot = g_prof.used++;
+      const int slot = g_prof.used++;
       g_prof.kind[slot] = kind;
+      ev.start = g_prof.ev[2 * slot];
+      ev.stop = g_prof.ev[2 * slot + 1];
     }
   }
-  if (slot >= 0) {
-    hipError_t e = hipEventRecord(g_prof.ev[2 * slot], s);
-    if (e != hipSuccess) return e;
-  }
-  hipError_t e = launch();
-  if (e != hipSuccess) return e;
-  if (slot >= 0) return hipEventRecord(g_prof.ev[2 * slot + 1], s);
-  return hipSuccess;
+  return launch(ev);
 }
 
 }  // namespace
@@ -209,7 +207,7 @@ int sparse_mla_fwd(const void* q, int64_t q_stride_t, int64_t q_stride_h,
   if (sort || has_invalid) {
     smla::PlanParams pp{indptr, indices, idx_bytes, T, smla::tile_tokens(H), has_invalid ? 1 : 0,
                         row_tiles, order};
-    e = timed(0, s, [&] { return smla::launch_plan(pp, sort, s); });
+    e = timed(0, [&](smla::Events ev) { return smla::launch_plan(pp, sort, ev, s); });
     if (e != hipSuccess) return hip_fail(e, "plan kernel launch");
   }
 
@@ -234,12 +232,12 @@ int sparse_mla_fwd(const void* q, int64_t q_stride_t, int64_t q_stride_h,
   fp.order = sort ? order : nullptr;
   fp.part_o = (float*)(ws + L.part_o);
   fp.part_lse = (float*)(ws + L.part_lse);
-  e = timed(1, s, [&] { return smla::launch_fwd(fp, s); });
+  e = timed(1, [&](smla::Events ev) { return smla::launch_fwd(fp, ev, s); });
   if (e != hipSuccess) return hip_fail(e, "forward kernel launch");
 
   if (L.S > 1) {
     smla::CombineParams cp{T, H, L.S, fp.order, fp.part_o, fp.part_lse, fp.out, o_stride_t, o_stride_h, lse};
-    e = timed(2, s, [&] { return smla::launch_combine(cp, s); });
+    e = timed(2, [&](smla::Events ev) { return smla::launch_combine(cp, ev, s); });
     if (e != hipSuccess) return hip_fail(e, "combine kernel launch");
   }
   return SMLA_OK;

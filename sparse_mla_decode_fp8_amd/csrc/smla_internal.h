@@ -56,13 +56,20 @@ inline int head_tiles(int H) { return (H + 15) / 16; }
 inline int token_groups(int H) { int ht = head_tiles(H); return ht >= 3 ? 1 : 4 / ht; }
 inline int tile_tokens(int H) { return kTokensPerWave * token_groups(H); }
 
+// Optional timing events: `start` is attached to the first kernel dispatch of
+// a launch and `stop` to the last (hipExtLaunchKernel); null = untimed.
+struct Events {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+
 // The has_invalid scan (row_tiles) when p.has_invalid; the longest-first sort
 // (order, and row_tiles from indptr when there was no scan) when `sort`.
-hipError_t launch_plan(const PlanParams& p, bool sort, hipStream_t s);
-hipError_t launch_fwd(const FwdParams& p, hipStream_t s);
+hipError_t launch_plan(const PlanParams& p, bool sort, Events ev, hipStream_t s);
+hipError_t launch_fwd(const FwdParams& p, Events ev, hipStream_t s);
 // Device address of the library's zero record on the current device.
 hipError_t zero_record_address(const uint8_t** out);
-hipError_t launch_combine(const CombineParams& p, hipStream_t s);
+hipError_t launch_combine(const CombineParams& p, Events ev, hipStream_t s);
 hipError_t launch_decode_rows(const uint8_t* kv, int64_t n_kv, const int32_t* rows, int64_t n,
                               float* out, hipStream_t s);
 

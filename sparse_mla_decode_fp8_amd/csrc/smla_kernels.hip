@@ -31,6 +31,7 @@
 //    (dispatch is round-robin over the 8 XCDs), so partials and q stay in that
 //    XCD's L2.
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <math.h>
@@ -754,39 +755,42 @@ hipError_t zero_record_address(const uint8_t** out) {
   return e;
 }
 
-hipError_t launch_plan(const PlanParams& p, bool sort, hipStream_t s) {
+hipError_t launch_plan(const PlanParams& p, bool sort, Events ev, hipStream_t s) {
   if (p.has_invalid) {
-    hipLaunchKernelGGL(smla_plan_scan_kernel, dim3((p.T + 3) / 4), dim3(256), 0, s, p);
+    hipExtLaunchKernelGGL(smla_plan_scan_kernel, dim3((p.T + 3) / 4), dim3(256), 0, s, ev.start,
+                          sort ? nullptr : ev.stop, 0, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (sort) {
-    hipLaunchKernelGGL(smla_plan_sort_kernel, dim3(1), dim3(1024), 0, s, p);
+    hipExtLaunchKernelGGL(smla_plan_sort_kernel, dim3(1), dim3(1024), 0, s,
+                          p.has_invalid ? nullptr : ev.start, ev.stop, 0, p);
     return hipGetLastError();
   }
   return hipSuccess;
 }
 
 template <int HT, int TG>
-static hipError_t launch_fwd_t(const FwdParams& p, hipStream_t s) {
+static hipError_t launch_fwd_t(const FwdParams& p, Events ev, hipStream_t s) {
   const int64_t blocks = xcd_grid(p.T, p.S);
-  hipLaunchKernelGGL((smla_fwd_kernel<HT, TG>), dim3((unsigned)blocks), dim3(FwdCfg<HT, TG>::kThreads), 0, s, p);
+  hipExtLaunchKernelGGL((smla_fwd_kernel<HT, TG>), dim3((unsigned)blocks), dim3(FwdCfg<HT, TG>::kThreads), 0, s,
+                        ev.start, ev.stop, 0, p);
   return hipGetLastError();
 }
 
-hipError_t launch_fwd(const FwdParams& p, hipStream_t s) {
+hipError_t launch_fwd(const FwdParams& p, Events ev, hipStream_t s) {
   switch (head_tiles(p.H)) {
-    case 1: return launch_fwd_t<1, 4>(p, s);
-    case 2: return launch_fwd_t<2, 2>(p, s);
-    case 3: return launch_fwd_t<3, 1>(p, s);
-    case 4: return launch_fwd_t<4, 1>(p, s);
+    case 1: return launch_fwd_t<1, 4>(p, ev, s);
+    case 2: return launch_fwd_t<2, 2>(p, ev, s);
+    case 3: return launch_fwd_t<3, 1>(p, ev, s);
+    case 4: return launch_fwd_t<4, 1>(p, ev, s);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_combine(const CombineParams& p, hipStream_t s) {
+hipError_t launch_combine(const CombineParams& p, Events ev, hipStream_t s) {
   const int64_t blocks = xcd_grid(p.T, p.H);
-  hipLaunchKernelGGL(smla_combine_kernel, dim3((unsigned)blocks), dim3(128), 0, s, p);
+  hipExtLaunchKernelGGL(smla_combine_kernel, dim3((unsigned)blocks), dim3(128), 0, s, ev.start, ev.stop, 0, p);
   return hipGetLastError();
 }
 
