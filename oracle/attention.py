@@ -27,22 +27,30 @@ import numpy as np
 from .codec import N_LATENT, bf16_bits_to_f64, decode_records
 
 
-def row_attention(Q: np.ndarray, K: np.ndarray, sigma: float):
+def row_attention(Q: np.ndarray, K: np.ndarray, sigma: float, with_abs: bool = False):
     """Softmax attention of Q [H, 576] over keys K [n, 576], values K[:, :512].
 
     Returns (out [H, 512], lse [H]) in float64; n == 0 gives (0, -inf).
     s = sigma * Q K^T;  m = max_j s;  p = exp(s - m);  l = sum_j p;
     out = p V / l;  lse = m + ln l.
+    with_abs: also return A = p |V| / l, the softmax-weighted mean of |V| per
+    output element (0 for n == 0).  It scales the rounding error of any
+    evaluation that rounds the weights p to a short format before the p V
+    product (the tests' error bound uses it).
     """
     H = Q.shape[0]
     if K.shape[0] == 0:
-        return np.zeros((H, N_LATENT)), np.full(H, -np.inf)
+        empty = (np.zeros((H, N_LATENT)), np.full(H, -np.inf))
+        return empty + (np.zeros((H, N_LATENT)),) if with_abs else empty
     s = sigma * (Q @ K.T)  # [H, n]
     m = s.max(axis=1, keepdims=True)
     p = np.exp(s - m)
     l = p.sum(axis=1)
     out = (p @ K[:, :N_LATENT]) / l[:, None]
-    return out, m[:, 0] + np.log(l)
+    lse = m[:, 0] + np.log(l)
+    if with_abs:
+        return out, lse, (p @ np.abs(K[:, :N_LATENT])) / l[:, None]
+    return out, lse
 
 
 def _row_keys(kv: np.ndarray, slice_: np.ndarray) -> np.ndarray:
@@ -53,7 +61,7 @@ def _row_keys(kv: np.ndarray, slice_: np.ndarray) -> np.ndarray:
 
 
 def sparse_mla_fwd(q_bits: np.ndarray, kv: np.ndarray, indptr: np.ndarray,
-                   indices: np.ndarray, sm_scale: float, rows=None):
+                   indices: np.ndarray, sm_scale: float, rows=None, with_abs: bool = False):
     """Oracle forward.
 
     q_bits  : bf16 bit patterns [T, H, 576] (uint16 or int16)
@@ -62,7 +70,8 @@ def sparse_mla_fwd(q_bits: np.ndarray, kv: np.ndarray, indptr: np.ndarray,
     sm_scale: the f32 value the C ABI receives (used as float64)
     rows    : optional iterable of row numbers to compute (others stay NaN)
 
-    Returns (out float64 [T, H, 512], lse float64 [T, H]).
+    Returns (out float64 [T, H, 512], lse float64 [T, H]), and with with_abs
+    also A float64 [T, H, 512] (see row_attention).
     """
     q_bits = np.asarray(q_bits)
     T, H, D = q_bits.shape
@@ -73,12 +82,16 @@ def sparse_mla_fwd(q_bits: np.ndarray, kv: np.ndarray, indptr: np.ndarray,
     sigma = float(np.float32(sm_scale))
     out = np.full((T, H, N_LATENT), np.nan)
     lse = np.full((T, H), np.nan)
+    absw = np.full((T, H, N_LATENT), np.nan) if with_abs else None
     for r in (range(T) if rows is None else rows):
         b, e = int(indptr[r]), int(indptr[r + 1])
         sl = indices[b:e] if e > b else indices[0:0]
         K = _row_keys(kv, sl)
-        out[r], lse[r] = row_attention(bf16_bits_to_f64(q_bits[r]), K, sigma)
-    return out, lse
+        res = row_attention(bf16_bits_to_f64(q_bits[r]), K, sigma, with_abs=with_abs)
+        out[r], lse[r] = res[0], res[1]
+        if with_abs:
+            absw[r] = res[2]
+    return (out, lse, absw) if with_abs else (out, lse)
 
 
 def lse_merge(parts):

@@ -34,6 +34,7 @@
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <type_traits>
 #include <math.h>
 
 #include "smla_internal.h"
@@ -48,6 +49,7 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef _Float16 v4h __attribute__((ext_vector_type(4)));
 
 #define LDSP(T, off) ((__attribute__((address_space(3))) T*)(uintptr_t)(off))
 
@@ -58,7 +60,6 @@ constexpr int kWaveLatBytes = kTokensPerWave * kLat;  // 16 KiB per wave per sta
 constexpr float kPShift = 8.0f;
 constexpr float kScaleCap = 128.0f;  // 2^7: P' = P * scale <= 2^15 fits f16
 constexpr float kLn2 = 0.693147180559945309f;
-constexpr int kMergeRow = kLat + 4;  // padded f32 row of the LDS merge area
 
 // A record of zeros: masked positions gather it, so they read finite data
 // (V = 0, scale = 0) wherever the cache is, and never address row 0.
@@ -257,7 +258,8 @@ struct FwdCfg {
   static constexpr int kIdxOff = kSideOff + kSideBytes;
   static constexpr int kTabOff = kIdxOff + kIdxBytes;
   static constexpr int kStreamBytes = kTabOff + kTabBytes;
-  static constexpr int kMergeBytes = TG > 1 ? TG * HT * 16 * kMergeRow * 4 : 0;
+  // merge area: per wave, its 32 accumulator slices (64 lanes x 16 B each)
+  static constexpr int kMergeBytes = TG > 1 ? kWaves * 32 * 64 * 16 : 0;
   static constexpr int kBigBytes = kStreamBytes > kMergeBytes ? kStreamBytes : kMergeBytes;
   // vector-memory instructions a wave issues after a tile's latent and side
   // DMA and before the next tile's wait: one index load
@@ -382,8 +384,21 @@ __global__ __launch_bounds__(64 * HT * TG, 1) void smla_fwd_kernel(FwdParams p) 
     }
   };
 
-  // ---- q as bf16 B operands.  Latent K-step 2m / 2m+1: dims 64m + 16g + [0..7] / [8..15];
-  // rope K-step i: dims 512 + 32i + 8g + [0..7].
+  // ---- prologue: indices of the first tiles, then tile t0's data
+#pragma unroll
+  for (int k = 0; k < kIdxAhead - 1; ++k) issue_idx(t0 + k);
+  wait_vm_all();
+  if (HT > 1) __syncthreads();
+  fill_table(t0);
+  fill_table(t0 + 1);
+  issue_latent(t0, 0);
+  issue_side(t0, 0);
+  issue_idx(t0 + kIdxAhead - 1);
+  // ---- q as bf16 B operands.  Loaded after tile t0's gather is queued, so
+  // they delay neither the index fetch nor the first records, and waited for
+  // together with tile t0 (so the loop sees them complete).  Latent K-step
+  // 2m / 2m+1: dims 64m + 16g + [0..7] / [8..15]; rope K-step i: dims
+  // 512 + 32i + 8g + [0..7].
   v8bf qlat[16];
   v8bf qrope[2];
   {
@@ -403,17 +418,7 @@ __global__ __launch_bounds__(64 * HT * TG, 1) void smla_fwd_kernel(FwdParams p) 
       qrope[i] = __builtin_bit_cast(v8bf, a);
     }
   }
-
-  // ---- prologue: indices of the first tiles, then tile t0's data
-#pragma unroll
-  for (int k = 0; k < kIdxAhead - 1; ++k) issue_idx(t0 + k);
   wait_vm_all();
-  if (HT > 1) __syncthreads();
-  fill_table(t0);
-  fill_table(t0 + 1);
-  issue_latent(t0, 0);
-  issue_side(t0, 0);
-  issue_idx(t0 + kIdxAhead - 1);
 
   float m_ref = -INFINITY;  // reference max (log2 units) of P and O
   float l_run = 0.0f;       // this lane's share of sum P
@@ -587,7 +592,10 @@ __global__ __launch_bounds__(64 * HT * TG, 1) void smla_fwd_kernel(FwdParams p) 
       }
     }
   } else {
-    // token groups of a head tile merge through LDS: weights 2^(m_own - M)
+    // token groups of a head tile merge through LDS.  Group tg owns the
+    // accumulator slices dt in [tg * 32/TG, (tg + 1) * 32/TG) of its heads:
+    // it writes its other slices (weighted by 2^(m_own - M) / L) for their
+    // owners, then adds the other groups' copies of its own slices.
     if (g == 0) {
       s_m[wave][t] = m_ref;
       s_l[wave][t] = l_run;
@@ -606,46 +614,369 @@ __global__ __launch_bounds__(64 * HT * TG, 1) void smla_fwd_kernel(FwdParams p) 
     const float w_own = (m_ref == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_ref - M);
     const float inv_h = L > 0.0f ? 1.0f / L : 0.0f;
     const float l2_h = L > 0.0f ? M + __builtin_log2f(L) - kShift : -INFINITY;
-    float* mrg = (float*)s_big;
-    float* mine = mrg + ((tg * HT + ht) * 16 + t) * kMergeRow;
+    const float wsc = w_own * inv_h;
+    constexpr int kOwn = 32 / TG;
+    v4f* const mrg = (v4f*)s_big;  // [HT][TG][32 slices][64 lanes]
+    auto slot = [&](int src, int dt) -> v4f* { return mrg + (((ht * TG + src) * 32 + dt) * 64 + lane); };
 #pragma unroll
-    for (int dt = 0; dt < 32; ++dt) *(v4f*)(mine + 16 * dt + 4 * g) = O[dt] * (w_own * inv_h);
+    for (int dt = 0; dt < 32; ++dt)
+      if (dt / kOwn != tg) *slot(tg, dt) = O[dt] * wsc;
     // this wave's heads' lse (one token group writes it)
     if (tg == 0 && g == 0 && h_ok) {
       if (split) p.part_lse[(int64_t)unit * p.H + h] = l2_h;
       else if (p.lse) p.lse[(int64_t)row * p.H + h] = l2_h * kLn2;
     }
     __syncthreads();
-    // wave (ht, tg) sums dims [tg * 512/TG, ...) of its 16 heads over the groups
-    constexpr int kDpw = kLat / TG;  // dims this wave reduces
-    constexpr int kDpl = kDpw / 64;  // dims per lane (2 or 4)
-    const int d0 = tg * kDpw + lane * kDpl;
-    const int hmax = min(16, p.H - 16 * ht);
-#pragma unroll 4
-    for (int hh = 0; hh < hmax; ++hh) {
-      const int hd = 16 * ht + hh;
-      float acc[kDpl];
+    // owner: slice dt of head t holds dims 16 dt + 4 g + [0..3]
+    auto finish = [&](auto own) {
+      constexpr int q = decltype(own)::value;
 #pragma unroll
-      for (int e = 0; e < kDpl; ++e) acc[e] = 0.0f;
+      for (int j = 0; j < kOwn; ++j) {
+        const int dt = q * kOwn + j;
+        v4f acc = O[dt] * wsc;
 #pragma unroll
-      for (int k = 0; k < TG; ++k) {
-        const float* src = mrg + ((k * HT + ht) * 16 + hh) * kMergeRow + d0;
-#pragma unroll
-        for (int e = 0; e < kDpl; ++e) acc[e] += src[e];
-      }
-      if (split) {
-        float* po = p.part_o + ((int64_t)unit * p.H + hd) * kLat + d0;
-        if constexpr (kDpl == 2) *(v2f*)po = v2f{acc[0], acc[1]};
-        else *(v4f*)po = v4f{acc[0], acc[1], acc[2], acc[3]};
-      } else {
-        uint16_t* po = p.out + row * p.o_st + hd * p.o_sh + d0;
-        if constexpr (kDpl == 2) {
-          *(uint32_t*)po = f32_to_bf16_rne(acc[0]) | ((uint32_t)f32_to_bf16_rne(acc[1]) << 16);
+        for (int src = 0; src < TG; ++src)
+          if (src != q) acc += *slot(src, dt);
+        if (!h_ok) continue;
+        if (split) {
+          *(v4f*)(p.part_o + ((int64_t)unit * p.H + h) * kLat + 16 * dt + 4 * g) = acc;
         } else {
-          const uint32_t w0 = f32_to_bf16_rne(acc[0]) | ((uint32_t)f32_to_bf16_rne(acc[1]) << 16);
-          const uint32_t w1 = f32_to_bf16_rne(acc[2]) | ((uint32_t)f32_to_bf16_rne(acc[3]) << 16);
-          *(v2i*)po = v2i{(int)w0, (int)w1};
+          const uint32_t w0 = f32_to_bf16_rne(acc.x) | ((uint32_t)f32_to_bf16_rne(acc.y) << 16);
+          const uint32_t w1 = f32_to_bf16_rne(acc.z) | ((uint32_t)f32_to_bf16_rne(acc.w) << 16);
+          *(v2i*)(p.out + row * p.o_st + h * p.o_sh + 16 * dt + 4 * g) = v2i{(int)w0, (int)w1};
         }
+      }
+    };
+    if (tg == 0) finish(std::integral_constant<int, 0>{});
+    else if (tg == 1) finish(std::integral_constant<int, 1 % TG>{});
+    else if (tg == 2) finish(std::integral_constant<int, 2 % TG>{});
+    else finish(std::integral_constant<int, 3 % TG>{});
+  }
+}
+
+// ---------------------------------------------------------------- forward, H <= 16
+
+// One block of 8 waves (two per SIMD) per unit; tiles of 128 tokens.
+//   QK: wave w scores tokens 16w .. 16w+15 of the tile for all 16 heads.
+//   PV: wave w accumulates output dims 64w .. 64w+63 (half a scale block, so
+//       the V scale folds into P) over all 128 tokens, and the softmax sum of
+//       every head from the same f16 P it multiplies.
+// P, the per-token V scales and the per-wave tile maxima go through LDS, with
+// two barriers per tile; no merge is needed at the end.
+namespace n16 {
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kTile = 128;
+constexpr int kPair = 2 * kLat + 16;             // two latent rows + 16-B pad
+constexpr int kLatStage = (kTile / 2) * kPair;   // 66560 B
+constexpr int kSide = 144;                       // scales (16 B) + rope (128 B)
+constexpr int kIdxRing = 4;                         // index ring slots (tiles)
+constexpr int kLatOff = 0;
+constexpr int kSideOff = kLatOff + 2 * kLatStage;
+constexpr int kPxOff = kSideOff + kTile * kSide;  // P, f16 [head 16][token 128]
+constexpr int kSxOff = kPxOff + 16 * kTile * 2;   // V scales, f16 [block 4][token 128]
+constexpr int kMxOff = kSxOff + 4 * kTile * 2;    // tile maxima, f32 [head 16][wave 8]
+constexpr int kIdxRingOff = kMxOff + 16 * kWaves * 4;
+constexpr int kTabOff = kIdxRingOff + kIdxRing * kTile * 4;  // record addresses [2][token 128]
+constexpr int kBytes = kTabOff + 2 * kTile * 8;
+static_assert(kBytes <= 160 * 1024, "LDS budget");
+
+// Byte offset of token tau's latent row inside a stage.  Rows come in pairs
+// (2 x 512 B, then a 16-B pad); the odd row of a pair stores chunk c (16 B)
+// at position c ^ 8.  With the 1040-B pair stride both the QK reads (16
+// tokens, one chunk column) and the transposed PV reads spread over all banks.
+__device__ __forceinline__ uint32_t row_off(int tau) { return (tau >> 1) * kPair + (tau & 1) * kLat; }
+}  // namespace n16
+
+__global__ __launch_bounds__(n16::kThreads, 1) void smla_fwd16_kernel(FwdParams p) {
+  using namespace n16;
+  __shared__ __attribute__((aligned(1024))) uint8_t s_lds[kBytes];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int t = lane & 15;
+  const int g = lane >> 4;
+
+  int rank, chunk;
+  xcd_unit(p.S, rank, chunk);
+  if (rank >= p.T) return;
+  const int row = p.order ? p.order[rank] : rank;
+  const int beg = p.indptr[row];
+  const int len = max(p.indptr[row + 1] - beg, 0);
+  const int tiles = p.row_tiles ? p.row_tiles[row] : (len + kTile - 1) / kTile;
+  const int ct = (tiles + p.S - 1) / p.S;
+  const int t0 = min(chunk * ct, tiles);
+  const int t1 = min(t0 + ct, tiles);
+  const int unit = row * p.S + chunk;
+  const bool split = p.S > 1;
+  const int h = t;  // head of this lane in QK (C column) and PV (B column)
+  const bool h_ok = h < p.H;
+
+  if (t0 >= t1) {  // nothing to attend: zero output / -inf lse, or an empty partial
+    if (split) {
+      for (int hh = tid; hh < p.H; hh += kThreads) p.part_lse[(int64_t)unit * p.H + hh] = -INFINITY;
+    } else {
+      for (int e = tid; e < p.H * (kLat / 8); e += kThreads) {
+        const int hh = e / (kLat / 8), d = (e % (kLat / 8)) * 8;
+        *(v4i*)(p.out + row * p.o_st + hh * p.o_sh + d) = v4i{0, 0, 0, 0};
+      }
+      if (p.lse)
+        for (int hh = tid; hh < p.H; hh += kThreads) p.lse[(int64_t)row * p.H + hh] = -INFINITY;
+    }
+    return;
+  }
+
+  const uint32_t base = lds_addr(s_lds);
+  const __amdgpu_buffer_rsrc_t irs = idx_rsrc(p.indices, p.idx_bytes);
+  const uint8_t* const kv = p.kv;
+  const uint8_t* const zero = p.zero;
+  auto lat_at = [&](int st) -> uint32_t { return base + kLatOff + st * kLatStage; };
+  auto ring_at = [&](int n) -> uint32_t { return base + kIdxRingOff + (n & (kIdxRing - 1)) * kTile * 4; };
+  auto tab_at = [&](int n) -> uint32_t { return base + kTabOff + (n & 1) * kTile * 8; };
+  const uint32_t side_w = base + kSideOff + 16 * w * kSide;  // this wave's 16 tokens
+  // Every wave touches only its own 16 entries of the index ring, the address
+  // table and the side area, so those need no barrier.
+
+  // Index of this wave's token j (0..15) in tile n, -1 past the row.
+  // Positions past nnz read 0 (bounded reads) and are masked here.
+  auto ring_ix = [&](int n, int j) -> int {
+    const int raw = *LDSP(int, ring_at(n) + 4 * (16 * w + j));
+    return (n * kTile + 16 * w + j < len) ? raw : -1;
+  };
+  auto rec_of = [&](int ix) -> const uint8_t* { return ix >= 0 ? kv + (int64_t)ix * kRecordBytes : zero; };
+  // index DMA of tile n: this wave's 16 entries (lanes 0..15)
+  auto issue_idx = [&](int n) {
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(ring_at(n) + 64 * w);
+    if (lane < 16) buf_dma4(irs, (uint32_t)(beg + n * kTile + 16 * w + lane) * 4u, dst);
+  };
+  // record addresses of this wave's tokens of tile n; tiles at or past t1 get the zero record
+  auto fill_table = [&](int n) {
+    if (lane < 16) {
+      const int ix = n < t1 ? ring_ix(n, lane) : -1;
+      *LDSP(uint64_t, tab_at(n) + 8 * (16 * w + lane)) = (uint64_t)(uintptr_t)rec_of(ix);
+    }
+  };
+  // latent DMA of this wave's 16 tokens of tile n into stage st: one
+  // instruction per token pair, lanes 0..31 the even token, 32..63 the odd one
+  // (lane position p of the odd row loads chunk p ^ 8).
+  const uint32_t src_chunk = 16u * (uint32_t)((lane & 31) ^ ((lane >> 5) << 3));
+  auto issue_latent = [&](int n, int st) {
+    const uint32_t tab = tab_at(n) + 8 * (16 * w + (lane >> 5));
+    uint64_t a[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[i] = *LDSP(uint64_t, tab + 16 * i);
+    const uint32_t dst = lat_at(st) + 8 * w * kPair;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      dma16((const uint8_t*)(uintptr_t)(a[i] + src_chunk), __builtin_amdgcn_readfirstlane(dst + i * kPair));
+  };
+  // scales + rope (9 chunks per token) of this wave's tokens of tile n: 144 pieces
+  auto issue_side = [&](int n) {
+    const uint32_t tab = tab_at(n) + 8 * 16 * w;
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      const int piece = 64 * k + lane;
+      if (piece < 16 * 9) {
+        const int j = piece / 9, c = piece % 9;
+        const uint8_t* rec = (const uint8_t*)(uintptr_t)*LDSP(uint64_t, tab + 8 * j);
+        dma16(rec + kScaleOff + 16 * c, __builtin_amdgcn_readfirstlane(side_w + 1024 * k));
+      }
+    }
+  };
+
+  // ---- prologue: indices, then tile t0's records, then q
+#pragma unroll
+  for (int k = 0; k < kIdxRing - 1; ++k) issue_idx(t0 + k);
+  wait_vm_all();
+  fill_table(t0);
+  fill_table(t0 + 1);
+  issue_latent(t0, 0);
+  issue_side(t0);
+  issue_idx(t0 + kIdxRing - 1);
+  // q as bf16 B operands (head = lane column t).  Latent K-step 2m / 2m+1: dims
+  // 64m + 16g + [0..7] / [8..15]; rope K-step i: dims 512 + 32i + 8g + [0..7].
+  v8bf qlat[16];
+  v8bf qrope[2];
+  {
+    const uint16_t* qr = p.q + row * p.q_st + (int64_t)(h_ok ? h : 0) * p.q_sh;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      v4i a = *(const v4i*)(qr + 64 * m + 16 * g);
+      v4i b = *(const v4i*)(qr + 64 * m + 16 * g + 8);
+      if (!h_ok) a = b = v4i{0, 0, 0, 0};
+      qlat[2 * m] = __builtin_bit_cast(v8bf, a);
+      qlat[2 * m + 1] = __builtin_bit_cast(v8bf, b);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      v4i a = *(const v4i*)(qr + kLat + 32 * i + 8 * g);
+      if (!h_ok) a = v4i{0, 0, 0, 0};
+      qrope[i] = __builtin_bit_cast(v8bf, a);
+    }
+  }
+  wait_vm_all();
+
+  float m_ref = -INFINITY;  // reference max (log2 units), the same in every wave
+  float l_run = 0.0f;       // head t's sum of P over this lane's tokens (PV side)
+  v4f O[4];                 // O^T slices: dims 64w + 16 dt + 4g + [0..3], head t
+#pragma unroll
+  for (int i = 0; i < 4; ++i) O[i] = v4f{0, 0, 0, 0};
+
+  // QK read addresses: token 16w + t, chunk 4m + g (stored at (4m + g) ^ 8 in odd rows,
+  // i.e. K-step m ^ 2): slices with m & 2 == 0 use qk_a, the others qk_b, + 64 m.
+  const uint32_t qk_row = row_off(16 * w + t) + 16 * g;
+  const uint32_t qk_a = qk_row + ((t & 1) ? 128u : 0u);
+  const uint32_t qk_b = qk_row - ((t & 1) ? 128u : 0u);
+  // PV transposed reads: lane (t, g) loads token 32 k + 8 g + t/2, bytes
+  // 8(t&1) .. +7 of chunk 4w + dt (stored at (4w + dt) ^ 8 in odd rows), so
+  // lane (i, g) receives dim i of tokens 8g .. 8g+7 of K-step k; dt and k are
+  // immediate offsets.
+  const int tv = 8 * g + (t >> 1);
+  const uint32_t pv_off = row_off(tv) + 64 * (w ^ (2 * (tv & 1))) + 8 * (t & 1);
+  const v2h ones = v2h{(_Float16)1.0f, (_Float16)1.0f};
+
+  const uint32_t mx = base + kMxOff;
+  const uint32_t px = base + kPxOff;
+  const uint32_t sx = base + kSxOff;
+
+  for (int n = t0; n < t1; ++n) {
+    const int st = (n - t0) & 1;
+    // this wave's records of tile n have landed (one later index load may be in flight)
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(1));
+    // every wave's records have landed and every wave is done with tile n-1
+    // (its stage, P, scales and maxima may be overwritten)
+    __syncthreads();
+    const int ix_n = ring_ix(n, t);
+    const uint32_t vmask = (uint32_t)__ballot(ix_n >= 0) & 0xFFFFu;  // bit j: token 16w + j is a key
+    const bool more = n + 1 < t1;
+    if (more) issue_latent(n + 1, st ^ 1);
+    fill_table(n + 2);
+
+    // ---- QK: lane (t, g) gets head t, tokens 16w + 4g + r
+    const uint32_t lat = lat_at(st);
+    v4f S;
+    v4f ksc;
+    {
+      v4i kr[8];
+#pragma unroll
+      for (int m = 0; m < 8; ++m) kr[m] = *LDSP(v4i, lat + ((m & 2) ? qk_b : qk_a) + 64 * m);
+      const uint32_t sb = side_w + kSide * t;
+      ksc = *LDSP(v4f, sb);
+      const v4i rp0 = *LDSP(v4i, sb + 16 + 16 * g);
+      const v4i rp1 = *LDSP(v4i, sb + 80 + 16 * g);
+      v4f acc = v4f{0, 0, 0, 0};
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const float sc = ksc[m >> 1];
+        v2bf a0, a1, a2, a3, b0, b1, b2, b3;
+        cvt4_bf16(kr[m].x, sc, a0, a1);
+        cvt4_bf16(kr[m].y, sc, a2, a3);
+        cvt4_bf16(kr[m].z, sc, b0, b1);
+        cvt4_bf16(kr[m].w, sc, b2, b3);
+        const v8bf ka = {a0.x, a0.y, a1.x, a1.y, a2.x, a2.y, a3.x, a3.y};
+        const v8bf kb = {b0.x, b0.y, b1.x, b1.y, b2.x, b2.y, b3.x, b3.y};
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qlat[2 * m], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qlat[2 * m + 1], acc, 0, 0, 0);
+      }
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, rp0), qrope[0], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, rp1), qrope[1], acc, 0, 0, 0);
+      S = acc;
+    }
+
+    // ---- side data of tile n+1 into this wave's side area (its reads of tile n
+    // are complete), index load kIdxRing-1 tiles ahead
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    if (more) issue_side(n + 1);
+    issue_idx(n + kIdxRing);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- softmax (log2 domain) of this wave's 16 tokens
+    float x[4];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      x[r] = ((vmask >> (4 * g + r)) & 1u) ? S[r] * p.c_log2 : -INFINITY;
+      tmax = fmax_(tmax, x[r]);
+    }
+    tmax = xor_max(tmax);
+    if (g == 0) *LDSP(float, mx + 4 * (8 * t + w)) = tmax;
+    // P with the current reference (valid unless some head's max moves it)
+    auto write_p = [&](float m_use) {
+      _Float16 ph[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ph[r] = (_Float16)__builtin_amdgcn_exp2f(x[r] - m_use + kShift);
+      *LDSP(v2i, px + 2 * (kTile * t + 16 * w + 4 * g)) =
+          __builtin_bit_cast(v2i, (v4h{ph[0], ph[1], ph[2], ph[3]}));
+    };
+    write_p(m_ref == -INFINITY ? 0.0f : m_ref);
+    // V scale of block g for token 16w + t, clamped to 2^7, as f16
+    *LDSP(_Float16, sx + 2 * (kTile * g + 16 * w + t)) = (_Float16)__builtin_fminf(ksc[g], kScaleCap);
+    __syncthreads();
+
+    // ---- tile max of head t over all waves (lane group g reads waves 2g, 2g+1);
+    // move the reference if it grew by more than kTau
+    {
+      const v2f mg = *LDSP(v2f, mx + 4 * (8 * t + 2 * g));
+      const float M = xor_max(fmax_(mg.x, mg.y));
+      if (__builtin_amdgcn_ballot_w64(M > m_ref + kTau)) {  // the same decision in every wave
+        const float m_new = fmax_(m_ref, M);
+        const float alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_ref - m_new);
+        if (__builtin_amdgcn_ballot_w64(m_ref != -INFINITY)) {  // O and l are still zero otherwise
+          l_run *= alpha;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) O[i] *= alpha;
+        }
+        m_ref = m_new;
+        write_p(m_ref == -INFINITY ? 0.0f : m_ref);
+        __syncthreads();
+      }
+    }
+
+    // ---- PV: O^T[d, h] += V^T[d, tok] P'^T[tok, h] over the tile's 128 tokens;
+    // l sums the same f16 P (so numerator and denominator share the rounding)
+    const uint32_t vaddr = lat + pv_off;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int tok = 32 * k + 8 * g;
+      const v8h pr = *LDSP(v8h, px + 2 * (kTile * t + tok));
+      const v8h sr = *LDSP(v8h, sx + 2 * (kTile * (w >> 1) + tok));
+      const v8h pb = pr * sr;
+      l_run = __builtin_amdgcn_fdot2(v2h{pr[0], pr[1]}, ones, l_run, false);
+      l_run = __builtin_amdgcn_fdot2(v2h{pr[2], pr[3]}, ones, l_run, false);
+      l_run = __builtin_amdgcn_fdot2(v2h{pr[4], pr[5]}, ones, l_run, false);
+      l_run = __builtin_amdgcn_fdot2(v2h{pr[6], pr[7]}, ones, l_run, false);
+      v2i vr[4];
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+        vr[dt] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(LDSP(v2i, vaddr + 16 * kPair * k + 16 * dt));
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+        O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(cvt8_f16(vr[dt]), pb, O[dt], 0, 0, 0);
+    }
+  }
+  wait_vm_all();  // no DMA may still target LDS when the block ends
+
+  // ---- epilogue: head t's sum over all tokens, then this wave's 64 dims
+  l_run = xor_sum(l_run);
+  const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;
+  const float l2 = l_run > 0.0f ? m_ref + __builtin_log2f(l_run) - kShift : -INFINITY;
+  if (w == 0 && g == 0 && h_ok) {
+    if (split) p.part_lse[(int64_t)unit * p.H + h] = l2;
+    else if (p.lse) p.lse[(int64_t)row * p.H + h] = l2 * kLn2;
+  }
+  if (h_ok) {
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      const v4f acc = O[dt] * inv;
+      const int d = 64 * w + 16 * dt + 4 * g;
+      if (split) {
+        *(v4f*)(p.part_o + ((int64_t)unit * p.H + h) * kLat + d) = acc;
+      } else {
+        const uint32_t w0 = f32_to_bf16_rne(acc.x) | ((uint32_t)f32_to_bf16_rne(acc.y) << 16);
+        const uint32_t w1 = f32_to_bf16_rne(acc.z) | ((uint32_t)f32_to_bf16_rne(acc.w) << 16);
+        *(v2i*)(p.out + row * p.o_st + h * p.o_sh + d) = v2i{(int)w0, (int)w1};
       }
     }
   }
@@ -780,7 +1111,12 @@ static hipError_t launch_fwd_t(const FwdParams& p, Events ev, hipStream_t s) {
 
 hipError_t launch_fwd(const FwdParams& p, Events ev, hipStream_t s) {
   switch (head_tiles(p.H)) {
-    case 1: return launch_fwd_t<1, 4>(p, ev, s);
+    case 1: {
+      const int64_t blocks = xcd_grid(p.T, p.S);
+      hipExtLaunchKernelGGL(smla_fwd16_kernel, dim3((unsigned)blocks), dim3(n16::kThreads), 0, s,
+                            ev.start, ev.stop, 0, p);
+      return hipGetLastError();
+    }
     case 2: return launch_fwd_t<2, 2>(p, ev, s);
     case 3: return launch_fwd_t<3, 1>(p, ev, s);
     case 4: return launch_fwd_t<4, 1>(p, ev, s);

@@ -88,8 +88,12 @@ def test_config_parity(smla, cfg):
     w = synth.make_workload(cfg, device="cuda")
     out, lse = run_gpu(w)
     rows = None if cfg != 5 else sample_rows(w.T, 48, seed=cfg)
-    ro, rl = run_oracle(w, rows=rows)
-    compare(out, lse, ro, rl, rows=rows, large_values=(cfg == 3), label=f"config{cfg}")
+    if cfg == 3:
+        ro, rl, ra = run_oracle(w, rows=rows, with_abs=True)
+        compare(out, lse, ro, rl, rows=rows, large_values=True, abs_ref=ra, label=f"config{cfg}")
+    else:
+        ro, rl = run_oracle(w, rows=rows)
+        compare(out, lse, ro, rl, rows=rows, label=f"config{cfg}")
 
 
 # ------------------------------------------------------------------ edge cases

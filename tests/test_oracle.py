@@ -241,6 +241,30 @@ def test_equal_scores_give_mean():
     assert np.allclose(lse, math.log(17), rtol=0, atol=1e-14)
 
 
+def test_weighted_abs_value():
+    """The oracle's A = p |V| / l: equal to out when every latent is >= 0, never
+    below |out|, the plain mean of |V| when all scores are equal, and the same
+    out and lse as without it."""
+    rng = np.random.default_rng(14)
+    kv = random_records(rng, 40)
+    q = random_q(rng, 3, 4)
+    ip = np.array([0, 25, 25, 40])
+    ix = rng.integers(0, 40, size=40)
+    o, l = oracle.sparse_mla_fwd(q, kv, ip, ix, SIGMA)
+    o2, l2, A = oracle.sparse_mla_fwd(q, kv, ip, ix, SIGMA, with_abs=True)
+    assert np.array_equal(o, o2) and np.array_equal(l, l2)
+    assert np.all(A >= np.abs(o) - 1e-12 * np.maximum(1.0, A))
+    assert np.array_equal(A[1], np.zeros_like(A[1]))  # empty row
+    pos = kv.copy()
+    pos[:, :512] &= 0x7F  # clear every latent code's sign bit
+    op, _, Ap = oracle.sparse_mla_fwd(q, pos, ip, ix, SIGMA, with_abs=True)
+    assert np.max(np.abs(Ap - op)) <= 1e-12 * max(1.0, np.abs(op).max())
+    q0 = np.zeros((1, 2, 576), np.uint16)  # equal scores: A is the mean of |V|
+    _, _, A0 = oracle.sparse_mla_fwd(q0, kv, [0, 17], ix[:17], SIGMA, with_abs=True)
+    want = np.abs(torch_decode(kv[ix[:17]])[:, :512]).mean(axis=0)
+    assert np.max(np.abs(A0[0] - want)) <= 1e-12 * max(1.0, want.max())
+
+
 def test_permutation_invariance():
     q, kv, ip, ix = tiny_case(100)
     rng = np.random.default_rng(5)
