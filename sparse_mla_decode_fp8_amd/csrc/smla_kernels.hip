@@ -52,6 +52,7 @@ typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 typedef _Float16 v4h __attribute__((ext_vector_type(4)));
 
 #define LDSP(T, off) ((__attribute__((address_space(3))) T*)(uintptr_t)(off))
+#define GLBP(T, addr) ((const __attribute__((address_space(1))) T*)(uintptr_t)(addr))
 
 constexpr int kLat = 512;
 constexpr int kScaleOff = 512;
@@ -662,18 +663,19 @@ __global__ __launch_bounds__(64 * HT * TG, 1) void smla_fwd_kernel(FwdParams p) 
 //       the V scale folds into P) over all 128 tokens, and the softmax sum of
 //       every head from the same f16 P it multiplies.
 // P, the per-token V scales and the per-wave tile maxima go through LDS, with
-// two barriers per tile; no merge is needed at the end.
+// two barriers per tile; no merge is needed at the end.  Latent rows reach
+// LDS by DMA one tile ahead; each lane loads the scales and rope it needs for
+// QK into registers at the same time.
 namespace n16 {
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTile = 128;
 constexpr int kPair = 2 * kLat + 16;             // two latent rows + 16-B pad
 constexpr int kLatStage = (kTile / 2) * kPair;   // 66560 B
-constexpr int kSide = 144;                       // scales (16 B) + rope (128 B)
 constexpr int kIdxRing = 4;                         // index ring slots (tiles)
 constexpr int kLatOff = 0;
-constexpr int kSideOff = kLatOff + 2 * kLatStage;
-constexpr int kPxOff = kSideOff + kTile * kSide;  // P, f16 [head 16][token 128]
+constexpr int kQOff = kLatOff + 2 * kLatStage;    // q of the row, bf16 [head 16][576]
+constexpr int kPxOff = kQOff + 16 * 576 * 2;      // P, f16 [head 16][token 128]
 constexpr int kSxOff = kPxOff + 16 * kTile * 2;   // V scales, f16 [block 4][token 128]
 constexpr int kMxOff = kSxOff + 4 * kTile * 2;    // tile maxima, f32 [head 16][wave 8]
 constexpr int kIdxRingOff = kMxOff + 16 * kWaves * 4;
@@ -734,9 +736,8 @@ __global__ __launch_bounds__(n16::kThreads, 1) void smla_fwd16_kernel(FwdParams 
   auto lat_at = [&](int st) -> uint32_t { return base + kLatOff + st * kLatStage; };
   auto ring_at = [&](int n) -> uint32_t { return base + kIdxRingOff + (n & (kIdxRing - 1)) * kTile * 4; };
   auto tab_at = [&](int n) -> uint32_t { return base + kTabOff + (n & 1) * kTile * 8; };
-  const uint32_t side_w = base + kSideOff + 16 * w * kSide;  // this wave's 16 tokens
-  // Every wave touches only its own 16 entries of the index ring, the address
-  // table and the side area, so those need no barrier.
+  // Every wave touches only its own 16 entries of the index ring and the
+  // address table, so those need no barrier.
 
   // Index of this wave's token j (0..15) in tile n, -1 past the row.
   // Positions past nnz read 0 (bounded reads) and are masked here.
@@ -771,51 +772,67 @@ __global__ __launch_bounds__(n16::kThreads, 1) void smla_fwd16_kernel(FwdParams 
     for (int i = 0; i < 8; ++i)
       dma16((const uint8_t*)(uintptr_t)(a[i] + src_chunk), __builtin_amdgcn_readfirstlane(dst + i * kPair));
   };
-  // scales + rope (9 chunks per token) of this wave's tokens of tile n: 144 pieces
-  auto issue_side = [&](int n) {
-    const uint32_t tab = tab_at(n) + 8 * 16 * w;
-#pragma unroll
-    for (int k = 0; k < 3; ++k) {
-      const int piece = 64 * k + lane;
-      if (piece < 16 * 9) {
-        const int j = piece / 9, c = piece % 9;
-        const uint8_t* rec = (const uint8_t*)(uintptr_t)*LDSP(uint64_t, tab + 8 * j);
-        dma16(rec + kScaleOff + 16 * c, __builtin_amdgcn_readfirstlane(side_w + 1024 * k));
-      }
-    }
+  // scales and rope of token 16w + t of tile n that lane (t, g) needs for QK:
+  // the 4 block scales, rope dims 8g .. 8g+7 and 32 + 8g .. 32 + 8g + 7
+  v4f ksc_nx;
+  v4i rp0_nx, rp1_nx;
+  auto load_side = [&](int n) {
+    // global (not flat) loads: they must count in vmcnt only
+    const uint64_t rec = *LDSP(uint64_t, tab_at(n) + 8 * (16 * w + t));
+    ksc_nx = *GLBP(v4f, rec + kScaleOff);
+    rp0_nx = *GLBP(v4i, rec + kRopeOff + 16 * g);
+    rp1_nx = *GLBP(v4i, rec + kRopeOff + 64 + 16 * g);
   };
 
-  // ---- prologue: indices, then tile t0's records, then q
+  // ---- prologue: indices; then q of the row into LDS (each wave an eighth,
+  // once per block), tile t0's latent rows, this lane's scales and rope of
+  // tile t0, and the next index load
 #pragma unroll
   for (int k = 0; k < kIdxRing - 1; ++k) issue_idx(t0 + k);
   wait_vm_all();
   fill_table(t0);
   fill_table(t0 + 1);
+  {
+    // q chunk c (16 B, 72 per head) of head c / 72 lands at q_lds + 16 c;
+    // chunks of heads >= H are not loaded (their lanes use zeros)
+    const uint16_t* qrow = p.q + row * p.q_st;
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      const int c = 144 * w + 64 * k + lane;
+      const int hh = c / 72;
+      if (64 * k + lane < 144 && hh < p.H)
+        dma16((const uint8_t*)(qrow + (int64_t)hh * p.q_sh + 8 * (c % 72)),
+              __builtin_amdgcn_readfirstlane(base + kQOff + 16 * (144 * w + 64 * k)));
+    }
+  }
   issue_latent(t0, 0);
-  issue_side(t0);
+  load_side(t0);
   issue_idx(t0 + kIdxRing - 1);
+  // this wave's q chunks have landed (12 later instructions may be in flight),
+  // then every wave's
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(12));
+  __syncthreads();
   // q as bf16 B operands (head = lane column t).  Latent K-step 2m / 2m+1: dims
   // 64m + 16g + [0..7] / [8..15]; rope K-step i: dims 512 + 32i + 8g + [0..7].
   v8bf qlat[16];
   v8bf qrope[2];
   {
-    const uint16_t* qr = p.q + row * p.q_st + (int64_t)(h_ok ? h : 0) * p.q_sh;
+    const uint32_t qr = base + kQOff + 2 * 576 * t;
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
-      v4i a = *(const v4i*)(qr + 64 * m + 16 * g);
-      v4i b = *(const v4i*)(qr + 64 * m + 16 * g + 8);
+      v4i a = *LDSP(v4i, qr + 2 * (64 * m + 16 * g));
+      v4i b = *LDSP(v4i, qr + 2 * (64 * m + 16 * g + 8));
       if (!h_ok) a = b = v4i{0, 0, 0, 0};
       qlat[2 * m] = __builtin_bit_cast(v8bf, a);
       qlat[2 * m + 1] = __builtin_bit_cast(v8bf, b);
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      v4i a = *(const v4i*)(qr + kLat + 32 * i + 8 * g);
+      v4i a = *LDSP(v4i, qr + 2 * (kLat + 32 * i + 8 * g));
       if (!h_ok) a = v4i{0, 0, 0, 0};
       qrope[i] = __builtin_bit_cast(v8bf, a);
     }
   }
-  wait_vm_all();
 
   float m_ref = -INFINITY;  // reference max (log2 units), the same in every wave
   float l_run = 0.0f;       // head t's sum of P over this lane's tokens (PV side)
@@ -847,24 +864,30 @@ __global__ __launch_bounds__(n16::kThreads, 1) void smla_fwd16_kernel(FwdParams 
     // every wave's records have landed and every wave is done with tile n-1
     // (its stage, P, scales and maxima may be overwritten)
     __syncthreads();
+    // tile n's scales and rope: their loads completed with the wait above; the
+    // empty asm pins the compiler's own wait for them here, before the next
+    // tile's DMA is queued behind them
+    const v4f ksc = ksc_nx;
+    const v4i rp0 = rp0_nx, rp1 = rp1_nx;
+    asm volatile("" :: "v"(ksc), "v"(rp0), "v"(rp1));
     const int ix_n = ring_ix(n, t);
     const uint32_t vmask = (uint32_t)__ballot(ix_n >= 0) & 0xFFFFu;  // bit j: token 16w + j is a key
     const bool more = n + 1 < t1;
-    if (more) issue_latent(n + 1, st ^ 1);
+    if (more) {
+      issue_latent(n + 1, st ^ 1);
+      load_side(n + 1);
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // ring slot n is read before its reload lands
+    issue_idx(n + kIdxRing);
     fill_table(n + 2);
 
     // ---- QK: lane (t, g) gets head t, tokens 16w + 4g + r
     const uint32_t lat = lat_at(st);
     v4f S;
-    v4f ksc;
     {
       v4i kr[8];
 #pragma unroll
       for (int m = 0; m < 8; ++m) kr[m] = *LDSP(v4i, lat + ((m & 2) ? qk_b : qk_a) + 64 * m);
-      const uint32_t sb = side_w + kSide * t;
-      ksc = *LDSP(v4f, sb);
-      const v4i rp0 = *LDSP(v4i, sb + 16 + 16 * g);
-      const v4i rp1 = *LDSP(v4i, sb + 80 + 16 * g);
       v4f acc = v4f{0, 0, 0, 0};
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
@@ -883,14 +906,6 @@ __global__ __launch_bounds__(n16::kThreads, 1) void smla_fwd16_kernel(FwdParams 
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, rp1), qrope[1], acc, 0, 0, 0);
       S = acc;
     }
-
-    // ---- side data of tile n+1 into this wave's side area (its reads of tile n
-    // are complete), index load kIdxRing-1 tiles ahead
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-    if (more) issue_side(n + 1);
-    issue_idx(n + kIdxRing);
-    __builtin_amdgcn_sched_barrier(0);
 
     // ---- softmax (log2 domain) of this wave's 16 tokens
     float x[4];
