@@ -108,7 +108,7 @@ Layout layout(int32_t T, int32_t H, int64_t nnz) {
   if (L.S > 1) {
     off = align256(off + sizeof(float) * (size_t)T * L.S * H);
     L.part_o = off;
-    off = align256(off + sizeof(float) * (size_t)T * L.S * H * 512);
+    off = align256(off + sizeof(uint16_t) * (size_t)T * L.S * H * 512);  // f16 partial outputs
   }
   L.total = off;
   return L;
@@ -230,7 +230,7 @@ int sparse_mla_fwd(const void* q, int64_t q_stride_t, int64_t q_stride_h,
   fp.lse = lse;
   fp.row_tiles = (sort || has_invalid) ? row_tiles : nullptr;
   fp.order = sort ? order : nullptr;
-  fp.part_o = (float*)(ws + L.part_o);
+  fp.part_o = (uint16_t*)(ws + L.part_o);
   fp.part_lse = (float*)(ws + L.part_lse);
   e = timed(1, [&](smla::Events ev) { return smla::launch_fwd(fp, ev, s); });
   if (e != hipSuccess) return hip_fail(e, "forward kernel launch");

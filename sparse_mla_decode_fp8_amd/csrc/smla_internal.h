@@ -37,14 +37,14 @@ struct FwdParams {
   float* lse;          // nullable
   const int32_t* row_tiles;  // nullable: tiles from indptr
   const int32_t* order;      // nullable: rows in their own order
-  float* part_o;       // [T*S, H, 512] when S > 1
+  uint16_t* part_o;    // f16 bits [T*S, H, 512] when S > 1
   float* part_lse;     // [T*S, H]  (log2 units) when S > 1
 };
 
 struct CombineParams {
   int32_t T, H, S;
   const int32_t* order;  // nullable: rows in their own order
-  const float* part_o;
+  const uint16_t* part_o;  // f16 bits
   const float* part_lse;
   uint16_t* out;
   int64_t o_st, o_sh;

@@ -144,6 +144,17 @@ __device__ __forceinline__ v8h cvt8_f16(v2i w) {
 }
 
 
+// Split partials of the output are stored as f16: a normalised partial is a
+// convex combination of V values, |V| <= 448 * 2^7 = 57344, so it fits f16's
+// range, and its 11-bit precision is finer than the bf16 of the result.
+__device__ __forceinline__ void st_half4(uint16_t* dst, v4f v) {
+  *(v4h*)dst = v4h{(_Float16)v.x, (_Float16)v.y, (_Float16)v.z, (_Float16)v.w};
+}
+__device__ __forceinline__ v4f half4_to_f32(v2i raw) {
+  const v4h hv = __builtin_bit_cast(v4h, raw);
+  return v4f{(float)hv.x, (float)hv.y, (float)hv.z, (float)hv.w};
+}
+
 // XCD-aware unit mapping: block b runs on XCD b % 8; rows of rank r go to XCD
 // r % 8 and the `per_row` blocks of a row are consecutive on that XCD.
 __device__ __forceinline__ void xcd_unit(int per_row, int& rank, int& sub) {
@@ -576,9 +587,9 @@ __global__ __launch_bounds__(64 * HT * TG, 1) void smla_fwd_kernel(FwdParams p) 
     const float l2 = l_run > 0.0f ? m_ref + __builtin_log2f(l_run) - kShift : -INFINITY;
     if (h_ok) {
       if (split) {
-        float* po = p.part_o + ((int64_t)unit * p.H + h) * kLat;
+        uint16_t* po = p.part_o + ((int64_t)unit * p.H + h) * kLat;
 #pragma unroll
-        for (int dt = 0; dt < 32; ++dt) *(v4f*)(po + 16 * dt + 4 * g) = O[dt] * inv;
+        for (int dt = 0; dt < 32; ++dt) st_half4(po + 16 * dt + 4 * g, O[dt] * inv);
         if (g == 0) p.part_lse[(int64_t)unit * p.H + h] = l2;
       } else {
         uint16_t* po = p.out + row * p.o_st + h * p.o_sh;
@@ -640,7 +651,7 @@ __global__ __launch_bounds__(64 * HT * TG, 1) void smla_fwd_kernel(FwdParams p) 
           if (src != q) acc += *slot(src, dt);
         if (!h_ok) continue;
         if (split) {
-          *(v4f*)(p.part_o + ((int64_t)unit * p.H + h) * kLat + 16 * dt + 4 * g) = acc;
+          st_half4(p.part_o + ((int64_t)unit * p.H + h) * kLat + 16 * dt + 4 * g, acc);
         } else {
           const uint32_t w0 = f32_to_bf16_rne(acc.x) | ((uint32_t)f32_to_bf16_rne(acc.y) << 16);
           const uint32_t w1 = f32_to_bf16_rne(acc.z) | ((uint32_t)f32_to_bf16_rne(acc.w) << 16);
@@ -663,16 +674,23 @@ __global__ __launch_bounds__(64 * HT * TG, 1) void smla_fwd_kernel(FwdParams p) 
 //       the V scale folds into P) over all 128 tokens, and the softmax sum of
 //       every head from the same f16 P it multiplies.
 // P, the per-token V scales and the per-wave tile maxima go through LDS, with
-// two barriers per tile; no merge is needed at the end.  Latent rows reach
-// LDS by DMA one tile ahead; each lane loads the scales and rope it needs for
-// QK into registers at the same time.
+// two barriers per tile; no merge is needed at the end.
+//
+// Pipeline: two latent stages.  Tile n+2 is queued into tile n's stage as soon
+// as every wave has finished tile n, so while a wave waits for tile n+1 both
+// n+1 and n+2 are in flight.  Each wave's QK reads only the records its own
+// DMA brought in, so a wave starts tile n after its own wait; the barrier
+// after the scores publishes every wave's records for the P.V stage.  The
+// scales and rope a lane needs for QK travel with the records into one of two
+// register sets (tiles alternate between them, so the loop is unrolled by
+// two).
 namespace n16 {
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTile = 128;
 constexpr int kPair = 2 * kLat + 16;             // two latent rows + 16-B pad
 constexpr int kLatStage = (kTile / 2) * kPair;   // 66560 B
-constexpr int kIdxRing = 4;                         // index ring slots (tiles)
+constexpr int kIdxRing = 4;                      // index ring slots (tiles)
 constexpr int kLatOff = 0;
 constexpr int kQOff = kLatOff + 2 * kLatStage;    // q of the row, bf16 [head 16][576]
 constexpr int kPxOff = kQOff + 16 * 576 * 2;      // P, f16 [head 16][token 128]
@@ -682,12 +700,44 @@ constexpr int kIdxRingOff = kMxOff + 16 * kWaves * 4;
 constexpr int kTabOff = kIdxRingOff + kIdxRing * kTile * 4;  // record addresses [2][token 128]
 constexpr int kBytes = kTabOff + 2 * kTile * 8;
 static_assert(kBytes <= 160 * 1024, "LDS budget");
+// Vector-memory instructions one wave issues per tile: 8 latent DMAs (token
+// pairs) and 3 side loads; one index DMA per tile besides.
+constexpr int kTileVm = 8 + 3;
 
 // Byte offset of token tau's latent row inside a stage.  Rows come in pairs
 // (2 x 512 B, then a 16-B pad); the odd row of a pair stores chunk c (16 B)
 // at position c ^ 8.  With the 1040-B pair stride both the QK reads (16
 // tokens, one chunk column) and the transposed PV reads spread over all banks.
 __device__ __forceinline__ uint32_t row_off(int tau) { return (tau >> 1) * kPair + (tau & 1) * kLat; }
+
+// Scales and rope of the token a lane scores (token 16w + t): the 4 block
+// scales, rope dims 8g .. 8g+7 and 32 + 8g .. 32 + 8g + 7; and the wave's
+// valid-token mask of that tile (bit j: token 16w + j is a key).
+struct Side {
+  v4f ksc;
+  v4i rp0, rp1;
+  uint32_t vmask;
+};
+
+// 16 bytes from global memory into registers, issued from asm: the compiler
+// does not count it, so it never inserts a wait for it; the kernel waits with
+// explicit vmcnt counts and then pins the registers (pin()).
+__device__ __forceinline__ void gload16(v4f& dst, uint64_t addr) {
+  asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(dst) : "v"(addr) : "memory");
+}
+__device__ __forceinline__ void gload16(v4i& dst, uint64_t addr) {
+  asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(dst) : "v"(addr) : "memory");
+}
+// After the wait that covers a side load: later reads of the registers may
+// not move above this point.
+__device__ __forceinline__ void pin(Side& s) { asm volatile("" : "+v"(s.ksc), "+v"(s.rp0), "+v"(s.rp1)); }
+
+// vmcnt waits with a compile-time count
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(N));
+}
 }  // namespace n16
 
 __global__ __launch_bounds__(n16::kThreads, 1) void smla_fwd16_kernel(FwdParams p) {
@@ -739,24 +789,23 @@ __global__ __launch_bounds__(n16::kThreads, 1) void smla_fwd16_kernel(FwdParams 
   // Every wave touches only its own 16 entries of the index ring and the
   // address table, so those need no barrier.
 
-  // Index of this wave's token j (0..15) in tile n, -1 past the row.
-  // Positions past nnz read 0 (bounded reads) and are masked here.
-  auto ring_ix = [&](int n, int j) -> int {
-    const int raw = *LDSP(int, ring_at(n) + 4 * (16 * w + j));
-    return (n * kTile + 16 * w + j < len) ? raw : -1;
-  };
-  auto rec_of = [&](int ix) -> const uint8_t* { return ix >= 0 ? kv + (int64_t)ix * kRecordBytes : zero; };
-  // index DMA of tile n: this wave's 16 entries (lanes 0..15)
+  // index DMA of tile n: this wave's 16 entries (lanes 0..15).  Positions past
+  // nnz read 0 (bounded reads); positions past the row are masked in fill_table.
   auto issue_idx = [&](int n) {
     const uint32_t dst = __builtin_amdgcn_readfirstlane(ring_at(n) + 64 * w);
     if (lane < 16) buf_dma4(irs, (uint32_t)(beg + n * kTile + 16 * w + lane) * 4u, dst);
   };
-  // record addresses of this wave's tokens of tile n; tiles at or past t1 get the zero record
-  auto fill_table = [&](int n) {
+  // record addresses of this wave's tokens of tile n (masked ones: the zero
+  // record); returns the wave's valid-token mask
+  auto fill_table = [&](int n) -> uint32_t {
+    int ix = -1;
     if (lane < 16) {
-      const int ix = n < t1 ? ring_ix(n, lane) : -1;
-      *LDSP(uint64_t, tab_at(n) + 8 * (16 * w + lane)) = (uint64_t)(uintptr_t)rec_of(ix);
+      const int raw = *LDSP(int, ring_at(n) + 4 * (16 * w + lane));
+      ix = (n * kTile + 16 * w + lane < len) ? raw : -1;
+      *LDSP(uint64_t, tab_at(n) + 8 * (16 * w + lane)) =
+          (uint64_t)(uintptr_t)(ix >= 0 ? kv + (int64_t)ix * kRecordBytes : zero);
     }
+    return (uint32_t)__ballot(ix >= 0) & 0xFFFFu;
   };
   // latent DMA of this wave's 16 tokens of tile n into stage st: one
   // instruction per token pair, lanes 0..31 the even token, 32..63 the odd one
@@ -772,26 +821,19 @@ __global__ __launch_bounds__(n16::kThreads, 1) void smla_fwd16_kernel(FwdParams 
     for (int i = 0; i < 8; ++i)
       dma16((const uint8_t*)(uintptr_t)(a[i] + src_chunk), __builtin_amdgcn_readfirstlane(dst + i * kPair));
   };
-  // scales and rope of token 16w + t of tile n that lane (t, g) needs for QK:
-  // the 4 block scales, rope dims 8g .. 8g+7 and 32 + 8g .. 32 + 8g + 7
-  v4f ksc_nx;
-  v4i rp0_nx, rp1_nx;
-  auto load_side = [&](int n) {
-    // global (not flat) loads: they must count in vmcnt only
+  auto load_side = [&](int n, Side& s) {
     const uint64_t rec = *LDSP(uint64_t, tab_at(n) + 8 * (16 * w + t));
-    ksc_nx = *GLBP(v4f, rec + kScaleOff);
-    rp0_nx = *GLBP(v4i, rec + kRopeOff + 16 * g);
-    rp1_nx = *GLBP(v4i, rec + kRopeOff + 64 + 16 * g);
+    gload16(s.ksc, rec + kScaleOff);
+    gload16(s.rp0, rec + kRopeOff + 16 * g);
+    gload16(s.rp1, rec + kRopeOff + 64 + 16 * g);
   };
 
-  // ---- prologue: indices; then q of the row into LDS (each wave an eighth,
-  // once per block), tile t0's latent rows, this lane's scales and rope of
-  // tile t0, and the next index load
-#pragma unroll
-  for (int k = 0; k < kIdxRing - 1; ++k) issue_idx(t0 + k);
-  wait_vm_all();
-  fill_table(t0);
-  fill_table(t0 + 1);
+  // ---- prologue.  q of the row into LDS (each wave an eighth, once per
+  // block) alongside the first three index tiles; then the first two tiles'
+  // records, with index tiles t0+3 and t0+4 queued as if by iterations
+  // t0-2 and t0-1, so every iteration sees the same order of loads:
+  //   ... S(n) | I(n+3) | L(n+1) S(n+1) | I(n+4) ...
+  // (L latent DMA, S side loads, I index DMA of a tile).
   {
     // q chunk c (16 B, 72 per head) of head c / 72 lands at q_lds + 16 c;
     // chunks of heads >= H are not loaded (their lanes use zeros)
@@ -805,13 +847,17 @@ __global__ __launch_bounds__(n16::kThreads, 1) void smla_fwd16_kernel(FwdParams 
               __builtin_amdgcn_readfirstlane(base + kQOff + 16 * (144 * w + 64 * k)));
     }
   }
+  issue_idx(t0);
+  issue_idx(t0 + 1);
+  issue_idx(t0 + 2);
+  wait_vm_all();  // this wave's q chunks and index tiles have landed
+  Side sA, sB;    // tiles t0, t0+2, ... use sA; t0+1, t0+3, ... sB
+  sA.vmask = fill_table(t0);
+  sB.vmask = (t0 + 1 < t1) ? fill_table(t0 + 1) : 0u;
   issue_latent(t0, 0);
-  load_side(t0);
-  issue_idx(t0 + kIdxRing - 1);
-  // this wave's q chunks have landed (12 later instructions may be in flight),
-  // then every wave's
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(12));
-  __syncthreads();
+  load_side(t0, sA);
+  issue_idx(t0 + 3);
+  __syncthreads();  // every wave's q chunks have landed
   // q as bf16 B operands (head = lane column t).  Latent K-step 2m / 2m+1: dims
   // 64m + 16g + [0..7] / [8..15]; rope K-step i: dims 512 + 32i + 8g + [0..7].
   v8bf qlat[16];
@@ -857,41 +903,42 @@ __global__ __launch_bounds__(n16::kThreads, 1) void smla_fwd16_kernel(FwdParams 
   const uint32_t px = base + kPxOff;
   const uint32_t sx = base + kSxOff;
 
-  for (int n = t0; n < t1; ++n) {
-    const int st = (n - t0) & 1;
-    // this wave's records of tile n have landed (one later index load may be in flight)
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(1));
-    // every wave's records have landed and every wave is done with tile n-1
-    // (its stage, P, scales and maxima may be overwritten)
-    __syncthreads();
-    // tile n's scales and rope: their loads completed with the wait above; the
-    // empty asm pins the compiler's own wait for them here, before the next
-    // tile's DMA is queued behind them
-    const v4f ksc = ksc_nx;
-    const v4i rp0 = rp0_nx, rp1 = rp1_nx;
-    asm volatile("" :: "v"(ksc), "v"(rp0), "v"(rp1));
-    const int ix_n = ring_ix(n, t);
-    const uint32_t vmask = (uint32_t)__ballot(ix_n >= 0) & 0xFFFFu;  // bit j: token 16w + j is a key
-    const bool more = n + 1 < t1;
-    if (more) {
-      issue_latent(n + 1, st ^ 1);
-      load_side(n + 1);
+  // One tile: n, its stage st (= (n - t0) & 1) and its side registers.
+  auto tile = [&](int n, int st, Side& sd) __attribute__((always_inline)) {
+    // this wave's records, scales and rope of tile n have landed; the loads
+    // queued after them (I(n+3), tile n+1's, I(n+4)) may still be in flight.
+    // Tile t0 alone is queued by itself (followed by I(t0+3) only), so that
+    // the first records of every block arrive as early as they can; tile
+    // t0+1 follows as soon as they have.
+    if (n == t0) {
+      wait_vm<1>();
+      if (n + 1 < t1) {
+        issue_latent(n + 1, st ^ 1);
+        load_side(n + 1, sB);
+      }
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // ring slot t0 was read before I(t0+4) lands in it
+      issue_idx(n + 4);
+    } else if (n + 1 < t1) {
+      wait_vm<2 + kTileVm>();
+    } else {
+      wait_vm<2>();
     }
-    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // ring slot n is read before its reload lands
-    issue_idx(n + kIdxRing);
-    fill_table(n + 2);
+    pin(sd);
 
-    // ---- QK: lane (t, g) gets head t, tokens 16w + 4g + r
+    // ---- QK: lane (t, g) gets head t, tokens 16w + 4g + r (own records only)
     const uint32_t lat = lat_at(st);
     v4f S;
     {
       v4i kr[8];
 #pragma unroll
       for (int m = 0; m < 8; ++m) kr[m] = *LDSP(v4i, lat + ((m & 2) ? qk_b : qk_a) + 64 * m);
-      v4f acc = v4f{0, 0, 0, 0};
+      // two independent accumulation chains (K-steps 2m and 2m+1), summed at the end
+      v4f acc0 = v4f{0, 0, 0, 0}, acc1 = v4f{0, 0, 0, 0};
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, sd.rp0), qrope[0], acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, sd.rp1), qrope[1], acc1, 0, 0, 0);
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
-        const float sc = ksc[m >> 1];
+        const float sc = sd.ksc[m >> 1];
         v2bf a0, a1, a2, a3, b0, b1, b2, b3;
         cvt4_bf16(kr[m].x, sc, a0, a1);
         cvt4_bf16(kr[m].y, sc, a2, a3);
@@ -899,12 +946,10 @@ __global__ __launch_bounds__(n16::kThreads, 1) void smla_fwd16_kernel(FwdParams 
         cvt4_bf16(kr[m].w, sc, b2, b3);
         const v8bf ka = {a0.x, a0.y, a1.x, a1.y, a2.x, a2.y, a3.x, a3.y};
         const v8bf kb = {b0.x, b0.y, b1.x, b1.y, b2.x, b2.y, b3.x, b3.y};
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qlat[2 * m], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qlat[2 * m + 1], acc, 0, 0, 0);
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qlat[2 * m], acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qlat[2 * m + 1], acc1, 0, 0, 0);
       }
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, rp0), qrope[0], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, rp1), qrope[1], acc, 0, 0, 0);
-      S = acc;
+      S = acc0 + acc1;
     }
 
     // ---- softmax (log2 domain) of this wave's 16 tokens
@@ -912,7 +957,7 @@ __global__ __launch_bounds__(n16::kThreads, 1) void smla_fwd16_kernel(FwdParams 
     float tmax = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      x[r] = ((vmask >> (4 * g + r)) & 1u) ? S[r] * p.c_log2 : -INFINITY;
+      x[r] = ((sd.vmask >> (4 * g + r)) & 1u) ? S[r] * p.c_log2 : -INFINITY;
       tmax = fmax_(tmax, x[r]);
     }
     tmax = xor_max(tmax);
@@ -927,7 +972,9 @@ __global__ __launch_bounds__(n16::kThreads, 1) void smla_fwd16_kernel(FwdParams 
     };
     write_p(m_ref == -INFINITY ? 0.0f : m_ref);
     // V scale of block g for token 16w + t, clamped to 2^7, as f16
-    *LDSP(_Float16, sx + 2 * (kTile * g + 16 * w + t)) = (_Float16)__builtin_fminf(ksc[g], kScaleCap);
+    *LDSP(_Float16, sx + 2 * (kTile * g + 16 * w + t)) = (_Float16)__builtin_fminf(sd.ksc[g], kScaleCap);
+    // every wave's records of tile n have landed (each waited for its own
+    // above) and its P, scales and maxima are written
     __syncthreads();
 
     // ---- tile max of head t over all waves (lane group g reads waves 2g, 2g+1);
@@ -970,6 +1017,22 @@ __global__ __launch_bounds__(n16::kThreads, 1) void smla_fwd16_kernel(FwdParams 
       for (int dt = 0; dt < 4; ++dt)
         O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(cvt8_f16(vr[dt]), pb, O[dt], 0, 0, 0);
     }
+    // every wave is done with stage st, P, the scales and the maxima of tile n
+    __syncthreads();
+
+    // ---- tile n+2 into stage st and this side set, then index tile n+5
+    if (n + 2 < t1) {
+      sd.vmask = fill_table(n + 2);
+      issue_latent(n + 2, st);
+      load_side(n + 2, sd);
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // ring slot n+1 was read (fill_table) before its reload lands
+    issue_idx(n + 5);
+  };
+
+  for (int n = t0; n < t1; n += 2) {
+    tile(n, 0, sA);
+    if (n + 1 < t1) tile(n + 1, 1, sB);
   }
   wait_vm_all();  // no DMA may still target LDS when the block ends
 
@@ -987,7 +1050,7 @@ __global__ __launch_bounds__(n16::kThreads, 1) void smla_fwd16_kernel(FwdParams 
       const v4f acc = O[dt] * inv;
       const int d = 64 * w + 16 * dt + 4 * g;
       if (split) {
-        *(v4f*)(p.part_o + ((int64_t)unit * p.H + h) * kLat + d) = acc;
+        st_half4(p.part_o + ((int64_t)unit * p.H + h) * kLat + d, acc);
       } else {
         const uint32_t w0 = f32_to_bf16_rne(acc.x) | ((uint32_t)f32_to_bf16_rne(acc.y) << 16);
         const uint32_t w1 = f32_to_bf16_rne(acc.z) | ((uint32_t)f32_to_bf16_rne(acc.w) << 16);
@@ -1001,18 +1064,19 @@ __global__ __launch_bounds__(n16::kThreads, 1) void smla_fwd16_kernel(FwdParams 
 
 // LSE merge of a split row's chunks (K2-back page, stage_combine, without the
 // sink): M = max_c lse2_c, w_c = 2^(lse2_c - M), out = sum w_c o_c / sum w_c.
-// All chunk loads are issued before any is used.
+// All chunk loads are issued before any is used: they are unconditional
+// (chunk slots past S re-read chunk 0 and are ignored), and the f16 partials
+// are converted only after the last load.
 template <int SMAX>
 __device__ __forceinline__ void combine_row(const CombineParams& p, int row, int h) {
   const int64_t u0 = (int64_t)row * p.S;
   float lc[SMAX];
-  v4f oc[SMAX];
+  v2i raw[SMAX];
 #pragma unroll
   for (int c = 0; c < SMAX; ++c) {
-    if (c < p.S) {
-      lc[c] = p.part_lse[(u0 + c) * p.H + h];
-      oc[c] = *(const v4f*)(p.part_o + ((u0 + c) * p.H + h) * kLat + 4 * threadIdx.x);
-    }
+    const int64_t u = u0 + (c < p.S ? c : 0);
+    lc[c] = p.part_lse[u * p.H + h];
+    raw[c] = *(const v2i*)(p.part_o + (u * p.H + h) * kLat + 4 * threadIdx.x);
   }
   float M = -INFINITY;
 #pragma unroll
@@ -1026,7 +1090,7 @@ __device__ __forceinline__ void combine_row(const CombineParams& p, int row, int
       if (c < p.S && lc[c] != -INFINITY) {  // an empty chunk's o_c was never written
         const float w = __builtin_amdgcn_exp2f(lc[c] - M);
         L += w;
-        acc += w * oc[c];
+        acc += w * half4_to_f32(raw[c]);
       }
     }
   }

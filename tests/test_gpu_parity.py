@@ -165,6 +165,47 @@ def test_forced_split(smla, split):
     compare(out, lse, ro, rl, label=f"split{split}")
 
 
+@pytest.mark.parametrize("split,H", [(2, 16), (3, 7), (4, 16), (8, 16), (8, 1)])
+def test_split_merge_back_to_back(smla, split, H):
+    """Split rows: several forwards queued back to back on one stream (new
+    inputs each time) must each match the oracle, so the partials of one call
+    never leak into the next."""
+    rng = np.random.default_rng(20 + split)
+    N = 9000
+    ws = []
+    for k in range(4):
+        sl = [rng.integers(0, N, int(L)) for L in (1024, 0, 1, 513, 1024, 97, 300)]
+        ws.append(custom(f"b2b{k}", H, N, sl, seed=100 + k))
+    smla.set_option("split", split)
+    note(f"back-to-back split={split} H={H}")
+    outs = []
+    for w in ws:
+        outs.append(smla.fwd(w.q, w.kv, w.indptr, w.indices, w.sm_scale))
+    torch.cuda.synchronize()
+    for k, (w, (out, lse)) in enumerate(zip(ws, outs)):
+        ro, rl = run_oracle(w)
+        compare(out, lse, ro, rl, label=f"b2b{k} split{split} H{H}")
+
+
+def test_workspace_reuse_across_shapes(smla):
+    """One uninitialised workspace serves a split forward, a larger unsplit one
+    and the split one again."""
+    rng = np.random.default_rng(31)
+    N = 5000
+    small = custom("reuse_small", 16, N, [rng.integers(0, N, 900) for _ in range(5)])
+    big = custom("reuse_big", 16, N, [rng.integers(0, N, 200) for _ in range(300)], seed=12)
+    ws = torch.empty(max(smla.workspace_bytes(5, 16, small.nnz), smla.workspace_bytes(300, 16, big.nnz)),
+                     dtype=torch.uint8, device=DEV)
+    note("workspace reuse across shapes")
+    res = []
+    for w in (small, big, small):
+        res.append(smla.fwd(w.q, w.kv, w.indptr, w.indices, w.sm_scale, ws=ws))
+    torch.cuda.synchronize()
+    for w, (out, lse) in zip((small, big, small), res):
+        ro, rl = run_oracle(w)
+        compare(out, lse, ro, rl, label=w.name)
+
+
 def test_single_index_is_exact(smla):
     rng = np.random.default_rng(8)
     N = 700
