@@ -257,7 +257,7 @@ def main() -> int:
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": read_traffic(cfg["name"]),
-            "kernel": "smla_fwd_kernel",
+            "kernel": _fwd_kernel_name(w.H),
             "bytes_per_launch": gathered,
             "launch_ms": round(fwd_ms, 5),
         },
@@ -272,6 +272,15 @@ def main() -> int:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_budget, 16)
     print(json.dumps(result), flush=True)
     return 0
+
+
+def _fwd_kernel_name(H: int) -> str:
+    """The forward kernel the library launches for H heads."""
+    if H <= 16:
+        return "smla_fwd16_kernel"
+    ht = (H + 15) // 16
+    tg = 1 if ht >= 3 else 4 // ht
+    return f"smla_fwd_kernel<{ht}, {tg}>"
 
 
 def _split_of(smla, w) -> int:

@@ -692,10 +692,15 @@ constexpr int kPair = 2 * kLat + 16;             // two latent rows + 16-B pad
 constexpr int kLatStage = (kTile / 2) * kPair;   // 66560 B
 constexpr int kIdxRing = 4;                      // index ring slots (tiles)
 constexpr int kLatOff = 0;
-constexpr int kQOff = kLatOff + 2 * kLatStage;    // q of the row, bf16 [head 16][576]
-constexpr int kPxOff = kQOff + 16 * 576 * 2;      // P, f16 [head 16][token 128]
-constexpr int kSxOff = kPxOff + 16 * kTile * 2;   // V scales, f16 [block 4][token 128]
-constexpr int kMxOff = kSxOff + 4 * kTile * 2;    // tile maxima, f32 [head 16][wave 8]
+// Rows of q, P and the V scales are padded by 16 bytes so that the rows of
+// different heads (blocks) start on different LDS banks: the reads of one
+// instruction then spread over all banks instead of piling onto the same few.
+constexpr int kQRow = 2 * 576 + 16;               // 1168 B
+constexpr int kPRow = 2 * kTile + 16;             // 272 B
+constexpr int kQOff = kLatOff + 2 * kLatStage;    // q of the row, bf16 [head 16][576 (+pad)]
+constexpr int kPxOff = kQOff + 16 * kQRow;        // P, f16 [head 16][token 128 (+pad)]
+constexpr int kSxOff = kPxOff + 16 * kPRow;       // V scales, f16 [block 4][token 128 (+pad)]
+constexpr int kMxOff = kSxOff + 4 * kPRow;        // tile maxima, f32 [head 16][wave 8]
 constexpr int kIdxRingOff = kMxOff + 16 * kWaves * 4;
 constexpr int kTabOff = kIdxRingOff + kIdxRing * kTile * 4;  // record addresses [2][token 128]
 constexpr int kBytes = kTabOff + 2 * kTile * 8;
@@ -835,16 +840,19 @@ __global__ __launch_bounds__(n16::kThreads, 1) void smla_fwd16_kernel(FwdParams 
   //   ... S(n) | I(n+3) | L(n+1) S(n+1) | I(n+4) ...
   // (L latent DMA, S side loads, I index DMA of a tile).
   {
-    // q chunk c (16 B, 72 per head) of head c / 72 lands at q_lds + 16 c;
-    // chunks of heads >= H are not loaded (their lanes use zeros)
+    // wave w loads heads 2w and 2w+1: chunk c (16 B, 72 per head) of head hh
+    // lands at q_lds + kQRow hh + 16 c; heads >= H are not loaded (their
+    // lanes use zeros)
     const uint16_t* qrow = p.q + row * p.q_st;
 #pragma unroll
-    for (int k = 0; k < 3; ++k) {
-      const int c = 144 * w + 64 * k + lane;
-      const int hh = c / 72;
-      if (64 * k + lane < 144 && hh < p.H)
-        dma16((const uint8_t*)(qrow + (int64_t)hh * p.q_sh + 8 * (c % 72)),
-              __builtin_amdgcn_readfirstlane(base + kQOff + 16 * (144 * w + 64 * k)));
+    for (int j = 0; j < 2; ++j) {
+      const int hh = 2 * w + j;
+      if (hh < p.H) {
+        const uint16_t* qh = qrow + (int64_t)hh * p.q_sh;
+        const uint32_t dst = base + kQOff + kQRow * hh;
+        dma16((const uint8_t*)(qh + 8 * lane), __builtin_amdgcn_readfirstlane(dst));
+        if (lane < 8) dma16((const uint8_t*)(qh + 8 * (64 + lane)), __builtin_amdgcn_readfirstlane(dst + 1024));
+      }
     }
   }
   issue_idx(t0);
@@ -863,7 +871,7 @@ __global__ __launch_bounds__(n16::kThreads, 1) void smla_fwd16_kernel(FwdParams 
   v8bf qlat[16];
   v8bf qrope[2];
   {
-    const uint32_t qr = base + kQOff + 2 * 576 * t;
+    const uint32_t qr = base + kQOff + kQRow * t;
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
       v4i a = *LDSP(v4i, qr + 2 * (64 * m + 16 * g));
@@ -967,12 +975,12 @@ __global__ __launch_bounds__(n16::kThreads, 1) void smla_fwd16_kernel(FwdParams 
       _Float16 ph[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) ph[r] = (_Float16)__builtin_amdgcn_exp2f(x[r] - m_use + kShift);
-      *LDSP(v2i, px + 2 * (kTile * t + 16 * w + 4 * g)) =
+      *LDSP(v2i, px + kPRow * t + 2 * (16 * w + 4 * g)) =
           __builtin_bit_cast(v2i, (v4h{ph[0], ph[1], ph[2], ph[3]}));
     };
     write_p(m_ref == -INFINITY ? 0.0f : m_ref);
     // V scale of block g for token 16w + t, clamped to 2^7, as f16
-    *LDSP(_Float16, sx + 2 * (kTile * g + 16 * w + t)) = (_Float16)__builtin_fminf(sd.ksc[g], kScaleCap);
+    *LDSP(_Float16, sx + kPRow * g + 2 * (16 * w + t)) = (_Float16)__builtin_fminf(sd.ksc[g], kScaleCap);
     // every wave's records of tile n have landed (each waited for its own
     // above) and its P, scales and maxima are written
     __syncthreads();
@@ -1002,8 +1010,8 @@ __global__ __launch_bounds__(n16::kThreads, 1) void smla_fwd16_kernel(FwdParams 
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int tok = 32 * k + 8 * g;
-      const v8h pr = *LDSP(v8h, px + 2 * (kTile * t + tok));
-      const v8h sr = *LDSP(v8h, sx + 2 * (kTile * (w >> 1) + tok));
+      const v8h pr = *LDSP(v8h, px + kPRow * t + 2 * tok);
+      const v8h sr = *LDSP(v8h, sx + kPRow * (w >> 1) + 2 * tok);
       const v8h pb = pr * sr;
       l_run = __builtin_amdgcn_fdot2(v2h{pr[0], pr[1]}, ones, l_run, false);
       l_run = __builtin_amdgcn_fdot2(v2h{pr[2], pr[3]}, ones, l_run, false);
