@@ -91,7 +91,8 @@ int32_t sparse_mla_split_for(int32_t T, int32_t H, int64_t nnz);
  *   sm_scale   logit scale (e.g. 1/sqrt(576)).
  *   has_invalid  nonzero: the caller pads slices with trailing entries < 0;
  *              tiles after the last entry >= 0 of a row are skipped (found by a
- *              scan of the slice).  Zero: every slice position is scheduled.
+ *              scan of the slice, in the forward itself or in the plan kernel
+ *              when there is one).  Zero: every slice position is scheduled.
  *              The result is the same either way.
  *   out        device, bf16 [T, H, 512] at out + r*o_stride_t + h*o_stride_h + d;
  *              16-byte aligned, strides multiples of 8.
@@ -113,11 +114,12 @@ int32_t sparse_mla_split_for(int32_t T, int32_t H, int64_t nnz);
  *     give unspecified rows).
  *
  * Returns SMLA_OK, or SMLA_EINVAL / SMLA_EUNSUPPORTED / SMLA_EWORKSPACE /
- * SMLA_EHIP with nothing queued.  Queues on `stream`: a slice scan when
- * has_invalid; a one-block longest-first sort of the rows when there are
- * more (row, chunk) units than compute units (otherwise every unit starts at
- * once and rows run in their own order); the forward; and a combine when
- * rows are split.  No host sync, no allocation.
+ * SMLA_EHIP with nothing queued.  Queues on `stream`: a plan when there are
+ * more (row, chunk) units than compute units (a slice scan when has_invalid,
+ * then a one-block longest-first sort of the rows; otherwise every unit
+ * starts at once, rows run in their own order and each forward block scans
+ * its own slice); the forward; and a combine when rows are split.  No host
+ * sync, no allocation.
  * Deterministic for a fixed device and arguments.  nnz must be below
  * 2^30 - 4096 (index reads use 32-bit byte offsets).
  */

@@ -200,11 +200,12 @@ int sparse_mla_fwd(const void* q, int64_t q_stride_t, int64_t q_stride_h,
 
   // Longest-first order only pays when there are more units than CUs (one
   // forward block fits a CU): otherwise every unit starts at once and the
-  // order cannot shorten the slowest.  Without has_invalid and without an
-  // order there is nothing to plan: the forward reads lengths from indptr.
+  // order cannot shorten the slowest.  Without an order there is nothing to
+  // plan: each forward block takes its row's length from indptr and, with
+  // has_invalid, trims the trailing masked entries by a scan of its own row.
   const bool sort = (int64_t)T * L.S > device_cus();
   hipError_t e = hipSuccess;
-  if (sort || has_invalid) {
+  if (sort) {
     smla::PlanParams pp{indptr, indices, idx_bytes, T, smla::tile_tokens(H), has_invalid ? 1 : 0,
                         row_tiles, order};
     e = timed(0, [&](smla::Events ev) { return smla::launch_plan(pp, sort, ev, s); });
@@ -228,7 +229,8 @@ int sparse_mla_fwd(const void* q, int64_t q_stride_t, int64_t q_stride_h,
   fp.o_st = o_stride_t;
   fp.o_sh = o_stride_h;
   fp.lse = lse;
-  fp.row_tiles = (sort || has_invalid) ? row_tiles : nullptr;
+  fp.row_tiles = sort ? row_tiles : nullptr;
+  fp.scan = (!sort && has_invalid) ? 1 : 0;
   fp.order = sort ? order : nullptr;
   fp.part_o = (uint16_t*)(ws + L.part_o);
   fp.part_lse = (float*)(ws + L.part_lse);

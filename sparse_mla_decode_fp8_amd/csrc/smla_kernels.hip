@@ -169,6 +169,38 @@ __device__ __forceinline__ void xcd_unit(int per_row, int& rank, int& sub) {
 // Tiles of a row from its effective length.
 __device__ __forceinline__ int tiles_of(int len, int tile) { return (len + tile - 1) / tile; }
 
+// Tiles of row `row` for a forward block of NT threads: the plan's count when
+// there is a plan; with has_invalid and no plan, 1 + the last slice position
+// whose entry is >= 0, found by every thread of the block (bounded index
+// reads, one round of NT x 4 entries per pass) and a block-wide max through
+// `red` (NT / 64 ints of LDS); otherwise the slice length.
+template <int NT>
+__device__ __forceinline__ int unit_tiles(const FwdParams& p, int row, int beg, int len, int tile, int* red) {
+  if (p.row_tiles) return p.row_tiles[row];
+  if (!p.scan) return tiles_of(len, tile);
+  const __amdgpu_buffer_rsrc_t r = idx_rsrc(p.indices, p.idx_bytes);
+  const int tid = threadIdx.x;
+  int lastp = 0;
+  for (int base = 0; base < len; base += 4 * NT) {
+    int v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = load_idx(r, (uint32_t)(beg + base + NT * j + tid) * 4u);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int pos = base + NT * j + tid;
+      if (pos < len && v[j] >= 0) lastp = max(lastp, pos + 1);
+    }
+  }
+#pragma unroll
+  for (int sh = 32; sh >= 1; sh >>= 1) lastp = max(lastp, __shfl_xor(lastp, sh));
+  if ((tid & 63) == 0) red[tid >> 6] = lastp;
+  __syncthreads();
+  int m = 0;
+#pragma unroll
+  for (int k = 0; k < NT / 64; ++k) m = max(m, red[k]);
+  return tiles_of(m, tile);
+}
+
 // has_invalid only: one wave per row finds 1 + the last slice position whose
 // entry is >= 0 (bounded index reads) and stores the row's tile count.
 __global__ __launch_bounds__(256) void smla_plan_scan_kernel(PlanParams p) {
@@ -303,7 +335,7 @@ __global__ __launch_bounds__(64 * HT * TG, 1) void smla_fwd_kernel(FwdParams p) 
   const int row = p.order ? p.order[rank] : rank;
   const int beg = p.indptr[row];
   const int len = max(p.indptr[row + 1] - beg, 0);
-  const int tiles = p.row_tiles ? p.row_tiles[row] : (len + C::kTile - 1) / C::kTile;
+  const int tiles = unit_tiles<C::kThreads>(p, row, beg, len, C::kTile, (int*)&s_m[0][0]);
   const int ct = (tiles + p.S - 1) / p.S;
   const int t0 = min(chunk * ct, tiles);
   const int t1 = min(t0 + ct, tiles);
@@ -761,7 +793,7 @@ __global__ __launch_bounds__(n16::kThreads, 1) void smla_fwd16_kernel(FwdParams 
   const int row = p.order ? p.order[rank] : rank;
   const int beg = p.indptr[row];
   const int len = max(p.indptr[row + 1] - beg, 0);
-  const int tiles = p.row_tiles ? p.row_tiles[row] : (len + kTile - 1) / kTile;
+  const int tiles = unit_tiles<kThreads>(p, row, beg, len, kTile, (int*)(s_lds + kMxOff));
   const int ct = (tiles + p.S - 1) / p.S;
   const int t0 = min(chunk * ct, tiles);
   const int t1 = min(t0 + ct, tiles);
