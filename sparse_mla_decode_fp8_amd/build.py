@@ -35,6 +35,8 @@ def command(out: str, extra=()) -> list:
         # packed fp32 VALU forms are kept out of the generated code
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-Wno-unused-command-line-argument",
+        # scalar kernel arguments are preloaded into SGPRs at wave launch
+        "-mllvm", "-amdgpu-kernarg-preload-count=16",
         "-I", INCLUDE, "-I", CSRC,
         *[os.path.join(CSRC, s) for s in SOURCES],
         *extra,

@@ -231,6 +231,9 @@ int sparse_mla_fwd(const void* q, int64_t q_stride_t, int64_t q_stride_h,
   fp.lse = lse;
   fp.row_tiles = sort ? row_tiles : nullptr;
   fp.scan = (!sort && has_invalid) ? 1 : 0;
+  // slices laid out at a fixed stride (a [T, top-k] index buffer) let each
+  // block start its index reads before indptr arrives
+  fp.stride = (!sort && nnz % T == 0 && nnz / T > 0) ? (int32_t)(nnz / T) : 0;
   fp.order = sort ? order : nullptr;
   fp.part_o = (uint16_t*)(ws + L.part_o);
   fp.part_lse = (float*)(ws + L.part_lse);

@@ -37,6 +37,7 @@ struct FwdParams {
   float* lse;          // nullable
   const int32_t* row_tiles;  // nullable: tiles from a scan of the slice (scan) or indptr
   int32_t scan;        // no plan and has_invalid: each block finds its row's last entry >= 0
+  int32_t stride;      // > 0: no plan and every slice may start at row * stride (a guess the kernel checks)
   const int32_t* order;      // nullable: rows in their own order
   uint16_t* part_o;    // f16 bits [T*S, H, 512] when S > 1
   float* part_lse;     // [T*S, H]  (log2 units) when S > 1

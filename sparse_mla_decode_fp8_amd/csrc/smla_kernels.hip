@@ -777,7 +777,16 @@ __device__ __forceinline__ void wait_vm() {
 }
 }  // namespace n16
 
-__global__ __launch_bounds__(n16::kThreads, 1) void smla_fwd16_kernel(FwdParams p) {
+// The fields the prologue needs first come as separate scalar arguments ahead
+// of the parameter block, so that they are preloaded into SGPRs at wave
+// launch instead of waiting for a load of the kernel arguments.  `stride`
+// (> 0) is the slice stride nnz / T when there is no plan and nnz divides
+// evenly: each block then guesses its slice start (rank * stride) and queues
+// its first index tiles before indptr arrives, and queues them again from the
+// real start if the guess was wrong.
+__global__ __launch_bounds__(n16::kThreads, 1) void smla_fwd16_kernel(
+    const int32_t* __restrict__ indptr, const int32_t* __restrict__ indices, const uint16_t* __restrict__ qbase,
+    int32_t T, int32_t S, uint32_t idx_bytes, int32_t stride, FwdParams p) {
   using namespace n16;
   __shared__ __attribute__((aligned(1024))) uint8_t s_lds[kBytes];
 
@@ -788,50 +797,64 @@ __global__ __launch_bounds__(n16::kThreads, 1) void smla_fwd16_kernel(FwdParams 
   const int g = lane >> 4;
 
   int rank, chunk;
-  xcd_unit(p.S, rank, chunk);
-  if (rank >= p.T) return;
+  xcd_unit(S, rank, chunk);
+  if (rank >= T) return;
+
+  const uint32_t base = lds_addr(s_lds);
+  const __amdgpu_buffer_rsrc_t irs = idx_rsrc(indices, idx_bytes);
+  auto ring_at = [&](int n) -> uint32_t { return base + kIdxRingOff + (n & (kIdxRing - 1)) * kTile * 4; };
+  // index DMA of tile n of the slice starting at b: this wave's 16 entries
+  // (lanes 0..15).  Positions past nnz read 0 (bounded reads); positions past
+  // the row are masked in fill_table.
+  auto issue_idx_at = [&](int b, int n) {
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(ring_at(n) + 64 * w);
+    if (lane < 16) buf_dma4(irs, (uint32_t)(b + n * kTile + 16 * w + lane) * 4u, dst);
+  };
+  // speculative start (no plan: row = rank)
+  const int beg_g = rank * stride;
+  const int tiles_g = (stride + kTile - 1) / kTile;
+  const int t0_g = min(chunk * ((tiles_g + S - 1) / S), tiles_g);
+  if (stride > 0) {
+    issue_idx_at(beg_g, t0_g);
+    issue_idx_at(beg_g, t0_g + 1);
+    issue_idx_at(beg_g, t0_g + 2);
+  }
+
   const int row = p.order ? p.order[rank] : rank;
-  const int beg = p.indptr[row];
-  const int len = max(p.indptr[row + 1] - beg, 0);
+  const int beg = indptr[row];
+  const int len = max(indptr[row + 1] - beg, 0);
   const int tiles = unit_tiles<kThreads>(p, row, beg, len, kTile, (int*)(s_lds + kMxOff));
-  const int ct = (tiles + p.S - 1) / p.S;
+  const int ct = (tiles + S - 1) / S;
   const int t0 = min(chunk * ct, tiles);
   const int t1 = min(t0 + ct, tiles);
-  const int unit = row * p.S + chunk;
-  const bool split = p.S > 1;
+  const int unit = row * S + chunk;
+  const bool split = S > 1;
+  const int H = p.H;
   const int h = t;  // head of this lane in QK (C column) and PV (B column)
-  const bool h_ok = h < p.H;
+  const bool h_ok = h < H;
 
   if (t0 >= t1) {  // nothing to attend: zero output / -inf lse, or an empty partial
+    if (stride > 0) wait_vm_all();  // the speculative index DMA must land before the block ends
     if (split) {
-      for (int hh = tid; hh < p.H; hh += kThreads) p.part_lse[(int64_t)unit * p.H + hh] = -INFINITY;
+      for (int hh = tid; hh < H; hh += kThreads) p.part_lse[(int64_t)unit * H + hh] = -INFINITY;
     } else {
-      for (int e = tid; e < p.H * (kLat / 8); e += kThreads) {
+      for (int e = tid; e < H * (kLat / 8); e += kThreads) {
         const int hh = e / (kLat / 8), d = (e % (kLat / 8)) * 8;
         *(v4i*)(p.out + row * p.o_st + hh * p.o_sh + d) = v4i{0, 0, 0, 0};
       }
       if (p.lse)
-        for (int hh = tid; hh < p.H; hh += kThreads) p.lse[(int64_t)row * p.H + hh] = -INFINITY;
+        for (int hh = tid; hh < H; hh += kThreads) p.lse[(int64_t)row * H + hh] = -INFINITY;
     }
     return;
   }
 
-  const uint32_t base = lds_addr(s_lds);
-  const __amdgpu_buffer_rsrc_t irs = idx_rsrc(p.indices, p.idx_bytes);
   const uint8_t* const kv = p.kv;
   const uint8_t* const zero = p.zero;
   auto lat_at = [&](int st) -> uint32_t { return base + kLatOff + st * kLatStage; };
-  auto ring_at = [&](int n) -> uint32_t { return base + kIdxRingOff + (n & (kIdxRing - 1)) * kTile * 4; };
   auto tab_at = [&](int n) -> uint32_t { return base + kTabOff + (n & 1) * kTile * 8; };
   // Every wave touches only its own 16 entries of the index ring and the
   // address table, so those need no barrier.
-
-  // index DMA of tile n: this wave's 16 entries (lanes 0..15).  Positions past
-  // nnz read 0 (bounded reads); positions past the row are masked in fill_table.
-  auto issue_idx = [&](int n) {
-    const uint32_t dst = __builtin_amdgcn_readfirstlane(ring_at(n) + 64 * w);
-    if (lane < 16) buf_dma4(irs, (uint32_t)(beg + n * kTile + 16 * w + lane) * 4u, dst);
-  };
+  auto issue_idx = [&](int n) { issue_idx_at(beg, n); };
   // record addresses of this wave's tokens of tile n (masked ones: the zero
   // record); returns the wave's valid-token mask
   auto fill_table = [&](int n) -> uint32_t {
@@ -871,15 +894,23 @@ __global__ __launch_bounds__(n16::kThreads, 1) void smla_fwd16_kernel(FwdParams 
   // t0-2 and t0-1, so every iteration sees the same order of loads:
   //   ... S(n) | I(n+3) | L(n+1) S(n+1) | I(n+4) ...
   // (L latent DMA, S side loads, I index DMA of a tile).
+  // index tiles t0 .. t0+2, unless the speculative ones are those
+  if (!(stride > 0 && beg == beg_g && t0 == t0_g)) {
+    if (stride > 0) wait_vm_all();  // the guessed tiles land before the ring is refilled
+    issue_idx(t0);
+    issue_idx(t0 + 1);
+    issue_idx(t0 + 2);
+  }
+  // wave w loads q heads 2w and 2w+1: chunk c (16 B, 72 per head) of head hh
+  // lands at q_lds + kQRow hh + 16 c; heads >= H are not loaded (their lanes
+  // use zeros).  nq: q DMA instructions this wave issues.
+  const int nq = 2 * ((2 * w < H) + (2 * w + 1 < H));
   {
-    // wave w loads heads 2w and 2w+1: chunk c (16 B, 72 per head) of head hh
-    // lands at q_lds + kQRow hh + 16 c; heads >= H are not loaded (their
-    // lanes use zeros)
-    const uint16_t* qrow = p.q + row * p.q_st;
+    const uint16_t* qrow = qbase + row * p.q_st;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int hh = 2 * w + j;
-      if (hh < p.H) {
+      if (hh < H) {
         const uint16_t* qh = qrow + (int64_t)hh * p.q_sh;
         const uint32_t dst = base + kQOff + kQRow * hh;
         dma16((const uint8_t*)(qh + 8 * lane), __builtin_amdgcn_readfirstlane(dst));
@@ -887,17 +918,18 @@ __global__ __launch_bounds__(n16::kThreads, 1) void smla_fwd16_kernel(FwdParams 
       }
     }
   }
-  issue_idx(t0);
-  issue_idx(t0 + 1);
-  issue_idx(t0 + 2);
-  wait_vm_all();  // this wave's q chunks and index tiles have landed
+  // this wave's index tiles have landed (its q chunks may still be in flight)
+  if (nq == 4) wait_vm<4>();
+  else if (nq == 2) wait_vm<2>();
+  else wait_vm<0>();
   Side sA, sB;    // tiles t0, t0+2, ... use sA; t0+1, t0+3, ... sB
   sA.vmask = fill_table(t0);
   sB.vmask = (t0 + 1 < t1) ? fill_table(t0 + 1) : 0u;
   issue_latent(t0, 0);
   load_side(t0, sA);
   issue_idx(t0 + 3);
-  __syncthreads();  // every wave's q chunks have landed
+  wait_vm<kTileVm + 1>();  // this wave's q chunks have landed (tile t0 and I(t0+3) may not)
+  __syncthreads();         // every wave's q chunks have landed
   // q as bf16 B operands (head = lane column t).  Latent K-step 2m / 2m+1: dims
   // 64m + 16g + [0..7] / [8..15]; rope K-step i: dims 512 + 32i + 8g + [0..7].
   v8bf qlat[16];
@@ -1081,8 +1113,8 @@ __global__ __launch_bounds__(n16::kThreads, 1) void smla_fwd16_kernel(FwdParams 
   const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;
   const float l2 = l_run > 0.0f ? m_ref + __builtin_log2f(l_run) - kShift : -INFINITY;
   if (w == 0 && g == 0 && h_ok) {
-    if (split) p.part_lse[(int64_t)unit * p.H + h] = l2;
-    else if (p.lse) p.lse[(int64_t)row * p.H + h] = l2 * kLn2;
+    if (split) p.part_lse[(int64_t)unit * H + h] = l2;
+    else if (p.lse) p.lse[(int64_t)row * H + h] = l2 * kLn2;
   }
   if (h_ok) {
 #pragma unroll
@@ -1090,7 +1122,7 @@ __global__ __launch_bounds__(n16::kThreads, 1) void smla_fwd16_kernel(FwdParams 
       const v4f acc = O[dt] * inv;
       const int d = 64 * w + 16 * dt + 4 * g;
       if (split) {
-        st_half4(p.part_o + ((int64_t)unit * p.H + h) * kLat + d, acc);
+        st_half4(p.part_o + ((int64_t)unit * H + h) * kLat + d, acc);
       } else {
         const uint32_t w0 = f32_to_bf16_rne(acc.x) | ((uint32_t)f32_to_bf16_rne(acc.y) << 16);
         const uint32_t w1 = f32_to_bf16_rne(acc.z) | ((uint32_t)f32_to_bf16_rne(acc.w) << 16);
@@ -1233,7 +1265,7 @@ hipError_t launch_fwd(const FwdParams& p, Events ev, hipStream_t s) {
     case 1: {
       const int64_t blocks = xcd_grid(p.T, p.S);
       hipExtLaunchKernelGGL(smla_fwd16_kernel, dim3((unsigned)blocks), dim3(n16::kThreads), 0, s,
-                            ev.start, ev.stop, 0, p);
+                            ev.start, ev.stop, 0, p.indptr, p.indices, p.q, p.T, p.S, p.idx_bytes, p.stride, p);
       return hipGetLastError();
     }
     case 2: return launch_fwd_t<2, 2>(p, ev, s);
