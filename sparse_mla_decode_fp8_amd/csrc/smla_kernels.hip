@@ -927,9 +927,15 @@ __global__ __launch_bounds__(n16::kThreads, 1) void smla_fwd16_kernel(
   sB.vmask = (t0 + 1 < t1) ? fill_table(t0 + 1) : 0u;
   issue_latent(t0, 0);
   load_side(t0, sA);
-  issue_idx(t0 + 3);
-  wait_vm<kTileVm + 1>();  // this wave's q chunks have landed (tile t0 and I(t0+3) may not)
-  __syncthreads();         // every wave's q chunks have landed
+  // Index tiles past the unit's end are never queued (from here on), so
+  // none is left in flight when the block ends.
+  if (t0 + 3 < t1) {
+    issue_idx(t0 + 3);
+    wait_vm<kTileVm + 1>();  // this wave's q chunks have landed (tile t0 and I(t0+3) may not)
+  } else {
+    wait_vm<kTileVm>();
+  }
+  __syncthreads();  // every wave's q chunks have landed
   // q as bf16 B operands (head = lane column t).  Latent K-step 2m / 2m+1: dims
   // 64m + 16g + [0..7] / [8..15]; rope K-step i: dims 512 + 32i + 8g + [0..7].
   v8bf qlat[16];
@@ -978,22 +984,30 @@ __global__ __launch_bounds__(n16::kThreads, 1) void smla_fwd16_kernel(
   // One tile: n, its stage st (= (n - t0) & 1) and its side registers.
   auto tile = [&](int n, int st, Side& sd) __attribute__((always_inline)) {
     // this wave's records, scales and rope of tile n have landed; the loads
-    // queued after them (I(n+3), tile n+1's, I(n+4)) may still be in flight.
-    // Tile t0 alone is queued by itself (followed by I(t0+3) only), so that
-    // the first records of every block arrive as early as they can; tile
-    // t0+1 follows as soon as they have.
+    // queued after them (I(n+3), tile n+1's, I(n+4), each only if that tile
+    // exists) may still be in flight.  Tile t0 alone is queued by itself
+    // (followed by I(t0+3) only), so that the first records of every block
+    // arrive as early as they can; tile t0+1 follows as soon as they have.
+    const int left = t1 - n;  // tiles left, this one included
     if (n == t0) {
-      wait_vm<1>();
-      if (n + 1 < t1) {
+      if (left >= 4) wait_vm<1>();
+      else wait_vm<0>();
+      if (left >= 2) {
         issue_latent(n + 1, st ^ 1);
         load_side(n + 1, sB);
       }
-      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // ring slot t0 was read before I(t0+4) lands in it
-      issue_idx(n + 4);
-    } else if (n + 1 < t1) {
+      if (left >= 5) {
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // ring slot t0 was read before I(t0+4) lands in it
+        issue_idx(n + 4);
+      }
+    } else if (left >= 5) {
       wait_vm<2 + kTileVm>();
+    } else if (left == 4) {
+      wait_vm<1 + kTileVm>();
+    } else if (left >= 2) {
+      wait_vm<kTileVm>();
     } else {
-      wait_vm<2>();
+      wait_vm<0>();
     }
     pin(sd);
 
@@ -1089,17 +1103,21 @@ __global__ __launch_bounds__(n16::kThreads, 1) void smla_fwd16_kernel(
       for (int dt = 0; dt < 4; ++dt)
         O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(cvt8_f16(vr[dt]), pb, O[dt], 0, 0, 0);
     }
+    if (left == 1) return;  // the last tile: nothing reuses the stage or P
+
     // every wave is done with stage st, P, the scales and the maxima of tile n
     __syncthreads();
 
     // ---- tile n+2 into stage st and this side set, then index tile n+5
-    if (n + 2 < t1) {
+    if (left >= 3) {
       sd.vmask = fill_table(n + 2);
       issue_latent(n + 2, st);
       load_side(n + 2, sd);
     }
-    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // ring slot n+1 was read (fill_table) before its reload lands
-    issue_idx(n + 5);
+    if (left >= 6) {
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // ring slot n+1 was read (fill_table) before its reload lands
+      issue_idx(n + 5);
+    }
   };
 
   for (int n = t0; n < t1; n += 2) {
