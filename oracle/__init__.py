@@ -18,7 +18,7 @@ Sources (cited by page title and section, never by line):
                  (merge of chunk partials by their max and sum).
   [OCP FP8]      OCP 8-bit floating point specification, E4M3 encoding
                  (the format the FlyDSL page's writer rule with its 448 bound
-                 implies).
+                 implies), with round-to-nearest-even conversion.
 
 Every function is pinned by CPU tests in ``tests/test_oracle.py`` against
 closed forms, library routines, brute force or invariants; no oracle function
@@ -36,4 +36,11 @@ from .attention import (  # noqa: F401
     row_attention,
     sparse_mla_fwd,
     lse_merge,
+)
+from .writer import (  # noqa: F401
+    pow2ceil,
+    e4m3_encode,
+    block_scales,
+    encode_records,
+    write_cache,
 )

@@ -406,3 +406,135 @@ def test_planted_mistakes(monkeypatch, name):
     monkeypatch.setattr(oatt, attr, fn)
     failed = _pins_pass()
     assert failed, f"planted mistake {name!r} went unnoticed by every pin"
+
+
+# ----------------------------------------------------------------- cache writer pins
+
+import oracle.writer as owriter  # noqa: E402
+
+
+def _e4m3_finite_codes():
+    return [c for c in range(256) if (c & 0x7F) != 0x7F]
+
+
+def test_e4m3_encode_roundtrips_every_code():
+    """Every finite code's value encodes back to that code (-0.0 to 0x80)."""
+    codes = np.array(_e4m3_finite_codes())
+    vals = oracle.E4M3_TABLE[codes]
+    assert np.array_equal(owriter.e4m3_encode(vals), codes.astype(np.uint8))
+
+
+def test_e4m3_encode_ties_to_even():
+    """The midpoint of two neighbouring codes goes to the one with the even
+    mantissa; a hair above or below goes to the nearer one (closed form)."""
+    for c in range(0, 0x7E):  # positive finite neighbours (c, c + 1)
+        lo, hi = oracle.E4M3_TABLE[c], oracle.E4M3_TABLE[c + 1]
+        mid = (lo + hi) / 2.0
+        even = c if (c & 1) == 0 else c + 1
+        assert owriter.e4m3_encode(mid) == even, hex(c)
+        assert owriter.e4m3_encode(-mid) == (0x80 | even), hex(c)
+        eps = (hi - lo) * 2.0 ** -20
+        assert owriter.e4m3_encode(mid - eps) == c
+        assert owriter.e4m3_encode(mid + eps) == c + 1
+
+
+def test_e4m3_encode_matches_torch():
+    """Library routine: torch's float8_e4m3fn cast (round to nearest even)."""
+    rng = np.random.default_rng(21)
+    y = np.concatenate([
+        rng.uniform(-448.0, 448.0, 20000),
+        rng.uniform(-2.0 ** -6, 2.0 ** -6, 20000),           # subnormal range
+        np.ldexp(rng.uniform(-1, 1, 20000), rng.integers(-12, 9, 20000)),
+    ])
+    ref = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(owriter.e4m3_encode(y), ref)
+
+
+def test_e4m3_encode_rejects_out_of_range():
+    with pytest.raises(ValueError):
+        owriter.e4m3_encode(np.array([449.0]))
+
+
+def test_pow2ceil_closed_form(golden):
+    for k in range(-30, 20):
+        assert owriter.pow2ceil(2.0 ** k) == 2.0 ** k
+        assert owriter.pow2ceil(2.0 ** k * (1 + 2.0 ** -40)) == 2.0 ** (k + 1)
+        assert owriter.pow2ceil(2.0 ** k * 0.75) == 2.0 ** k
+    for amax, scale in golden("writer_bound.txt"):
+        assert owriter.pow2ceil(max(float(amax), owriter.AMAX_FLOOR) / 448.0) == float(scale)
+
+
+def _bf16_bits(x):
+    return torch.from_numpy(np.asarray(x, np.float32)).to(torch.bfloat16).view(torch.int16) \
+        .numpy().view(np.uint16)
+
+
+def test_writer_records_decode_within_half_step():
+    """Decoding a written record gives each latent value back within half an
+    e4m3 step of its magnitude times the block scale, and the rope exactly;
+    every block's largest value lands in (224, 448] times the scale."""
+    rng = np.random.default_rng(22)
+    n = 64
+    x = rng.standard_normal((n, 512)) * np.exp(rng.uniform(-12, 8, (n, 4))).repeat(128, axis=1)
+    x[:4, :128] = 0.0  # floored blocks
+    lb = _bf16_bits(x)
+    rb = _bf16_bits(rng.standard_normal((n, 64)))
+    rec = owriter.encode_records(lb, rb)
+    K = oracle.decode_records(rec)
+    xb = oracle.bf16_bits_to_f64(lb)
+    sc = np.frombuffer(rec[:, 512:528].tobytes(), "<f4").reshape(n, 4).astype(np.float64)
+    s = np.repeat(sc, 128, axis=1)
+    y = np.abs(xb) / s
+    step = np.where(y >= 2.0 ** -6, np.ldexp(1.0, np.frexp(np.maximum(y, 2.0 ** -6))[1] - 4), 2.0 ** -9)
+    assert np.all(np.abs(K[:, :512] - xb) <= 0.5 * step * s)
+    assert np.array_equal(K[:, 512:], oracle.bf16_bits_to_f64(rb))
+    amax = np.abs(xb).reshape(n, 4, 128).max(axis=2)
+    live = amax >= 1e-4
+    assert np.all((amax / sc)[live] <= 448.0) and np.all((amax / sc)[live] > 224.0)
+    assert np.all(sc[~live] == 2.0 ** -22)
+
+
+def test_writer_matches_generator_rule():
+    """The oracle writer and the workload generator (torch casts) store the
+    same bytes for bf16 inputs."""
+    rng = np.random.default_rng(23)
+    x = rng.standard_normal((32, 512)) * 3.0
+    x[:, 5] = 1000.0
+    lb, rb = _bf16_bits(x), _bf16_bits(rng.standard_normal((32, 64)))
+    lat = torch.from_numpy(oracle.bf16_bits_to_f64(lb).astype(np.float32))
+    rope = torch.from_numpy(oracle.bf16_bits_to_f64(rb).astype(np.float32))
+    assert np.array_equal(owriter.encode_records(lb, rb), synth.encode_records(lat, rope).numpy())
+
+
+def test_write_cache_slots():
+    rng = np.random.default_rng(24)
+    kv = rng.integers(0, 256, size=(10, 656), dtype=np.uint8)
+    lb, rb = _bf16_bits(rng.standard_normal((4, 512))), _bf16_bits(rng.standard_normal((4, 64)))
+    out = owriter.write_cache(kv, lb, rb, [7, -1, 2, 10])
+    rec = owriter.encode_records(lb, rb)
+    assert np.array_equal(out[7], rec[0]) and np.array_equal(out[2], rec[2])
+    untouched = [i for i in range(10) if i not in (2, 7)]
+    assert np.array_equal(out[untouched], kv[untouched])
+
+
+@pytest.mark.parametrize("name", ["half_away", "scale_floor", "no_floor"])
+def test_writer_planted_mistakes(monkeypatch, name):
+    """Plausible writer mistakes, planted in the oracle, fail some writer pin."""
+    checks = [test_e4m3_encode_ties_to_even, test_e4m3_encode_matches_torch,
+              test_writer_records_decode_within_half_step]
+    if name == "half_away":
+        monkeypatch.setattr(np, "rint", lambda v: np.floor(np.asarray(v) + 0.5))
+    elif name == "scale_floor":
+        def floor2(x):
+            m, e = np.frexp(np.asarray(x, np.float64))
+            return np.ldexp(1.0, (e - 1).astype(np.int64))
+        monkeypatch.setattr(owriter, "pow2ceil", floor2)
+    else:
+        monkeypatch.setattr(owriter, "AMAX_FLOOR", 0.0)
+    failed = 0
+    for fn in checks:
+        try:
+            fn()
+        except Exception:  # noqa: BLE001 - any failure counts as caught
+            failed += 1
+    assert failed, f"planted writer mistake {name!r} went unnoticed"
