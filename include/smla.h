@@ -144,6 +144,36 @@ int sparse_mla_fwd(const void* q, int64_t q_stride_t, int64_t q_stride_h,
 int sparse_mla_decode_rows(const void* kv, int64_t n_kv, const int32_t* rows, int64_t n,
                            float* out, void* stream);
 
+/*
+ * sparse_mla_cache_write -- write KV records in the fp8_ds_mla layout (the
+ * step before the forward: vLLM's concat_and_cache_ds_mla writer, whose rule
+ * the FlyDSL page states in its section "Preconditions the host cannot
+ * check").  For token i with slots[i] in [0, n_kv), record slots[i] of kv
+ * becomes:
+ *   bytes   0..511  e4m3 (OCP E4M3FN) codes of latent[i, j] / scale[j / 128],
+ *                   rounded to nearest, ties to even;
+ *   bytes 512..527  the four f32 scales, scale[b] = pow2ceil(max(amax_b, 1e-4)
+ *                   / 448) with amax_b the largest |latent[i, 128b .. 128b+127]|
+ *                   (a power of two, so every record satisfies the forward's
+ *                   preconditions whenever |latent| <= 57344);
+ *   bytes 528..655  rope[i, 0..63] as bf16, copied.
+ * Tokens with slots[i] < 0 (padding) or >= n_kv are skipped; no other byte of
+ * kv changes.  Two tokens with the same slot race (either record may win).
+ *
+ *   latent  device, bf16 [n, 512] at latent + i*latent_stride + j; 16-byte
+ *           aligned, latent_stride a multiple of 8 elements.  Finite values.
+ *   rope    device, bf16 [n, 64] at rope + i*rope_stride + j; 8-byte aligned,
+ *           rope_stride a multiple of 4 elements.
+ *   slots   device, int64 [n], 8-byte aligned.
+ *   kv      device, uint8 [n_kv, 656], rows contiguous, 16-byte aligned.
+ * Returns SMLA_OK, or SMLA_EINVAL / SMLA_EHIP with nothing queued.  Queues one
+ * kernel on `stream`; no host sync, no allocation.
+ */
+int sparse_mla_cache_write(const void* latent, int64_t latent_stride,
+                           const void* rope, int64_t rope_stride,
+                           const int64_t* slots, int64_t n,
+                           void* kv, int64_t n_kv, void* stream);
+
 /* Message for the calling thread's last non-OK status ("" if none). */
 const char* sparse_mla_last_error(void);
 

@@ -50,6 +50,8 @@ _lib.sparse_mla_fwd.argtypes = [
     _vp,                    # stream
 ]
 _lib.sparse_mla_fwd.restype = ctypes.c_int
+_lib.sparse_mla_cache_write.argtypes = [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp]
+_lib.sparse_mla_cache_write.restype = ctypes.c_int
 _lib.sparse_mla_decode_rows.argtypes = [_vp, _i64, _vp, _i64, _vp, _vp]
 _lib.sparse_mla_decode_rows.restype = ctypes.c_int
 _lib.sparse_mla_last_error.argtypes = []
@@ -63,7 +65,7 @@ _lib.sparse_mla_profile_end.restype = ctypes.c_int
 
 EXPORTED = (
     "sparse_mla_supported", "sparse_mla_workspace_bytes", "sparse_mla_split_for", "sparse_mla_fwd",
-    "sparse_mla_decode_rows", "sparse_mla_last_error", "sparse_mla_set_option",
+    "sparse_mla_cache_write", "sparse_mla_decode_rows", "sparse_mla_last_error", "sparse_mla_set_option",
     "sparse_mla_profile_begin", "sparse_mla_profile_end",
 )
 
@@ -175,6 +177,29 @@ def fwd(q: torch.Tensor, kv: torch.Tensor, indptr: torch.Tensor, indices: torch.
         _stream(dev))
     _check(rc)
     return out, lse
+
+
+def cache_write(latent: torch.Tensor, rope: torch.Tensor, slots: torch.Tensor, kv: torch.Tensor) -> torch.Tensor:
+    """Write records kv[slots[i]] from bf16 latent [n, 512] and rope [n, 64]
+    (fp8_ds_mla writer rule); slots int64 [n], negative = skip.  Returns kv."""
+    if latent.dtype != torch.bfloat16 or latent.dim() != 2 or latent.shape[1] != 512:
+        raise ValueError("latent must be bf16 [n, 512]")
+    if rope.dtype != torch.bfloat16 or rope.dim() != 2 or rope.shape != (latent.shape[0], 64):
+        raise ValueError("rope must be bf16 [n, 64]")
+    if latent.stride(1) != 1 or rope.stride(1) != 1:
+        raise ValueError("latent and rope rows must be contiguous")
+    if kv.dtype != torch.uint8 or kv.dim() != 2 or kv.shape[1] != RECORD_BYTES or not kv.is_contiguous():
+        raise ValueError(f"kv must be contiguous uint8 [N, {RECORD_BYTES}]")
+    slots = slots.to(torch.int64).contiguous()
+    if slots.numel() != latent.shape[0]:
+        raise ValueError("slots must have one entry per token")
+    for t in (rope, slots, kv):
+        if t.device != latent.device:
+            raise ValueError("all tensors must be on latent's device")
+    _check(_lib.sparse_mla_cache_write(_ptr(latent), latent.stride(0), _ptr(rope), rope.stride(0),
+                                       _ptr(slots), slots.numel(), _ptr(kv), kv.shape[0],
+                                       _stream(latent.device)))
+    return kv
 
 
 def decode_rows(kv: torch.Tensor, rows: torch.Tensor) -> torch.Tensor:

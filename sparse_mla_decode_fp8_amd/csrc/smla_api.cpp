@@ -261,6 +261,29 @@ int sparse_mla_decode_rows(const void* kv, int64_t n_kv, const int32_t* rows, in
   return SMLA_OK;
 }
 
+int sparse_mla_cache_write(const void* latent, int64_t latent_stride,
+                           const void* rope, int64_t rope_stride,
+                           const int64_t* slots, int64_t n,
+                           void* kv, int64_t n_kv, void* stream) {
+  g_err.clear();
+  if (n < 0 || n_kv < 0) return fail(SMLA_EINVAL, "n and n_kv must be >= 0");
+  if (n_kv > INT64_MAX / smla::kRecordBytes) return fail(SMLA_EINVAL, "n_kv out of range: %lld", (long long)n_kv);
+  if (n > (int64_t)0x7fffffff * 4) return fail(SMLA_EINVAL, "n too large for one launch");
+  if (n == 0) return SMLA_OK;
+  if (!latent || !rope || !slots || !kv) return fail(SMLA_EINVAL, "null pointer");
+  if (!aligned(latent, 16) || !aligned(kv, 16) || !aligned(rope, 8) || !aligned(slots, 8))
+    return fail(SMLA_EINVAL, "latent and kv must be 16-byte aligned, rope and slots 8-byte aligned");
+  if (latent_stride < 512 || latent_stride % 8 != 0)
+    return fail(SMLA_EINVAL, "latent_stride must be >= 512 and a multiple of 8 elements");
+  if (rope_stride < 64 || rope_stride % 4 != 0)
+    return fail(SMLA_EINVAL, "rope_stride must be >= 64 and a multiple of 4 elements");
+  smla::CacheWriteParams p{(const uint16_t*)latent, latent_stride, (const uint16_t*)rope, rope_stride,
+                           slots, n, (uint8_t*)kv, n_kv};
+  hipError_t e = smla::launch_cache_write(p, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "cache writer launch");
+  return SMLA_OK;
+}
+
 const char* sparse_mla_last_error(void) { return g_err.c_str(); }
 
 int sparse_mla_set_option(const char* name, int64_t value) {

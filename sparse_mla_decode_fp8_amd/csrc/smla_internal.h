@@ -53,6 +53,17 @@ struct CombineParams {
   float* lse;
 };
 
+struct CacheWriteParams {
+  const uint16_t* latent;  // bf16 bits [n, 512], row stride latent_st elements
+  int64_t latent_st;
+  const uint16_t* rope;    // bf16 bits [n, 64], row stride rope_st elements
+  int64_t rope_st;
+  const int64_t* slots;    // [n]: record index of token i; < 0 or >= n_kv: not written
+  int64_t n;
+  uint8_t* kv;             // [n_kv, 656]
+  int64_t n_kv;
+};
+
 // Head tiling: HT tiles of 16 heads; TG token groups of 32 tokens per tile.
 inline int head_tiles(int H) { return (H + 15) / 16; }
 inline int token_groups(int H) { int ht = head_tiles(H); return ht >= 3 ? 1 : 4 / ht; }
@@ -72,6 +83,7 @@ hipError_t launch_fwd(const FwdParams& p, Events ev, hipStream_t s);
 // Device address of the library's zero record on the current device.
 hipError_t zero_record_address(const uint8_t** out);
 hipError_t launch_combine(const CombineParams& p, Events ev, hipStream_t s);
+hipError_t launch_cache_write(const CacheWriteParams& p, hipStream_t s);
 hipError_t launch_decode_rows(const uint8_t* kv, int64_t n_kv, const int32_t* rows, int64_t n,
                               float* out, hipStream_t s);
 

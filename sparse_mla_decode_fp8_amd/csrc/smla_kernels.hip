@@ -1246,6 +1246,53 @@ __global__ __launch_bounds__(64) void smla_decode_rows_kernel(const uint8_t* kv,
   o[kLat + lane] = __builtin_bit_cast(float, (uint32_t)rb << 16);
 }
 
+// ---------------------------------------------------------------- cache writer
+
+// Writes token i's record at kv[slots[i]] by the fp8_ds_mla writer rule (FlyDSL
+// page, module docstring, "Preconditions the host cannot check"): per 128
+// latent values scale = pow2ceil(max(amax, 1e-4) / 448), an f32 power of two;
+// latent codes = e4m3(x / scale), rounded to nearest even; rope copied as bf16.
+// One wave per token: lane l holds latent values 8l .. 8l+7, so scale block b
+// is lanes 16b .. 16b+15.
+__global__ __launch_bounds__(256) void smla_cache_write_kernel(CacheWriteParams p) {
+  const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (i >= p.n) return;
+  const int lane = threadIdx.x & 63;
+  const int64_t slot = p.slots[i];
+  if (slot < 0 || slot >= p.n_kv) return;  // padding tokens; out-of-range slots are never written
+  uint8_t* rec = p.kv + slot * kRecordBytes;
+
+  const v4i raw = *(const v4i*)(p.latent + i * p.latent_st + 8 * lane);  // 8 bf16
+  float x[8];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    x[2 * k] = __builtin_bit_cast(float, (uint32_t)raw[k] << 16);
+    x[2 * k + 1] = __builtin_bit_cast(float, (uint32_t)raw[k] & 0xFFFF0000u);
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) amax = fmax_(amax, __builtin_fabsf(x[k]));
+#pragma unroll
+  for (int sh = 1; sh < 16; sh <<= 1) amax = fmax_(amax, __shfl_xor(amax, sh));
+  // pow2ceil of v = max(amax, 1e-4) / 448 (a positive normal f32): v itself if
+  // its mantissa is zero, else the next power of two.  The f32 quotient is a
+  // power of two exactly when the exact one is (amax has 8 significant bits),
+  // so the result is the exact rule's.
+  const float v = fmax_(amax, 1e-4f) / 448.0f;
+  const uint32_t vb = __builtin_bit_cast(uint32_t, v);
+  const uint32_t sb = (vb & 0x007FFFFFu) ? (vb & 0x7F800000u) + 0x00800000u : vb;
+  const float scale = __builtin_bit_cast(float, sb);
+  const float inv = __builtin_bit_cast(float, 0x7F000000u - sb);  // 1 / scale, exact
+  int w0 = 0, w1 = 0;
+  w0 = __builtin_amdgcn_cvt_pk_fp8_f32(x[0] * inv, x[1] * inv, w0, false);
+  w0 = __builtin_amdgcn_cvt_pk_fp8_f32(x[2] * inv, x[3] * inv, w0, true);
+  w1 = __builtin_amdgcn_cvt_pk_fp8_f32(x[4] * inv, x[5] * inv, w1, false);
+  w1 = __builtin_amdgcn_cvt_pk_fp8_f32(x[6] * inv, x[7] * inv, w1, true);
+  *(v2i*)(rec + 8 * lane) = v2i{w0, w1};
+  if ((lane & 15) == 0) *(float*)(rec + kScaleOff + 4 * (lane >> 4)) = scale;
+  if (lane < 16) *(v2i*)(rec + kRopeOff + 8 * lane) = *(const v2i*)(p.rope + i * p.rope_st + 4 * lane);
+}
+
 // ---------------------------------------------------------------- launchers
 
 hipError_t zero_record_address(const uint8_t** out) {
@@ -1296,6 +1343,12 @@ hipError_t launch_fwd(const FwdParams& p, Events ev, hipStream_t s) {
 hipError_t launch_combine(const CombineParams& p, Events ev, hipStream_t s) {
   const int64_t blocks = xcd_grid(p.T, p.H);
   hipExtLaunchKernelGGL(smla_combine_kernel, dim3((unsigned)blocks), dim3(128), 0, s, ev.start, ev.stop, 0, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_cache_write(const CacheWriteParams& p, hipStream_t s) {
+  const int64_t blocks = (p.n + 3) / 4;
+  hipLaunchKernelGGL(smla_cache_write_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

@@ -98,6 +98,23 @@ def test_decode_rows_validation(b):
     assert lib.sparse_mla_decode_rows(FAKE, 10, FAKE, 0, FAKE, None) == 0
 
 
+def test_cache_write_validation(b):
+    lib = b.lib()
+    ok = dict(latent=FAKE, lst=512, rope=FAKE, rst=64, slots=FAKE, n=3, kv=FAKE, n_kv=10)
+
+    def cw(**over):
+        a = dict(ok)
+        a.update(over)
+        return lib.sparse_mla_cache_write(a["latent"], a["lst"], a["rope"], a["rst"], a["slots"],
+                                          a["n"], a["kv"], a["n_kv"], None)
+    for over in (dict(n=-1), dict(n_kv=-1), dict(latent=None), dict(rope=None), dict(slots=None),
+                 dict(kv=None), dict(latent=FAKE + 8), dict(kv=FAKE + 4), dict(rope=FAKE + 4),
+                 dict(slots=FAKE + 4), dict(lst=511), dict(lst=516), dict(rst=62), dict(rst=66)):
+        assert cw(**over) == -1, over
+        assert lib.sparse_mla_last_error()
+    assert cw(n=0, latent=None, rope=None, slots=None, kv=None) == 0
+
+
 def test_profile_state_machine(b):
     lib = b.lib()
     ms = (ctypes.c_double * 3)()
