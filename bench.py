@@ -1,6 +1,7 @@
 """Benchmark of the sparse MLA forward (plan + forward + combine) on one GPU.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
+    python bench.py --op cache_write [--records N]     # the record writer
 
 One "step" is one call of the whole op on one batch of the workload.  Prints
 one JSON line (the last line of stdout).  Inputs are seeded synthetic tensors
@@ -146,6 +147,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run plain device copies of known size (counter scaling)")
+    ap.add_argument("--op", choices=("fwd", "cache_write"), default="fwd",
+                    help="fwd: the sparse MLA forward (default); cache_write: the record writer")
+    ap.add_argument("--records", type=int, default=65536, help="records written per call (cache_write)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -159,6 +163,8 @@ def main() -> int:
 
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    if args.op == "cache_write":
+        return bench_cache_write(args, torch, smla, dev)
     cfg = synth.make_config(args.config)
     print(f"[bench] generating {cfg['name']}", file=sys.stderr, flush=True)
     w = synth.make_workload(args.config, device="cuda")
@@ -270,6 +276,73 @@ def main() -> int:
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_budget, 16)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+WRITE_READ_BYTES = 512 * 2 + 64 * 2 + 8   # bf16 latent + bf16 rope + int64 slot per token
+WRITE_WRITTEN_BYTES = 656                  # one record per token
+
+
+def bench_cache_write(args, torch, smla, dev) -> int:
+    """The record writer on n tokens written to a permutation of n slots:
+    algorithmic bytes per token = 1,160 read + 656 written."""
+    n = args.records
+    g = torch.Generator(device=dev)
+    g.manual_seed(2024)
+    lat = torch.randn(n, 512, generator=g, device=dev).to(torch.bfloat16)
+    rope = torch.randn(n, 64, generator=g, device=dev).to(torch.bfloat16)
+    slots = torch.randperm(n, generator=g, device=dev).to(torch.int64)
+    kv = torch.empty(n, 656, dtype=torch.uint8, device=dev)
+    per_call = n * (WRITE_READ_BYTES + WRITE_WRITTEN_BYTES)
+
+    def step():
+        smla.cache_write(lat, rope, slots, kv)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    with smla.KernelTimer(args.steps) as kt:
+        for _ in range(args.steps):
+            step()
+    torch.cuda.synchronize()
+    kms = kt.ms["cache_write"] / max(kt.launches["cache_write"], 1)
+    achieved = per_call / (kms * 1e-3) / 1e9
+    result = {
+        "metric": "cache write GB/s (fp8_ds_mla records from bf16 latent + rope)",
+        "value": round(per_call / (ms_per_step * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"cache_write_N{n}", "records": n,
+                   "bytes_per_token": WRITE_READ_BYTES + WRITE_WRITTEN_BYTES},
+        "records_per_s": round(n / (ms_per_step * 1e-3), 1),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "kernel": "smla_cache_write_kernel",
+            "bytes_per_launch": per_call,
+            "launch_ms": round(kms, 5),
+        },
+    }
     print(json.dumps(result), flush=True)
     return 0
 

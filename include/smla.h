@@ -195,10 +195,12 @@ int sparse_mla_set_option(const char* name, int64_t value);
  * the last one's end, so queueing between launches is not counted);
  * sparse_mla_profile_end() waits for
  * those events, writes the summed device time in milliseconds and the launch
- * count of each kernel kind (0 plan, 1 forward, 2 combine) to ms[3] and
- * launches[3], and stops recording.  Creates and destroys events on the host
+ * count of each kernel kind (0 plan, 1 forward, 2 combine, 3 cache writer) to
+ * ms[SMLA_PROFILE_KINDS] and launches[SMLA_PROFILE_KINDS], and stops
+ * recording.  Calls of sparse_mla_cache_write are recorded too.  Creates and destroys events on the host
  * only; no device memory is allocated.
  */
+#define SMLA_PROFILE_KINDS 4
 int sparse_mla_profile_begin(int32_t max_calls);
 int sparse_mla_profile_end(double* ms, int64_t* launches);
 

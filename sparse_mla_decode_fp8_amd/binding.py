@@ -215,9 +215,10 @@ def decode_rows(kv: torch.Tensor, rows: torch.Tensor) -> torch.Tensor:
 
 class KernelTimer:
     """HIP-event timing of the library's kernels over the calls made inside
-    the ``with`` block: ``.ms`` and ``.launches`` per kind (plan, fwd, combine)."""
+    the ``with`` block: ``.ms`` and ``.launches`` per kind (plan, fwd, combine,
+    cache_write)."""
 
-    KINDS = ("plan", "fwd", "combine")
+    KINDS = ("plan", "fwd", "combine", "cache_write")
 
     def __init__(self, max_calls: int):
         self.max_calls = max_calls
@@ -229,8 +230,8 @@ class KernelTimer:
         return self
 
     def __exit__(self, *exc):
-        ms = (ctypes.c_double * 3)()
-        n = (_i64 * 3)()
+        ms = (ctypes.c_double * len(self.KINDS))()
+        n = (_i64 * len(self.KINDS))()
         _check(_lib.sparse_mla_profile_end(ms, n))
         self.ms = {k: ms[i] for i, k in enumerate(self.KINDS)}
         self.launches = {k: int(n[i]) for i, k in enumerate(self.KINDS)}

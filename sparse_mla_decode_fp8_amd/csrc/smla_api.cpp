@@ -279,7 +279,7 @@ int sparse_mla_cache_write(const void* latent, int64_t latent_stride,
     return fail(SMLA_EINVAL, "rope_stride must be >= 64 and a multiple of 4 elements");
   smla::CacheWriteParams p{(const uint16_t*)latent, latent_stride, (const uint16_t*)rope, rope_stride,
                            slots, n, (uint8_t*)kv, n_kv};
-  hipError_t e = smla::launch_cache_write(p, (hipStream_t)stream);
+  hipError_t e = timed(3, [&](smla::Events ev) { return smla::launch_cache_write(p, ev, (hipStream_t)stream); });
   if (e != hipSuccess) return hip_fail(e, "cache writer launch");
   return SMLA_OK;
 }
@@ -302,7 +302,7 @@ int sparse_mla_profile_begin(int32_t max_calls) {
   if (max_calls <= 0) return fail(SMLA_EINVAL, "max_calls must be > 0");
   std::lock_guard<std::mutex> lk(g_prof.mu);
   if (g_prof.active) return fail(SMLA_EINVAL, "profiling already active");
-  const int pairs = 3 * max_calls;
+  const int pairs = SMLA_PROFILE_KINDS * max_calls;
   g_prof.ev.assign(2 * pairs, nullptr);
   g_prof.kind.assign(pairs, -1);
   for (auto& ev : g_prof.ev) {
@@ -324,8 +324,8 @@ int sparse_mla_profile_end(double* ms, int64_t* launches) {
   g_err.clear();
   std::lock_guard<std::mutex> lk(g_prof.mu);
   if (!g_prof.active) return fail(SMLA_EINVAL, "profiling not active");
-  double acc[3] = {0, 0, 0};
-  int64_t cnt[3] = {0, 0, 0};
+  double acc[SMLA_PROFILE_KINDS] = {};
+  int64_t cnt[SMLA_PROFILE_KINDS] = {};
   int rc = SMLA_OK;
   for (int i = 0; i < g_prof.used; ++i) {
     hipError_t e = hipEventSynchronize(g_prof.ev[2 * i + 1]);
@@ -345,7 +345,7 @@ int sparse_mla_profile_end(double* ms, int64_t* launches) {
   g_prof.active = false;
   g_prof.cap = g_prof.used = 0;
   if (rc != SMLA_OK) return rc;
-  for (int k = 0; k < 3; ++k) {
+  for (int k = 0; k < SMLA_PROFILE_KINDS; ++k) {
     if (ms) ms[k] = acc[k];
     if (launches) launches[k] = cnt[k];
   }

@@ -83,7 +83,7 @@ hipError_t launch_fwd(const FwdParams& p, Events ev, hipStream_t s);
 // Device address of the library's zero record on the current device.
 hipError_t zero_record_address(const uint8_t** out);
 hipError_t launch_combine(const CombineParams& p, Events ev, hipStream_t s);
-hipError_t launch_cache_write(const CacheWriteParams& p, hipStream_t s);
+hipError_t launch_cache_write(const CacheWriteParams& p, Events ev, hipStream_t s);
 hipError_t launch_decode_rows(const uint8_t* kv, int64_t n_kv, const int32_t* rows, int64_t n,
                               float* out, hipStream_t s);
 

@@ -1346,9 +1346,9 @@ hipError_t launch_combine(const CombineParams& p, Events ev, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_cache_write(const CacheWriteParams& p, hipStream_t s) {
+hipError_t launch_cache_write(const CacheWriteParams& p, Events ev, hipStream_t s) {
   const int64_t blocks = (p.n + 3) / 4;
-  hipLaunchKernelGGL(smla_cache_write_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p);
+  hipExtLaunchKernelGGL(smla_cache_write_kernel, dim3((unsigned)blocks), dim3(256), 0, s, ev.start, ev.stop, 0, p);
   return hipGetLastError();
 }
 

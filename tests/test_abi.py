@@ -117,7 +117,7 @@ def test_cache_write_validation(b):
 
 def test_profile_state_machine(b):
     lib = b.lib()
-    ms = (ctypes.c_double * 3)()
-    n = (ctypes.c_int64 * 3)()
+    ms = (ctypes.c_double * 4)()
+    n = (ctypes.c_int64 * 4)()
     assert lib.sparse_mla_profile_end(ms, n) == -1      # not active
     assert lib.sparse_mla_profile_begin(0) == -1
