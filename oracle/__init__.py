@@ -14,8 +14,9 @@ Sources (cited by page title and section, never by line):
                  epilogue of ``build_sparse_mla_fp8ds_module`` (natural-log LSE,
                  empty rows).
   [K2-back page] vLLM API page "vllm.models.deepseek_v41.amd.mono.attention.back":
-                 module docstring (split / combine stages) and ``stage_combine``
-                 (merge of chunk partials by their max and sum).
+                 module docstring (split / combine stages), ``stage_combine``
+                 (merge of chunk partials by their max and sum, the sink folded
+                 in) and ``key_rec`` (paged two-pool key addressing).
   [OCP FP8]      OCP 8-bit floating point specification, E4M3 encoding
                  (the format the FlyDSL page's writer rule with its 448 bound
                  implies), with round-to-nearest-even conversion.
@@ -36,6 +37,12 @@ from .attention import (  # noqa: F401
     row_attention,
     sparse_mla_fwd,
     lse_merge,
+)
+from .paged import (  # noqa: F401
+    resolve,
+    gather_records,
+    row_attention_sink,
+    sparse_mla_fwd_paged,
 )
 from .writer import (  # noqa: F401
     pow2ceil,

@@ -538,3 +538,146 @@ def test_writer_planted_mistakes(monkeypatch, name):
         except Exception:  # noqa: BLE001 - any failure counts as caught
             failed += 1
     assert failed, f"planted writer mistake {name!r} went unnoticed"
+
+
+# ----------------------------------------------------------------- paged pools and sink pins
+
+import oracle.paged as opaged  # noqa: E402
+
+
+def paged_layout(rng, kv, per_page=(16, 8), pad=(3 * 656 + 16, 0)):
+    """Scatter the records of a contiguous kv over two paged pools (a random
+    pool and a random slot for every record; pages laid out page_stride apart
+    with garbage in the gaps).  Returns (pools, entry_of) with entry_of[i] the
+    key-table entry of record i."""
+    N = kv.shape[0]
+    pool_of = rng.integers(0, 2, N)
+    pools, entry_of = [], np.zeros(N, np.int64)
+    for p in range(2):
+        ids = np.flatnonzero(pool_of == p)
+        slots = rng.permutation(max(len(ids), 1))[: len(ids)]
+        blk = per_page[p]
+        stride = blk * 656 + pad[p]
+        npages = (int(slots.max()) // blk + 1) if len(ids) else 1
+        buf = rng.integers(0, 256, npages * stride, dtype=np.uint8)
+        for i, s in zip(ids, slots):
+            off = (s // blk) * stride + (s % blk) * 656
+            buf[off:off + 656] = kv[i]
+            entry_of[i] = s if p == 0 else np.int64(np.int32(np.uint32(s | (1 << 31))))
+        pools.append((buf, stride, blk))
+    return pools, entry_of
+
+
+def paged_case(seed):
+    rng = np.random.default_rng(seed)
+    N, T, H = 40, 5, 3
+    kv = random_records(rng, N, scale_exp=(-6, 0))
+    q = torch.from_numpy(rng.standard_normal((T, H, 576)).astype(np.float32)) \
+        .to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    lens = [7, 0, 12, 1, 20]
+    ip = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    ix = np.concatenate([rng.integers(0, N, L) for L in lens]).astype(np.int64)
+    ix[3] = -1
+    return rng, kv, q, ip, ix
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_paged_equals_contiguous(seed):
+    """The same keys through two paged pools give exactly the contiguous result."""
+    rng, kv, q, ip, ix = paged_case(seed)
+    pools, entry_of = paged_layout(rng, kv)
+    pix = np.where(ix >= 0, entry_of[np.maximum(ix, 0)], -1)
+    assert np.any(pix < -1) and np.any(pix >= 0)  # both pools in use
+    ro, rl = oracle.sparse_mla_fwd(q, kv, ip, ix, SIGMA)
+    po, pl = opaged.sparse_mla_fwd_paged(q, pools, ip, pix, SIGMA)
+    assert np.array_equal(ro, po) and np.array_equal(rl, pl)
+
+
+def test_paged_entry_decoding():
+    """-1 is no key; other negatives select the compressed pool by their low 31 bits."""
+    pools = [(np.zeros(10 * 656, np.uint8), 5 * 656, 5), (np.zeros(4 * 1000, np.uint8), 1000, 1)]
+    assert opaged.resolve(-1, pools) is None
+    assert opaged.resolve(7, pools) == (0, 1 * 5 * 656 + 2 * 656)
+    assert opaged.resolve(np.int32(np.uint32((1 << 31) | 3)), pools) == (1, 3 * 1000)
+    with pytest.raises(IndexError):
+        opaged.resolve(10, pools)
+
+
+def test_sink_none_equals_minus_inf():
+    rng, kv, q, ip, ix = paged_case(7)
+    pools, entry_of = paged_layout(rng, kv)
+    pix = np.where(ix >= 0, entry_of[np.maximum(ix, 0)], -1)
+    a = opaged.sparse_mla_fwd_paged(q, pools, ip, pix, SIGMA)
+    b = opaged.sparse_mla_fwd_paged(q, pools, ip, pix, SIGMA, sink=np.full(3, -np.inf))
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_sink_closed_form_equal_scores():
+    """q = 0: every logit is 0, so out = mean(V) n / (n + e^sink) and lse = ln(n + e^sink)."""
+    rng = np.random.default_rng(8)
+    K = oracle.decode_records(random_records(rng, 9, scale_exp=(-6, 0)))
+    sink = np.array([-3.0, 0.0, 2.5])
+    out, lse = opaged.row_attention_sink(np.zeros((3, 576)), K, SIGMA, sink)
+    n = K.shape[0]
+    want = K[:, :512].mean(axis=0)[None, :] * (n / (n + np.exp(sink)))[:, None]
+    assert np.allclose(out, want, rtol=0, atol=1e-13)
+    assert np.allclose(lse, np.log(n + np.exp(sink)), rtol=0, atol=1e-13)
+
+
+def test_sink_bruteforce_extra_key():
+    """Pure-Python softmax over the n logits plus the sink logit, the sink's value 0."""
+    rng = np.random.default_rng(9)
+    K = oracle.decode_records(random_records(rng, 6, scale_exp=(-4, 0)))
+    Q = rng.standard_normal((2, 576))
+    sink = np.array([0.7, -1.2])
+    out, lse = opaged.row_attention_sink(Q, K, SIGMA, sink)
+    for h in range(2):
+        logits = [SIGMA * float(np.dot(Q[h], K[j])) for j in range(6)] + [float(sink[h])]
+        mx = max(logits)
+        ws = [math.exp(x - mx) for x in logits]
+        tot = sum(ws)
+        for d in (0, 100, 511):
+            v = sum(ws[j] * K[j, d] for j in range(6)) / tot
+            assert abs(out[h, d] - v) <= 1e-12 * max(1.0, abs(v))
+        assert abs(lse[h] - (mx + math.log(tot))) <= 1e-12
+
+
+def test_sink_empty_row():
+    out, lse = opaged.row_attention_sink(np.zeros((2, 576)), np.zeros((0, 576)), SIGMA, np.array([1.5, -np.inf]))
+    assert np.all(out == 0.0) and lse[0] == 1.5 and lse[1] == -np.inf
+
+
+@pytest.mark.parametrize("name", ["sink_in_numerator", "sink_not_exponentiated", "pool_bit_ignored"])
+def test_paged_planted_mistakes(monkeypatch, name):
+    real_row, real_resolve = opaged.row_attention_sink, opaged.resolve
+    if name == "sink_in_numerator":
+        def f(Q, K, sigma, sink):
+            out, lse = real_row(Q, K, sigma, sink)
+            if sink is None or K.shape[0] == 0:
+                return out, lse
+            s = sigma * (Q @ K.T)
+            m = np.maximum(s.max(axis=1), sink)
+            w = np.exp(np.asarray(sink) - m) / np.exp(lse - m)
+            return out + w[:, None] * K[0, :512][None, :], lse
+        monkeypatch.setattr(opaged, "row_attention_sink", f)
+    elif name == "sink_not_exponentiated":
+        def f(Q, K, sigma, sink):
+            if sink is None or K.shape[0] == 0:
+                return real_row(Q, K, sigma, sink)
+            s = sigma * (Q @ K.T)
+            m = s.max(axis=1)
+            p = np.exp(s - m[:, None])
+            l = p.sum(axis=1) + np.asarray(sink)
+            return (p @ K[:, :512]) / l[:, None], m + np.log(np.abs(l))
+        monkeypatch.setattr(opaged, "row_attention_sink", f)
+    else:
+        monkeypatch.setattr(opaged, "resolve", lambda e, pools: None if int(e) == -1
+                            else real_resolve(int(e) & 0x7FFFFFFF, pools))
+    failed = 0
+    for fn in (lambda: [test_paged_equals_contiguous(s) for s in range(2)], test_sink_closed_form_equal_scores,
+               test_sink_bruteforce_extra_key):
+        try:
+            fn()
+        except Exception:  # noqa: BLE001 - any failure counts as caught
+            failed += 1
+    assert failed, f"planted mistake {name!r} went unnoticed"
