@@ -147,8 +147,10 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run plain device copies of known size (counter scaling)")
-    ap.add_argument("--op", choices=("fwd", "cache_write"), default="fwd",
-                    help="fwd: the sparse MLA forward (default); cache_write: the record writer")
+    ap.add_argument("--op", choices=("fwd", "fwd_paged", "cache_write"), default="fwd",
+                    help="fwd: the sparse MLA forward (default); fwd_paged: the same workload "
+                         "through two paged pools with a per-head sink; cache_write: the record writer")
+    ap.add_argument("--page-records", type=int, default=64, help="records per page (fwd_paged)")
     ap.add_argument("--records", type=int, default=65536, help="records written per call (cache_write)")
     args = ap.parse_args()
 
@@ -178,6 +180,16 @@ def main() -> int:
     def step():
         smla.fwd(w.q, w.kv, w.indptr, w.indices, w.sm_scale, has_invalid=bool(w.has_invalid),
                  out=out, lse=lse, ws=ws)
+
+    paged = None
+    if args.op == "fwd_paged":
+        pools, entries, sink = paged_inputs(torch, w, args.page_records, seed=args.config)
+        paged = {"page_records": args.page_records, "pool_bytes": [int(b.numel()) for b, _, _ in pools],
+                 "sink": "N(0, 3) per head"}
+
+        def step():  # noqa: F811 (the paged variant of the same step)
+            smla.fwd_paged(w.q, pools, w.indptr, entries, w.sm_scale, sink=sink,
+                           has_invalid=bool(w.has_invalid), out=out, lse=lse, ws=ws)
 
     for _ in range(args.warmup):
         step()
@@ -243,6 +255,7 @@ def main() -> int:
             "nnz": w.nnz, "valid_entries": valid, "has_invalid": w.has_invalid,
             "record_bytes": RECORD_BYTES, "split": _split_of(smla, w),
         },
+        "op": args.op,
         "rows_per_s": round(w.T / s, 1),
         "tflops": round(flop / s / 1e12, 2),
         "pct_hbm_peak": round(100.0 * gathered / s / 1e9 / HBM_PEAK_GBS, 2),
@@ -268,6 +281,11 @@ def main() -> int:
             "launch_ms": round(fwd_ms, 5),
         },
     }
+    if paged is not None:
+        result["metric"] = METRIC + ", paged two-pool keys + sink"
+        result["config"]["workload"] = cfg["name"] + f"_paged{args.page_records}_sink"
+        result["config"]["paged"] = paged
+        result["roofline"]["traffic"] = read_traffic(result["config"]["workload"])
     if args.config == 5:
         tf = flop / (fwd_ms * 1e-3) / 1e12
         result["roofline"].update({"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS,
@@ -278,6 +296,37 @@ def main() -> int:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_budget, 16)
     print(json.dumps(result), flush=True)
     return 0
+
+
+def paged_inputs(torch, w, per_page: int, seed: int):
+    """The workload's records scattered over two paged pools (key_rec
+    addressing: entries >= 0 window-pool slots, compressed-pool slots with bit
+    31 set), each record in a random pool at a random slot, pages of
+    per_page records with a 256-byte gap after each page; plus a per-head sink
+    drawn from N(0, 3).  Returns (pools, entries int32 [nnz], sink f32 [H])."""
+    dev = w.kv.device
+    g = torch.Generator(device=dev)
+    g.manual_seed(0xB00 + seed)
+    N = w.kv.shape[0]
+    pool_of = torch.randint(0, 2, (N,), generator=g, device=dev)
+    entry_of = torch.empty(N, dtype=torch.int64, device=dev)
+    pools = []
+    for p in range(2):
+        ids = torch.nonzero(pool_of == p).squeeze(1)
+        n = int(ids.numel())
+        stride = per_page * RECORD_BYTES + 256
+        npages = max((n + per_page - 1) // per_page, 1)
+        buf = torch.randint(0, 256, (npages * stride,), generator=g, device=dev, dtype=torch.uint8)
+        if n:
+            slots = torch.randperm(n, generator=g, device=dev)
+            recs = buf.as_strided((npages, per_page, RECORD_BYTES), (stride, RECORD_BYTES, 1))
+            recs[slots // per_page, slots % per_page] = w.kv[ids]
+            entry_of[ids] = slots if p == 0 else slots - (1 << 31)   # bit 31 set, as int32
+        pools.append((buf, stride, per_page))
+    ix = w.indices.to(torch.int64)
+    entries = torch.where(ix >= 0, entry_of[ix.clamp(min=0)], -1).to(torch.int32)
+    sink = (torch.randn(w.H, generator=g, device=dev) * 3.0).float()
+    return pools, entries, sink
 
 
 WRITE_READ_BYTES = 512 * 2 + 64 * 2 + 8   # bf16 latent + bf16 rope + int64 slot per token

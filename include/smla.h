@@ -133,6 +133,61 @@ int sparse_mla_fwd(const void* q, int64_t q_stride_t, int64_t q_stride_h,
                    void* stream);
 
 /*
+ * smla_kv_pool -- one paged pool of 656-byte records (K2-back page of the
+ * DeepSeek V4.1 AMD attention module, "key_rec": a key-table entry names a
+ * slot of the window pool or of the compressed pool; a pool is a run of
+ * pages).  Slot s of a pool is the record at
+ *   base + (s / page_records) * page_stride + (s % page_records) * 656.
+ *   base          device, page 0, 16-byte aligned; NULL: the pool is absent and
+ *                 entries naming it are not keys.
+ *   page_stride   bytes from one page to the next: a multiple of 16 and at
+ *                 least page_records * 656 (a page may carry trailing bytes
+ *                 that are never read).
+ *   page_records  records per page, a power of two in [1, 2^30].
+ */
+typedef struct smla_kv_pool {
+  const void* base;
+  int64_t page_stride;
+  int64_t page_records;
+} smla_kv_pool;
+
+/*
+ * sparse_mla_fwd_paged -- sparse_mla_fwd over two paged pools, with an
+ * optional per-head attention sink (K2-back page: "key_rec" for the entries,
+ * "stage_combine" for the sink).
+ *
+ *   pools      host, smla_kv_pool[2]: pools[0] the window pool, pools[1] the
+ *              compressed pool.  Read during the call only.
+ *   indices    device, int32 [nnz]: -1 is no key; an entry e >= 0 is slot e
+ *              of pools[0]; any other negative entry is slot (e & 0x7fffffff)
+ *              of pools[1] (the slot with bit 31 set).  Entries naming an
+ *              absent pool are no key.
+ *   has_invalid  nonzero: slices may hold entries that are no key (-1, or of
+ *              an absent pool); as in sparse_mla_fwd, trailing ones are skipped
+ *              and the result is the same either way.
+ *   sink       device, f32 [H] natural-log logits, or NULL for none.  Head h
+ *              gains one more key of logit sink[h] (not scaled by sm_scale)
+ *              and value 0: it joins the softmax maximum and sum but adds
+ *              nothing to out.  A row with no key gets out = 0 and lse = sink[h]
+ *              (-inf without a sink).  Finite or -inf values.
+ * Every other argument, the workspace and the behaviour are those of
+ * sparse_mla_fwd (with lse including the sink's term).  Preconditions the
+ * library cannot check: every consumed slot lies inside its pool's
+ * allocation, and the records meet sparse_mla_fwd's scale preconditions.
+ * Returns SMLA_OK, or SMLA_EINVAL (also for a malformed pool descriptor) /
+ * SMLA_EUNSUPPORTED / SMLA_EWORKSPACE / SMLA_EHIP with nothing queued.
+ */
+int sparse_mla_fwd_paged(const void* q, int64_t q_stride_t, int64_t q_stride_h,
+                         const smla_kv_pool* pools,
+                         const int32_t* indptr, const int32_t* indices, int64_t nnz,
+                         int32_t T, int32_t H, float sm_scale, int32_t has_invalid,
+                         const float* sink,
+                         void* out, int64_t o_stride_t, int64_t o_stride_h,
+                         float* lse,
+                         void* workspace, int64_t workspace_bytes,
+                         void* stream);
+
+/*
  * sparse_mla_decode_rows -- test hook: decode records rows[0..n) of kv to f32
  * out[n, 576] (latent * scale, then rope) exactly as the forward's QK stage
  * sees them (scale applied through its exponent field), cross-checked on the

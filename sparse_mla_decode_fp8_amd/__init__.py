@@ -8,7 +8,8 @@ there is no fallback path.
 """
 
 _PUBLIC = (
-    "MAX_HEADS", "MAX_SPLIT", "KernelTimer", "SmlaError", "cache_write", "decode_rows", "fwd",
+    "MAX_HEADS", "MAX_SPLIT", "KernelTimer", "KvPool", "SmlaError", "cache_write", "decode_rows", "fwd",
+    "fwd_paged",
     "set_option", "split_for", "supported", "workspace", "workspace_bytes", "LIB_PATH", "EXPORTED",
 )
 

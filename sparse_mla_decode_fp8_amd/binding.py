@@ -50,6 +50,25 @@ _lib.sparse_mla_fwd.argtypes = [
     _vp,                    # stream
 ]
 _lib.sparse_mla_fwd.restype = ctypes.c_int
+
+
+class KvPool(ctypes.Structure):
+    """smla_kv_pool: one paged pool of 656-byte records."""
+    _fields_ = [("base", _vp), ("page_stride", _i64), ("page_records", _i64)]
+
+
+_lib.sparse_mla_fwd_paged.argtypes = [
+    _vp, _i64, _i64,        # q, strides
+    ctypes.POINTER(KvPool),  # pools[2] (host)
+    _vp, _vp, _i64,         # indptr, indices, nnz
+    _i32, _i32, _f32, _i32,  # T, H, sm_scale, has_invalid
+    _vp,                    # sink
+    _vp, _i64, _i64,        # out, strides
+    _vp,                    # lse
+    _vp, _i64,              # workspace, bytes
+    _vp,                    # stream
+]
+_lib.sparse_mla_fwd_paged.restype = ctypes.c_int
 _lib.sparse_mla_cache_write.argtypes = [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp]
 _lib.sparse_mla_cache_write.restype = ctypes.c_int
 _lib.sparse_mla_decode_rows.argtypes = [_vp, _i64, _vp, _i64, _vp, _vp]
@@ -65,7 +84,7 @@ _lib.sparse_mla_profile_end.restype = ctypes.c_int
 
 EXPORTED = (
     "sparse_mla_supported", "sparse_mla_workspace_bytes", "sparse_mla_split_for", "sparse_mla_fwd",
-    "sparse_mla_cache_write", "sparse_mla_decode_rows", "sparse_mla_last_error", "sparse_mla_set_option",
+    "sparse_mla_fwd_paged", "sparse_mla_cache_write", "sparse_mla_decode_rows", "sparse_mla_last_error", "sparse_mla_set_option",
     "sparse_mla_profile_begin", "sparse_mla_profile_end",
 )
 
@@ -171,6 +190,75 @@ def fwd(q: torch.Tensor, kv: torch.Tensor, indptr: torch.Tensor, indices: torch.
         _ptr(kv), kv.shape[0],
         _ptr(indptr), _ptr(indices) if nnz else None, nnz,
         T, H, float(sm_scale), 1 if has_invalid else 0,
+        _ptr(out), out.stride(0), out.stride(1),
+        _ptr(lse),
+        _ptr(ws), ws.numel(),
+        _stream(dev))
+    _check(rc)
+    return out, lse
+
+
+def _check_fwd_args(q, indptr, indices):
+    if q.dtype != torch.bfloat16 or q.dim() != 3 or q.shape[2] != 576:
+        raise ValueError("q must be bf16 [T, H, 576]")
+    if indptr.dtype != torch.int32 or indices.dtype != torch.int32:
+        raise ValueError("indptr and indices must be int32")
+    if q.stride(2) != 1:
+        raise ValueError("q's last dimension must be contiguous")
+    for t in (indptr, indices):
+        if t.device != q.device:
+            raise ValueError("all tensors must be on q's device")
+    if indptr.numel() != q.shape[0] + 1:
+        raise ValueError("indptr must have T + 1 entries")
+
+
+def fwd_paged(q: torch.Tensor, pools, indptr: torch.Tensor, indices: torch.Tensor,
+              sm_scale: float, sink: Optional[torch.Tensor] = None, has_invalid: bool = False,
+              return_lse: bool = True, out: Optional[torch.Tensor] = None,
+              lse: Optional[torch.Tensor] = None,
+              ws: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Sparse MLA forward over two paged pools with an optional sink.
+
+    pools: two (bytes, page_stride, page_records) triples, the window pool and
+    the compressed pool; bytes is a contiguous uint8 device tensor holding the
+    pool from page 0, or None for an absent pool.  Entries of indices: -1 no
+    key, >= 0 a window-pool slot, other negative values a compressed-pool slot
+    with bit 31 set.  sink: f32 [H] natural-log logits or None."""
+    _check_fwd_args(q, indptr, indices)
+    if len(pools) != 2:
+        raise ValueError("pools must hold two (bytes, page_stride, page_records) triples")
+    dev = q.device
+    desc = (KvPool * 2)()
+    for i, pl in enumerate(pools):
+        buf, stride, per_page = pl
+        if buf is None:
+            desc[i] = KvPool(None, 0, 0)
+            continue
+        if buf.dtype != torch.uint8 or buf.dim() != 1 or not buf.is_contiguous() or buf.device != dev:
+            raise ValueError("a pool's bytes must be a contiguous 1-D uint8 tensor on q's device")
+        desc[i] = KvPool(buf.data_ptr(), int(stride), int(per_page))
+    if sink is not None:
+        if sink.dtype != torch.float32 or sink.numel() != q.shape[1] or sink.device != dev:
+            raise ValueError("sink must be f32 [H] on q's device")
+        sink = sink.contiguous()
+    T, H, _ = q.shape
+    indptr = indptr.contiguous()
+    indices = indices.contiguous()
+    nnz = indices.numel()
+    if out is None:
+        out = torch.empty(T, H, 512, dtype=torch.bfloat16, device=dev)
+    if return_lse and lse is None:
+        lse = torch.empty(T, H, dtype=torch.float32, device=dev)
+    if not return_lse:
+        lse = None
+    if ws is None:
+        ws = workspace(dev, workspace_bytes(T, H, nnz))
+    rc = _lib.sparse_mla_fwd_paged(
+        _ptr(q), q.stride(0), q.stride(1),
+        desc,
+        _ptr(indptr), _ptr(indices) if nnz else None, nnz,
+        T, H, float(sm_scale), 1 if has_invalid else 0,
+        _ptr(sink),
         _ptr(out), out.stride(0), out.stride(1),
         _ptr(lse),
         _ptr(ws), ws.numel(),

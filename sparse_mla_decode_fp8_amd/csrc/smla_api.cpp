@@ -162,25 +162,35 @@ int32_t sparse_mla_split_for(int32_t T, int32_t H, int64_t nnz) {
   return choose_split(T, H, nnz);
 }
 
-int sparse_mla_fwd(const void* q, int64_t q_stride_t, int64_t q_stride_h,
-                   const void* kv, int64_t n_kv,
-                   const int32_t* indptr, const int32_t* indices, int64_t nnz,
-                   int32_t T, int32_t H, float sm_scale, int32_t has_invalid,
-                   void* out, int64_t o_stride_t, int64_t o_stride_h,
-                   float* lse,
-                   void* workspace, int64_t workspace_bytes,
-                   void* stream) {
-  g_err.clear();
+}  // extern "C"
+
+namespace {
+
+// Where the keys live: one contiguous cache, or two paged pools.
+struct KeySource {
+  smla::KeyMode km;
+  const uint8_t* kv;
+  const uint8_t* pool[2];
+  int64_t pool_stride[2];
+  int32_t pool_shift[2];
+};
+
+// The forward shared by both entry points (keys already validated).
+int fwd_impl(const void* q, int64_t q_stride_t, int64_t q_stride_h, const KeySource& ks,
+             const int32_t* indptr, const int32_t* indices, int64_t nnz,
+             int32_t T, int32_t H, float sm_scale, int32_t has_invalid, const float* sink,
+             void* out, int64_t o_stride_t, int64_t o_stride_h, float* lse,
+             void* workspace, int64_t workspace_bytes, void* stream) {
   if (!sparse_mla_supported(H)) return fail(SMLA_EUNSUPPORTED, "num_heads must be in [1, %d], got %d", SMLA_MAX_HEADS, H);
   if (T < 0) return fail(SMLA_EINVAL, "T must be >= 0, got %d", T);
   if (nnz < 0) return fail(SMLA_EINVAL, "nnz must be >= 0, got %lld", (long long)nnz);
   if (nnz > kMaxNnz) return fail(SMLA_EINVAL, "nnz must be <= %lld (32-bit bounded index reads), got %lld", (long long)kMaxNnz, (long long)nnz);
-  if (n_kv < 0 || n_kv > INT64_MAX / smla::kRecordBytes) return fail(SMLA_EINVAL, "n_kv out of range: %lld", (long long)n_kv);
   if (!isfinite(sm_scale)) return fail(SMLA_EINVAL, "sm_scale must be finite");
   if (T == 0) return SMLA_OK;
-  if (!q || !kv || !indptr || !out || !workspace) return fail(SMLA_EINVAL, "null pointer (q, kv, indptr, out and workspace are required)");
+  if (!q || !indptr || !out || !workspace) return fail(SMLA_EINVAL, "null pointer (q, indptr, out and workspace are required)");
   if (nnz > 0 && !indices) return fail(SMLA_EINVAL, "indices is null but nnz > 0");
-  if (!aligned(q, 16) || !aligned(out, 16) || !aligned(kv, 16)) return fail(SMLA_EINVAL, "q, out and kv must be 16-byte aligned");
+  if (!aligned(q, 16) || !aligned(out, 16)) return fail(SMLA_EINVAL, "q and out must be 16-byte aligned");
+  if (sink && !aligned(sink, 4)) return fail(SMLA_EINVAL, "sink must be 4-byte aligned");
   if (!aligned(workspace, 256)) return fail(SMLA_EINVAL, "workspace must be 256-byte aligned");
   if (q_stride_t < 0 || q_stride_h < 0 || o_stride_t < 0 || o_stride_h < 0 ||
       (q_stride_t | q_stride_h | o_stride_t | o_stride_h) % 8 != 0)
@@ -207,7 +217,7 @@ int sparse_mla_fwd(const void* q, int64_t q_stride_t, int64_t q_stride_h,
   hipError_t e = hipSuccess;
   if (sort) {
     smla::PlanParams pp{indptr, indices, idx_bytes, T, smla::tile_tokens(H), has_invalid ? 1 : 0,
-                        row_tiles, order};
+                        ks.km, row_tiles, order};
     e = timed(0, [&](smla::Events ev) { return smla::launch_plan(pp, sort, ev, s); });
     if (e != hipSuccess) return hip_fail(e, "plan kernel launch");
   }
@@ -216,7 +226,7 @@ int sparse_mla_fwd(const void* q, int64_t q_stride_t, int64_t q_stride_h,
   fp.q = (const uint16_t*)q;
   fp.q_st = q_stride_t;
   fp.q_sh = q_stride_h;
-  fp.kv = (const uint8_t*)kv;
+  fp.kv = ks.kv;
   fp.zero = zero;
   fp.indptr = indptr;
   fp.indices = indices;
@@ -237,15 +247,84 @@ int sparse_mla_fwd(const void* q, int64_t q_stride_t, int64_t q_stride_h,
   fp.order = sort ? order : nullptr;
   fp.part_o = (uint16_t*)(ws + L.part_o);
   fp.part_lse = (float*)(ws + L.part_lse);
+  fp.km = ks.km;
+  for (int i = 0; i < 2; ++i) {
+    fp.pool[i] = ks.pool[i];
+    fp.pool_stride[i] = ks.pool_stride[i];
+    fp.pool_shift[i] = ks.pool_shift[i];
+  }
+  fp.sink = sink;
   e = timed(1, [&](smla::Events ev) { return smla::launch_fwd(fp, ev, s); });
   if (e != hipSuccess) return hip_fail(e, "forward kernel launch");
 
   if (L.S > 1) {
-    smla::CombineParams cp{T, H, L.S, fp.order, fp.part_o, fp.part_lse, fp.out, o_stride_t, o_stride_h, lse};
+    smla::CombineParams cp{T, H, L.S, sink, fp.order, fp.part_o, fp.part_lse, fp.out, o_stride_t, o_stride_h, lse};
     e = timed(2, [&](smla::Events ev) { return smla::launch_combine(cp, ev, s); });
     if (e != hipSuccess) return hip_fail(e, "combine kernel launch");
   }
   return SMLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sparse_mla_fwd(const void* q, int64_t q_stride_t, int64_t q_stride_h,
+                   const void* kv, int64_t n_kv,
+                   const int32_t* indptr, const int32_t* indices, int64_t nnz,
+                   int32_t T, int32_t H, float sm_scale, int32_t has_invalid,
+                   void* out, int64_t o_stride_t, int64_t o_stride_h,
+                   float* lse,
+                   void* workspace, int64_t workspace_bytes,
+                   void* stream) {
+  g_err.clear();
+  if (n_kv < 0 || n_kv > INT64_MAX / smla::kRecordBytes) return fail(SMLA_EINVAL, "n_kv out of range: %lld", (long long)n_kv);
+  if (T > 0 && !kv) return fail(SMLA_EINVAL, "null pointer (kv is required)");
+  if (!aligned(kv, 16)) return fail(SMLA_EINVAL, "kv must be 16-byte aligned");
+  KeySource ks{};
+  ks.km = smla::KeyMode{0, {1, 1}};
+  ks.kv = (const uint8_t*)kv;
+  return fwd_impl(q, q_stride_t, q_stride_h, ks, indptr, indices, nnz, T, H, sm_scale, has_invalid, nullptr,
+                  out, o_stride_t, o_stride_h, lse, workspace, workspace_bytes, stream);
+}
+
+int sparse_mla_fwd_paged(const void* q, int64_t q_stride_t, int64_t q_stride_h,
+                         const smla_kv_pool* pools,
+                         const int32_t* indptr, const int32_t* indices, int64_t nnz,
+                         int32_t T, int32_t H, float sm_scale, int32_t has_invalid,
+                         const float* sink,
+                         void* out, int64_t o_stride_t, int64_t o_stride_h,
+                         float* lse,
+                         void* workspace, int64_t workspace_bytes,
+                         void* stream) {
+  g_err.clear();
+  if (!pools) return fail(SMLA_EINVAL, "pools is null (two pool descriptors are required)");
+  KeySource ks{};
+  ks.km.paged = 1;
+  for (int i = 0; i < 2; ++i) {
+    const smla_kv_pool& pl = pools[i];
+    if (!pl.base) {  // absent: its entries are not keys
+      ks.km.present[i] = 0;
+      continue;
+    }
+    const int64_t pr = pl.page_records;
+    if (pr < 1 || pr > (int64_t(1) << 30) || (pr & (pr - 1)) != 0)
+      return fail(SMLA_EINVAL, "pool %d: page_records must be a power of two in [1, 2^30], got %lld", i, (long long)pr);
+    if (!aligned(pl.base, 16)) return fail(SMLA_EINVAL, "pool %d: base must be 16-byte aligned", i);
+    if (pl.page_stride % 16 != 0 || pl.page_stride < pr * smla::kRecordBytes)
+      return fail(SMLA_EINVAL, "pool %d: page_stride must be a multiple of 16 and >= page_records * %d bytes, got %lld",
+                  i, smla::kRecordBytes, (long long)pl.page_stride);
+    if (pl.page_stride > INT64_MAX / (int64_t(1) << 31))
+      return fail(SMLA_EINVAL, "pool %d: page_stride too large: %lld", i, (long long)pl.page_stride);
+    ks.km.present[i] = 1;
+    ks.pool[i] = (const uint8_t*)pl.base;
+    ks.pool_stride[i] = pl.page_stride;
+    int sh = 0;
+    while ((int64_t(1) << sh) < pr) ++sh;
+    ks.pool_shift[i] = sh;
+  }
+  return fwd_impl(q, q_stride_t, q_stride_h, ks, indptr, indices, nnz, T, H, sm_scale, has_invalid, sink,
+                  out, o_stride_t, o_stride_h, lse, workspace, workspace_bytes, stream);
 }
 
 int sparse_mla_decode_rows(const void* kv, int64_t n_kv, const int32_t* rows, int64_t n,

@@ -11,6 +11,18 @@ constexpr int kRecordBytes = 656;  // 512 e4m3 | 4 x f32 scale | 64 x bf16 rope
 constexpr int kTokensPerWave = 32;  // tokens one wave owns in a tile
 constexpr int kPlanBuckets = 256;   // longest-first counting-sort buckets (tiles, capped)
 
+// Which index entries are keys.  Contiguous cache: entries >= 0.  Paged pools
+// (K2-back page, key_rec): -1 is no key, an entry >= 0 a slot of pool 0 (the
+// window pool), any other negative entry a slot of pool 1 (the compressed
+// pool, slot = entry & 0x7fffffff); an entry of a pool that is absent is no key.
+struct KeyMode {
+  int32_t paged;
+  int32_t present[2];
+  __host__ __device__ bool valid(int32_t e) const {
+    return paged ? (e != -1 && (e < 0 ? present[1] : present[0]) != 0) : e >= 0;
+  }
+};
+
 struct PlanParams {
   const int32_t* indptr;
   const int32_t* indices;
@@ -18,6 +30,7 @@ struct PlanParams {
   int32_t T;
   int32_t tile;        // tokens per tile
   int32_t has_invalid;
+  KeyMode km;
   int32_t* row_tiles;  // [T] out: tiles of each row
   int32_t* order;      // [T] out: rows, longest first
 };
@@ -41,10 +54,16 @@ struct FwdParams {
   const int32_t* order;      // nullable: rows in their own order
   uint16_t* part_o;    // f16 bits [T*S, H, 512] when S > 1
   float* part_lse;     // [T*S, H]  (log2 units) when S > 1
+  KeyMode km;
+  const uint8_t* pool[2];     // paged: page 0 of each pool
+  int64_t pool_stride[2];     // paged: bytes from one page to the next
+  int32_t pool_shift[2];      // paged: log2 of the records per page
+  const float* sink;          // nullable: per-head sink logit [H] (natural log); unsplit rows only
 };
 
 struct CombineParams {
   int32_t T, H, S;
+  const float* sink;     // nullable: per-head sink logit [H] (natural log)
   const int32_t* order;  // nullable: rows in their own order
   const uint16_t* part_o;  // f16 bits
   const float* part_lse;

@@ -164,6 +164,19 @@ __device__ __forceinline__ void xcd_unit(int per_row, int& rank, int& sub) {
   sub = i % per_row;
 }
 
+// Record address of an index entry that is a key (KeyMode::valid).
+__device__ __forceinline__ const uint8_t* key_addr(const FwdParams& p, int e) {
+  if (!p.km.paged) return p.kv + (int64_t)e * kRecordBytes;
+  // selects, not a dynamic index into the kernel argument (that would copy
+  // the whole argument to scratch memory)
+  const bool c = e < 0;
+  const uint32_t slot = (uint32_t)e & 0x7FFFFFFFu;
+  const uint32_t sh = (uint32_t)(c ? p.pool_shift[1] : p.pool_shift[0]);
+  const uint8_t* const base = c ? p.pool[1] : p.pool[0];
+  const int64_t stride = c ? p.pool_stride[1] : p.pool_stride[0];
+  return base + (int64_t)(slot >> sh) * stride + (int64_t)(slot & ((1u << sh) - 1u)) * kRecordBytes;
+}
+
 // ---------------------------------------------------------------- plan
 
 // Tiles of a row from its effective length.
@@ -188,7 +201,7 @@ __device__ __forceinline__ int unit_tiles(const FwdParams& p, int row, int beg, 
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int pos = base + NT * j + tid;
-      if (pos < len && v[j] >= 0) lastp = max(lastp, pos + 1);
+      if (pos < len && p.km.valid(v[j])) lastp = max(lastp, pos + 1);
     }
   }
 #pragma unroll
@@ -218,7 +231,7 @@ __global__ __launch_bounds__(256) void smla_plan_scan_kernel(PlanParams p) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int pos = base + 4 * lane + j;
-      if (pos < len && v[j] >= 0) lastp = pos + 1;
+      if (pos < len && p.km.valid(v[j])) lastp = pos + 1;
     }
   }
 #pragma unroll
@@ -288,6 +301,26 @@ constexpr int kIdxAhead = 5;        // tile n issues the index load of tile n + 
 constexpr float kShift = 4.0f;      // P = exp2(x - m_ref + 4)
 constexpr float kTau = 4.0f;        // m_ref moves only when a head's max exceeds it by > 4
 
+// A head's final normalisation.  l is its softmax sum of P = 2^(x - m + kShift)
+// (m in log2 units), sink2 its sink logit in log2 units (-inf: none; the sink
+// is one more key whose value is 0, K2-back page, stage_combine).  Returns the
+// factor that turns the accumulated O into the output, and the lse in log2
+// units.  Without a sink this is 1 / l and m - kShift + log2 l.
+struct Norm {
+  float scale, lse2;
+};
+__device__ __forceinline__ Norm finish_norm(float l, float m, float sink2) {
+  const float mo = l > 0.0f ? m - kShift : -INFINITY;
+  const float mm = fmax_(mo, sink2);
+  if (mm == -INFINITY) return Norm{0.0f, -INFINITY};
+  const float a = l > 0.0f ? __builtin_amdgcn_exp2f(mo - mm) : 0.0f;
+  const float L = l * a + __builtin_amdgcn_exp2f(sink2 - mm);
+  return Norm{a / L, mm + __builtin_log2f(L)};
+}
+__device__ __forceinline__ float sink_log2(const float* sink, int h) {
+  return sink ? sink[h] * 1.4426950408889634f : -INFINITY;
+}
+
 template <int HT, int TG>
 struct FwdCfg {
   static constexpr int kWaves = HT * TG;
@@ -345,7 +378,7 @@ __global__ __launch_bounds__(64 * HT * TG, 1) void smla_fwd_kernel(FwdParams p) 
   const int h = 16 * ht + t;
   const bool h_ok = h < p.H;
 
-  if (t0 >= t1) {  // nothing to attend: zero output / -inf lse, or an empty partial
+  if (t0 >= t1) {  // nothing to attend: zero output and the sink's lse, or an empty partial
     if (split) {
       for (int hh = tid; hh < p.H; hh += C::kThreads) p.part_lse[(int64_t)unit * p.H + hh] = -INFINITY;
     } else {
@@ -353,8 +386,9 @@ __global__ __launch_bounds__(64 * HT * TG, 1) void smla_fwd_kernel(FwdParams p) 
         const int hh = e / (kLat / 8), d = (e % (kLat / 8)) * 8;
         *(v4i*)(p.out + row * p.o_st + hh * p.o_sh + d) = v4i{0, 0, 0, 0};
       }
-      if (p.lse)
-        for (int hh = tid; hh < p.H; hh += C::kThreads) p.lse[(int64_t)row * p.H + hh] = -INFINITY;
+      if (p.lse)  // a row with no key: lse is the sink (-inf without one)
+        for (int hh = tid; hh < p.H; hh += C::kThreads)
+          p.lse[(int64_t)row * p.H + hh] = p.sink ? p.sink[hh] : -INFINITY;
     }
     return;
   }
@@ -382,7 +416,7 @@ __global__ __launch_bounds__(64 * HT * TG, 1) void smla_fwd_kernel(FwdParams p) 
     const int raw = *LDSP(int, ring_at(n) + 4 * tau);
     return (n * C::kTile + kTokensPerWave * tg + tau < len) ? raw : -1;
   };
-  auto rec_of = [&](int ix) -> const uint8_t* { return ix >= 0 ? kv + (int64_t)ix * kRecordBytes : zero; };
+  auto rec_of = [&](int ix) -> const uint8_t* { return p.km.valid(ix) ? key_addr(p, ix) : zero; };
   // C: index DMA of tile n (bounded buffer reads, 32 entries) into its ring slot.
   auto issue_idx = [&](int n) {
     const uint32_t base = __builtin_amdgcn_readfirstlane(ring_at(n));
@@ -484,7 +518,7 @@ __global__ __launch_bounds__(64 * HT * TG, 1) void smla_fwd_kernel(FwdParams p) 
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(C::kTrailingVm));
     if (HT > 1) __syncthreads();
     const int ix_n = ring_ix(n, lane & 31);
-    const uint32_t vmask = (uint32_t)__ballot(ix_n >= 0);  // bit tau: token tau is a key
+    const uint32_t vmask = (uint32_t)__ballot(p.km.valid(ix_n));  // bit tau: token tau is a key
     const bool more = n + 1 < t1;
     if (more) issue_latent(n + 1, st ^ 1);
     fill_table(n + 2);
@@ -615,8 +649,10 @@ __global__ __launch_bounds__(64 * HT * TG, 1) void smla_fwd_kernel(FwdParams p) 
   // ---- epilogue
   l_run = xor_sum(l_run);  // lane (t, *) now holds head t's sum over this wave's tokens
   if constexpr (TG == 1) {
-    const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;
-    const float l2 = l_run > 0.0f ? m_ref + __builtin_log2f(l_run) - kShift : -INFINITY;
+    // split: a partial without the sink (the combine folds it in)
+    const Norm nm = finish_norm(l_run, m_ref, (split || !h_ok) ? -INFINITY : sink_log2(p.sink, h));
+    const float inv = nm.scale;
+    const float l2 = nm.lse2;
     if (h_ok) {
       if (split) {
         uint16_t* po = p.part_o + ((int64_t)unit * p.H + h) * kLat;
@@ -656,9 +692,9 @@ __global__ __launch_bounds__(64 * HT * TG, 1) void smla_fwd_kernel(FwdParams p) 
       if (mk != -INFINITY) L += s_l[k * HT + ht][t] * __builtin_amdgcn_exp2f(mk - M);
     }
     const float w_own = (m_ref == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_ref - M);
-    const float inv_h = L > 0.0f ? 1.0f / L : 0.0f;
-    const float l2_h = L > 0.0f ? M + __builtin_log2f(L) - kShift : -INFINITY;
-    const float wsc = w_own * inv_h;
+    const Norm nm = finish_norm(L, M, (split || !h_ok) ? -INFINITY : sink_log2(p.sink, h));
+    const float l2_h = nm.lse2;
+    const float wsc = w_own * nm.scale;
     constexpr int kOwn = 32 / TG;
     v4f* const mrg = (v4f*)s_big;  // [HT][TG][32 slices][64 lanes]
     auto slot = [&](int src, int dt) -> v4f* { return mrg + (((ht * TG + src) * 32 + dt) * 64 + lane); };
@@ -833,7 +869,7 @@ __global__ __launch_bounds__(n16::kThreads, 1) void smla_fwd16_kernel(
   const int h = t;  // head of this lane in QK (C column) and PV (B column)
   const bool h_ok = h < H;
 
-  if (t0 >= t1) {  // nothing to attend: zero output / -inf lse, or an empty partial
+  if (t0 >= t1) {  // nothing to attend: zero output and the sink's lse, or an empty partial
     if (stride > 0) wait_vm_all();  // the speculative index DMA must land before the block ends
     if (split) {
       for (int hh = tid; hh < H; hh += kThreads) p.part_lse[(int64_t)unit * H + hh] = -INFINITY;
@@ -842,8 +878,9 @@ __global__ __launch_bounds__(n16::kThreads, 1) void smla_fwd16_kernel(
         const int hh = e / (kLat / 8), d = (e % (kLat / 8)) * 8;
         *(v4i*)(p.out + row * p.o_st + hh * p.o_sh + d) = v4i{0, 0, 0, 0};
       }
-      if (p.lse)
-        for (int hh = tid; hh < H; hh += kThreads) p.lse[(int64_t)row * H + hh] = -INFINITY;
+      if (p.lse)  // a row with no key: lse is the sink (-inf without one)
+        for (int hh = tid; hh < H; hh += kThreads)
+          p.lse[(int64_t)row * H + hh] = p.sink ? p.sink[hh] : -INFINITY;
     }
     return;
   }
@@ -863,9 +900,9 @@ __global__ __launch_bounds__(n16::kThreads, 1) void smla_fwd16_kernel(
       const int raw = *LDSP(int, ring_at(n) + 4 * (16 * w + lane));
       ix = (n * kTile + 16 * w + lane < len) ? raw : -1;
       *LDSP(uint64_t, tab_at(n) + 8 * (16 * w + lane)) =
-          (uint64_t)(uintptr_t)(ix >= 0 ? kv + (int64_t)ix * kRecordBytes : zero);
+          (uint64_t)(uintptr_t)(p.km.valid(ix) ? key_addr(p, ix) : zero);
     }
-    return (uint32_t)__ballot(ix >= 0) & 0xFFFFu;
+    return (uint32_t)__ballot(lane < 16 && p.km.valid(ix)) & 0xFFFFu;
   };
   // latent DMA of this wave's 16 tokens of tile n into stage st: one
   // instruction per token pair, lanes 0..31 the even token, 32..63 the odd one
@@ -1127,9 +1164,11 @@ __global__ __launch_bounds__(n16::kThreads, 1) void smla_fwd16_kernel(
   wait_vm_all();  // no DMA may still target LDS when the block ends
 
   // ---- epilogue: head t's sum over all tokens, then this wave's 64 dims
+  // (split: a partial without the sink, which the combine folds in)
   l_run = xor_sum(l_run);
-  const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;
-  const float l2 = l_run > 0.0f ? m_ref + __builtin_log2f(l_run) - kShift : -INFINITY;
+  const Norm nm = finish_norm(l_run, m_ref, (split || !h_ok) ? -INFINITY : sink_log2(p.sink, h));
+  const float inv = nm.scale;
+  const float l2 = nm.lse2;
   if (w == 0 && g == 0 && h_ok) {
     if (split) p.part_lse[(int64_t)unit * H + h] = l2;
     else if (p.lse) p.lse[(int64_t)row * H + h] = l2 * kLn2;
@@ -1152,8 +1191,10 @@ __global__ __launch_bounds__(n16::kThreads, 1) void smla_fwd16_kernel(
 
 // ---------------------------------------------------------------- combine
 
-// LSE merge of a split row's chunks (K2-back page, stage_combine, without the
-// sink): M = max_c lse2_c, w_c = 2^(lse2_c - M), out = sum w_c o_c / sum w_c.
+// LSE merge of a split row's chunks (K2-back page, stage_combine):
+// M = max(max_c lse2_c, sink2), w_c = 2^(lse2_c - M),
+// out = sum w_c o_c / (sum w_c + 2^(sink2 - M)); the sink (-inf when absent)
+// is one more key whose value is 0.
 // All chunk loads are issued before any is used: they are unconditional
 // (chunk slots past S re-read chunk 0 and are ignored), and the f16 partials
 // are converted only after the last load.
@@ -1168,13 +1209,15 @@ __device__ __forceinline__ void combine_row(const CombineParams& p, int row, int
     lc[c] = p.part_lse[u * p.H + h];
     raw[c] = *(const v2i*)(p.part_o + (u * p.H + h) * kLat + 4 * threadIdx.x);
   }
-  float M = -INFINITY;
+  const float sink2 = p.sink ? p.sink[h] * 1.4426950408889634f : -INFINITY;
+  float M = sink2;
 #pragma unroll
   for (int c = 0; c < SMAX; ++c)
     if (c < p.S) M = fmax_(M, lc[c]);
   v4f acc = v4f{0, 0, 0, 0};
   float L = 0.0f;
   if (M != -INFINITY) {
+    L = __builtin_amdgcn_exp2f(sink2 - M);
 #pragma unroll
     for (int c = 0; c < SMAX; ++c) {
       if (c < p.S && lc[c] != -INFINITY) {  // an empty chunk's o_c was never written

@@ -115,6 +115,47 @@ def test_cache_write_validation(b):
     assert cw(n=0, latent=None, rope=None, slots=None, kv=None) == 0
 
 
+def test_fwd_paged_validation(b):
+    """Pool descriptors are checked on the host: page_records a power of two in
+    [1, 2^30], base 16-byte aligned, page_stride a multiple of 16 and at least
+    page_records * 656; a NULL base is an absent pool (accepted)."""
+    lib = b.lib()
+
+    def paged(pools, **over):
+        a = dict(q=FAKE, qst=576 * 16, qsh=576, indptr=FAKE, indices=FAKE, nnz=4, T=1, H=16,
+                 scale=0.04, inv=0, sink=None, out=FAKE, ost=512 * 16, osh=512, lse=None,
+                 ws=FAKE, wsb=1 << 40)
+        a.update(over)
+        desc = None
+        if pools is not None:
+            desc = (b.KvPool * 2)(*[b.KvPool(*pl) for pl in pools])
+        return lib.sparse_mla_fwd_paged(a["q"], a["qst"], a["qsh"], desc, a["indptr"], a["indices"],
+                                        a["nnz"], a["T"], a["H"], a["scale"], a["inv"], a["sink"],
+                                        a["out"], a["ost"], a["osh"], a["lse"], a["ws"], a["wsb"],
+                                        None)
+    good = (FAKE, 64 * 656, 64)
+    bad_pools = [
+        (FAKE, 3 * 656 + 16, 3),           # page_records not a power of two
+        (FAKE, 0, 0),                      # page_records 0
+        (FAKE, 656 * 2 ** 31, 2 ** 31),    # page_records above 2^30
+        (FAKE + 8, 64 * 656, 64),          # misaligned base
+        (FAKE, 64 * 656 - 16, 64),         # stride below a page of records
+        (FAKE, 64 * 656 + 8, 64),          # stride not a multiple of 16
+        (FAKE, 1 << 40, 1),                # stride so large that slot offsets overflow
+    ]
+    for bad in bad_pools:
+        for pools in ([bad, good], [good, bad]):
+            assert paged(pools) == -1, (bad, pools)
+            assert lib.sparse_mla_last_error()
+    assert paged(None) == -1
+    assert paged([good, good], sink=FAKE + 2) == -1       # misaligned sink
+    assert paged([good, good], H=65) == -2
+    assert paged([good, good], wsb=100) == -3
+    # absent pools and T = 0 are accepted without touching the device
+    assert paged([(None, 0, 0), (None, 0, 0)], T=0, q=None, out=None, ws=None) == 0
+    assert paged([good, (None, 0, 0)], T=0) == 0
+
+
 def test_profile_state_machine(b):
     lib = b.lib()
     ms = (ctypes.c_double * 4)()

@@ -19,6 +19,7 @@ import oracle
 import oracle.attention as oatt
 import oracle.codec as ocodec
 import synth
+from pools import paged_layout
 
 SIGMA = float(np.float32(1.0 / math.sqrt(576)))
 
@@ -543,29 +544,6 @@ def test_writer_planted_mistakes(monkeypatch, name):
 # ----------------------------------------------------------------- paged pools and sink pins
 
 import oracle.paged as opaged  # noqa: E402
-
-
-def paged_layout(rng, kv, per_page=(16, 8), pad=(3 * 656 + 16, 0)):
-    """Scatter the records of a contiguous kv over two paged pools (a random
-    pool and a random slot for every record; pages laid out page_stride apart
-    with garbage in the gaps).  Returns (pools, entry_of) with entry_of[i] the
-    key-table entry of record i."""
-    N = kv.shape[0]
-    pool_of = rng.integers(0, 2, N)
-    pools, entry_of = [], np.zeros(N, np.int64)
-    for p in range(2):
-        ids = np.flatnonzero(pool_of == p)
-        slots = rng.permutation(max(len(ids), 1))[: len(ids)]
-        blk = per_page[p]
-        stride = blk * 656 + pad[p]
-        npages = (int(slots.max()) // blk + 1) if len(ids) else 1
-        buf = rng.integers(0, 256, npages * stride, dtype=np.uint8)
-        for i, s in zip(ids, slots):
-            off = (s // blk) * stride + (s % blk) * 656
-            buf[off:off + 656] = kv[i]
-            entry_of[i] = s if p == 0 else np.int64(np.int32(np.uint32(s | (1 << 31))))
-        pools.append((buf, stride, blk))
-    return pools, entry_of
 
 
 def paged_case(seed):
