@@ -620,6 +620,31 @@ def test_sink_bruteforce_extra_key():
         assert abs(lse[h] - (mx + math.log(tot))) <= 1e-12
 
 
+def test_sink_is_one_more_merged_part():
+    """Chunk results without the sink, merged together with one extra part of
+    out 0 and lse = sink (stage_combine's fold), equal the unsplit forward with
+    the sink; this is how split rows take their sink."""
+    rng, kv, q, ip, ix = paged_case(9)
+    pools, entry_of = paged_layout(rng, kv)
+    pix = np.where(ix >= 0, entry_of[np.maximum(ix, 0)], -1)
+    sink = np.array([1.0, -np.inf, 6.0])
+    whole = opaged.sparse_mla_fwd_paged(q, pools, ip, pix, SIGMA, sink=sink)
+    for r in range(len(ip) - 1):
+        b, e = int(ip[r]), int(ip[r + 1])
+        for cuts in ([], [b + (e - b) // 2], [b, b + 1, e]):
+            edges = [b] + [c for c in cuts if b <= c <= e] + [e]
+            parts = []
+            for lo, hi in zip(edges[:-1], edges[1:]):
+                o, l = opaged.sparse_mla_fwd_paged(q[r:r + 1], pools, [0, hi - lo], pix[lo:hi], SIGMA)
+                parts.append((o[0], l[0]))
+            parts.append((np.zeros((3, 512)), sink))
+            out, lse = oracle.lse_merge(parts)
+            assert np.max(np.abs(out - whole[0][r])) <= 1e-12 * max(1.0, np.abs(whole[0][r]).max())
+            fin = np.isfinite(whole[1][r])
+            assert np.array_equal(np.isfinite(lse), fin)
+            assert np.max(np.abs(lse[fin] - whole[1][r][fin]), initial=0.0) <= 1e-12
+
+
 def test_sink_empty_row():
     out, lse = opaged.row_attention_sink(np.zeros((2, 576)), np.zeros((0, 576)), SIGMA, np.array([1.5, -np.inf]))
     assert np.all(out == 0.0) and lse[0] == 1.5 and lse[1] == -np.inf
