@@ -83,10 +83,10 @@ struct CacheWriteParams {
   int64_t n_kv;
 };
 
-// Head tiling: HT tiles of 16 heads; TG token groups of 32 tokens per tile.
+// Head tiling: tiles of 16 heads.  Tokens per tile: 128 for the H <= 16
+// kernel, 64 for the wide-head kernel.
 inline int head_tiles(int H) { return (H + 15) / 16; }
-inline int token_groups(int H) { int ht = head_tiles(H); return ht >= 3 ? 1 : 4 / ht; }
-inline int tile_tokens(int H) { return kTokensPerWave * token_groups(H); }
+inline int tile_tokens(int H) { return head_tiles(H) == 1 ? 128 : 64; }
 
 // Optional timing events: `start` is attached to the first kernel dispatch of
 // a launch and `stop` to the last (hipExtLaunchKernel); null = untimed.
@@ -99,6 +99,8 @@ struct Events {
 // (order, and row_tiles from indptr when there was no scan) when `sort`.
 hipError_t launch_plan(const PlanParams& p, bool sort, Events ev, hipStream_t s);
 hipError_t launch_fwd(const FwdParams& p, Events ev, hipStream_t s);
+// The wide-head forward (17 <= H <= 64), smla_wide.hip.
+hipError_t launch_fwd_wide(const FwdParams& p, Events ev, hipStream_t s);
 // Device address of the library's zero record on the current device.
 hipError_t zero_record_address(const uint8_t** out);
 hipError_t launch_combine(const CombineParams& p, Events ev, hipStream_t s);

@@ -37,182 +37,15 @@
 #include <type_traits>
 #include <math.h>
 
-#include "smla_internal.h"
+#include "smla_device.h"
 
 namespace smla {
-
-typedef int v4i __attribute__((ext_vector_type(4)));
-typedef int v2i __attribute__((ext_vector_type(2)));
-typedef float v4f __attribute__((ext_vector_type(4)));
-typedef float v2f __attribute__((ext_vector_type(2)));
-typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
-typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
-typedef _Float16 v8h __attribute__((ext_vector_type(8)));
-typedef _Float16 v2h __attribute__((ext_vector_type(2)));
-typedef _Float16 v4h __attribute__((ext_vector_type(4)));
-
-#define LDSP(T, off) ((__attribute__((address_space(3))) T*)(uintptr_t)(off))
-#define GLBP(T, addr) ((const __attribute__((address_space(1))) T*)(uintptr_t)(addr))
-
-constexpr int kLat = 512;
-constexpr int kScaleOff = 512;
-constexpr int kRopeOff = 528;
-constexpr int kWaveLatBytes = kTokensPerWave * kLat;  // 16 KiB per wave per stage
-constexpr float kPShift = 8.0f;
-constexpr float kScaleCap = 128.0f;  // 2^7: P' = P * scale <= 2^15 fits f16
-constexpr float kLn2 = 0.693147180559945309f;
 
 // A record of zeros: masked positions gather it, so they read finite data
 // (V = 0, scale = 0) wherever the cache is, and never address row 0.
 __device__ __attribute__((aligned(256))) uint8_t g_zero_record[kRecordBytes];
 
-// ---------------------------------------------------------------- helpers
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t idx_rsrc(const int32_t* base, uint32_t nbytes) {
-  // raw buffer, stride 0: reads at byte offsets >= nbytes return 0
-  return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)nbytes, 0x00020000);
-}
-
-__device__ __forceinline__ int load_idx(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
-  return __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0);
-}
-
-// 16 bytes from a 64-bit global address into LDS at lds_base + 16*lane (LDS
-// DMA).  Issued from asm so the compiler's wait-count insertion does not make
-// every later LDS read wait for it; callers wait explicitly (vmcnt(0)).
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"  // m0 is the DMA's LDS base; nothing else here uses it
-__device__ __forceinline__ void dma16(const uint8_t* src, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(src), "s"(lds_base) : "memory", "m0");
-}
-// 16 bytes per lane from the SGPR address `base` plus a per-lane 32-bit
-// offset into LDS at lds_base + 16*lane (LDS DMA, scalar-base form).
-__device__ __forceinline__ void dma16_s(const uint8_t* base, uint32_t voff, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :: "v"(voff), "s"(base), "s"(lds_base) : "memory", "m0");
-}
-// 4 bytes per lane through a bounded buffer descriptor (reads past its size
-// return 0) into LDS at lds_base + 4*lane.
-__device__ __forceinline__ void buf_dma4(__amdgpu_buffer_rsrc_t rsrc, uint32_t voffset, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
-               :: "v"(voffset), "s"(rsrc), "s"(lds_base) : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
-// vmcnt(0) only (expcnt, lgkmcnt left at their maxima), through the intrinsic
-// so the compiler's own wait tracking knows every load has completed here.
-__device__ __forceinline__ void wait_vm_all() {
-  __builtin_amdgcn_s_waitcnt(0x0F70);
-}
-
-__device__ __forceinline__ float fmax_(float a, float b) { return __builtin_fmaxf(a, b); }
-
-__device__ __forceinline__ float xor_max(float v) {
-  v = fmax_(v, __shfl_xor(v, 16));
-  return fmax_(v, __shfl_xor(v, 32));
-}
-__device__ __forceinline__ float xor_sum(float v) {
-  v += __shfl_xor(v, 16);
-  return v + __shfl_xor(v, 32);
-}
-
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __builtin_bit_cast(uint32_t, f);
-  if ((u & 0x7f800000u) == 0x7f800000u) return (uint16_t)((u >> 16) | ((u & 0xffff) ? 0x40 : 0));
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
-
-// 4 e4m3 codes (one word) x pow2 scale -> 4 bf16 (exact), as two v2bf.
-__device__ __forceinline__ void cvt4_bf16(int w, float sc, v2bf& lo, v2bf& hi) {
-  lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, sc, false);
-  hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, sc, true);
-}
-
-// 8 e4m3 codes (two words) -> 8 f16 (exact).
-__device__ __forceinline__ v8h cvt8_f16(v2i w) {
-  v2h a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.x, 1.0f, false);
-  v2h b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.x, 1.0f, true);
-  v2h c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.y, 1.0f, false);
-  v2h d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.y, 1.0f, true);
-  return v8h{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
-}
-
-
-// Split partials of the output are stored as f16: a normalised partial is a
-// convex combination of V values, |V| <= 448 * 2^7 = 57344, so it fits f16's
-// range, and its 11-bit precision is finer than the bf16 of the result.
-__device__ __forceinline__ void st_half4(uint16_t* dst, v4f v) {
-  *(v4h*)dst = v4h{(_Float16)v.x, (_Float16)v.y, (_Float16)v.z, (_Float16)v.w};
-}
-__device__ __forceinline__ v4f half4_to_f32(v2i raw) {
-  const v4h hv = __builtin_bit_cast(v4h, raw);
-  return v4f{(float)hv.x, (float)hv.y, (float)hv.z, (float)hv.w};
-}
-
-// XCD-aware unit mapping: block b runs on XCD b % 8; rows of rank r go to XCD
-// r % 8 and the `per_row` blocks of a row are consecutive on that XCD.
-__device__ __forceinline__ void xcd_unit(int per_row, int& rank, int& sub) {
-  const int b = blockIdx.x;
-  const int i = b >> 3;
-  rank = (b & 7) + 8 * (i / per_row);
-  sub = i % per_row;
-}
-
-// Record address of an index entry that is a key (KeyMode::valid).
-__device__ __forceinline__ const uint8_t* key_addr(const FwdParams& p, int e) {
-  if (!p.km.paged) return p.kv + (int64_t)e * kRecordBytes;
-  // selects, not a dynamic index into the kernel argument (that would copy
-  // the whole argument to scratch memory)
-  const bool c = e < 0;
-  const uint32_t slot = (uint32_t)e & 0x7FFFFFFFu;
-  const uint32_t sh = (uint32_t)(c ? p.pool_shift[1] : p.pool_shift[0]);
-  const uint8_t* const base = c ? p.pool[1] : p.pool[0];
-  const int64_t stride = c ? p.pool_stride[1] : p.pool_stride[0];
-  return base + (int64_t)(slot >> sh) * stride + (int64_t)(slot & ((1u << sh) - 1u)) * kRecordBytes;
-}
-
 // ---------------------------------------------------------------- plan
-
-// Tiles of a row from its effective length.
-__device__ __forceinline__ int tiles_of(int len, int tile) { return (len + tile - 1) / tile; }
-
-// Tiles of row `row` for a forward block of NT threads: the plan's count when
-// there is a plan; with has_invalid and no plan, 1 + the last slice position
-// whose entry is >= 0, found by every thread of the block (bounded index
-// reads, one round of NT x 4 entries per pass) and a block-wide max through
-// `red` (NT / 64 ints of LDS); otherwise the slice length.
-template <int NT>
-__device__ __forceinline__ int unit_tiles(const FwdParams& p, int row, int beg, int len, int tile, int* red) {
-  if (p.row_tiles) return p.row_tiles[row];
-  if (!p.scan) return tiles_of(len, tile);
-  const __amdgpu_buffer_rsrc_t r = idx_rsrc(p.indices, p.idx_bytes);
-  const int tid = threadIdx.x;
-  int lastp = 0;
-  for (int base = 0; base < len; base += 4 * NT) {
-    int v[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) v[j] = load_idx(r, (uint32_t)(beg + base + NT * j + tid) * 4u);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int pos = base + NT * j + tid;
-      if (pos < len && p.km.valid(v[j])) lastp = max(lastp, pos + 1);
-    }
-  }
-#pragma unroll
-  for (int sh = 32; sh >= 1; sh >>= 1) lastp = max(lastp, __shfl_xor(lastp, sh));
-  if ((tid & 63) == 0) red[tid >> 6] = lastp;
-  __syncthreads();
-  int m = 0;
-#pragma unroll
-  for (int k = 0; k < NT / 64; ++k) m = max(m, red[k]);
-  return tiles_of(m, tile);
-}
 
 // has_invalid only: one wave per row finds 1 + the last slice position whose
 // entry is >= 0 (bounded index reads) and stores the row's tile count.
@@ -287,39 +120,6 @@ __global__ __launch_bounds__(1024) void smla_plan_sort_kernel(PlanParams p) {
 }
 
 // ---------------------------------------------------------------- forward
-
-// s_waitcnt immediates (gfx9 layout: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14)
-constexpr int waitcnt_vm(int n) { return (n & 0xF) | (0x7 << 4) | (0xF << 8) | (((n >> 4) & 0x3) << 14); }
-constexpr int kWaitLgkm0 = 0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14);
-
-constexpr int kLatRow = kLat + 16;  // LDS row of a token's latent, padded: QK reads conflict-free
-constexpr int kWaveLatStage = kTokensPerWave * kLatRow;
-constexpr int kSideTok = 144;       // scales (16 B) + rope (128 B) of a record
-constexpr int kSideChunks = 9;
-constexpr int kRing = 8;            // index ring slots (tiles)
-constexpr int kIdxAhead = 5;        // tile n issues the index load of tile n + 5
-constexpr float kShift = 4.0f;      // P = exp2(x - m_ref + 4)
-constexpr float kTau = 4.0f;        // m_ref moves only when a head's max exceeds it by > 4
-
-// A head's final normalisation.  l is its softmax sum of P = 2^(x - m + kShift)
-// (m in log2 units), sink2 its sink logit in log2 units (-inf: none; the sink
-// is one more key whose value is 0, K2-back page, stage_combine).  Returns the
-// factor that turns the accumulated O into the output, and the lse in log2
-// units.  Without a sink this is 1 / l and m - kShift + log2 l.
-struct Norm {
-  float scale, lse2;
-};
-__device__ __forceinline__ Norm finish_norm(float l, float m, float sink2) {
-  const float mo = l > 0.0f ? m - kShift : -INFINITY;
-  const float mm = fmax_(mo, sink2);
-  if (mm == -INFINITY) return Norm{0.0f, -INFINITY};
-  const float a = l > 0.0f ? __builtin_amdgcn_exp2f(mo - mm) : 0.0f;
-  const float L = l * a + __builtin_amdgcn_exp2f(sink2 - mm);
-  return Norm{a / L, mm + __builtin_log2f(L)};
-}
-__device__ __forceinline__ float sink_log2(const float* sink, int h) {
-  return sink ? sink[h] * 1.4426950408889634f : -INFINITY;
-}
 
 template <int HT, int TG>
 struct FwdCfg {
@@ -792,25 +592,10 @@ struct Side {
   uint32_t vmask;
 };
 
-// 16 bytes from global memory into registers, issued from asm: the compiler
-// does not count it, so it never inserts a wait for it; the kernel waits with
-// explicit vmcnt counts and then pins the registers (pin()).
-__device__ __forceinline__ void gload16(v4f& dst, uint64_t addr) {
-  asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(dst) : "v"(addr) : "memory");
-}
-__device__ __forceinline__ void gload16(v4i& dst, uint64_t addr) {
-  asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(dst) : "v"(addr) : "memory");
-}
 // After the wait that covers a side load: later reads of the registers may
 // not move above this point.
 __device__ __forceinline__ void pin(Side& s) { asm volatile("" : "+v"(s.ksc), "+v"(s.rp0), "+v"(s.rp1)); }
 
-// vmcnt waits with a compile-time count
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(N));
-}
 }  // namespace n16
 
 // The fields the prologue needs first come as separate scalar arguments ahead
@@ -1376,10 +1161,7 @@ hipError_t launch_fwd(const FwdParams& p, Events ev, hipStream_t s) {
                             ev.start, ev.stop, 0, p.indptr, p.indices, p.q, p.T, p.S, p.idx_bytes, p.stride, p);
       return hipGetLastError();
     }
-    case 2: return launch_fwd_t<2, 2>(p, ev, s);
-    case 3: return launch_fwd_t<3, 1>(p, ev, s);
-    case 4: return launch_fwd_t<4, 1>(p, ev, s);
-    default: return hipErrorInvalidValue;
+    default: return launch_fwd_wide(p, ev, s);
   }
 }
 
