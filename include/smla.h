@@ -45,8 +45,9 @@ typedef enum {
   SMLA_EHIP = -4             /* a HIP runtime call failed; the message carries hipGetErrorString */
 } smla_status;
 
-/* Largest head count the kernels implement (they tile heads by 16). */
-#define SMLA_MAX_HEADS 64
+/* Largest head count the kernels implement (they tile heads by 16; above
+ * 64 heads a row's heads are processed in groups of 64). */
+#define SMLA_MAX_HEADS 128
 
 /*
  * sparse_mla_supported -- 1 if a forward with `num_heads` heads is implemented,
@@ -115,7 +116,7 @@ int32_t sparse_mla_split_for(int32_t T, int32_t H, int64_t nnz);
  *
  * Returns SMLA_OK, or SMLA_EINVAL / SMLA_EUNSUPPORTED / SMLA_EWORKSPACE /
  * SMLA_EHIP with nothing queued.  Queues on `stream`: a plan when there are
- * more (row, chunk) units than compute units (a slice scan when has_invalid,
+ * more (row, chunk, head group) units than compute units (a slice scan when has_invalid,
  * then a one-block longest-first sort of the rows; otherwise every unit
  * starts at once, rows run in their own order and each forward block scans
  * its own slice); the forward; and a combine when rows are split.  No host

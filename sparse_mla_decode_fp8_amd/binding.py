@@ -21,7 +21,7 @@ SMLA_EINVAL = -1
 SMLA_EUNSUPPORTED = -2
 SMLA_EWORKSPACE = -3
 SMLA_EHIP = -4
-MAX_HEADS = 64
+MAX_HEADS = 128
 MAX_SPLIT = 32
 RECORD_BYTES = 656
 

@@ -81,8 +81,9 @@ int choose_split(int32_t T, int32_t H, int64_t nnz) {
   const int tile = smla::tile_tokens(H);
   const int64_t avg_tiles = (nnz / T + tile - 1) / tile;
   const int cus = device_cus();
-  if (T >= cus) return 1;
-  int64_t s = (cus + T - 1) / T;
+  const int64_t units = (int64_t)T * smla::head_groups(H);  // unsplit units
+  if (units >= cus) return 1;
+  int64_t s = (cus + units - 1) / units;
   if (s > avg_tiles) s = avg_tiles;
   if (s > SMLA_MAX_SPLIT) s = SMLA_MAX_SPLIT;
   return s < 1 ? 1 : (int)s;
@@ -213,7 +214,7 @@ int fwd_impl(const void* q, int64_t q_stride_t, int64_t q_stride_h, const KeySou
   // order cannot shorten the slowest.  Without an order there is nothing to
   // plan: each forward block takes its row's length from indptr and, with
   // has_invalid, trims the trailing masked entries by a scan of its own row.
-  const bool sort = (int64_t)T * L.S > device_cus();
+  const bool sort = (int64_t)T * L.S * smla::head_groups(H) > device_cus();
   hipError_t e = hipSuccess;
   if (sort) {
     smla::PlanParams pp{indptr, indices, idx_bytes, T, smla::tile_tokens(H), has_invalid ? 1 : 0,
@@ -254,6 +255,7 @@ int fwd_impl(const void* q, int64_t q_stride_t, int64_t q_stride_h, const KeySou
     fp.pool_shift[i] = ks.pool_shift[i];
   }
   fp.sink = sink;
+  fp.hg = smla::head_groups(H);
   e = timed(1, [&](smla::Events ev) { return smla::launch_fwd(fp, ev, s); });
   if (e != hipSuccess) return hip_fail(e, "forward kernel launch");
 

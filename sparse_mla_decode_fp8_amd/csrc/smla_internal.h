@@ -59,6 +59,7 @@ struct FwdParams {
   int64_t pool_stride[2];     // paged: bytes from one page to the next
   int32_t pool_shift[2];      // paged: log2 of the records per page
   const float* sink;          // nullable: per-head sink logit [H] (natural log); unsplit rows only
+  int32_t hg;                 // head groups per row (units per row = S * hg)
 };
 
 struct CombineParams {
@@ -87,6 +88,8 @@ struct CacheWriteParams {
 // kernel, 64 for the wide-head kernel.
 inline int head_tiles(int H) { return (H + 15) / 16; }
 inline int tile_tokens(int H) { return head_tiles(H) == 1 ? 128 : 64; }
+// Head groups of a row: the wide-head kernel takes at most 64 heads per unit.
+inline int head_groups(int H) { return (H + 63) / 64; }
 
 // Optional timing events: `start` is attached to the first kernel dispatch of
 // a launch and `stop` to the last (hipExtLaunchKernel); null = untimed.

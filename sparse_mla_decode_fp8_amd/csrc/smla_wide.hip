@@ -1,11 +1,12 @@
-// Wide-head forward: 17 <= H <= 64 heads (HT = 2 or 4 tiles of 16 heads),
-// the prefill and wide decode shapes.  Same method as the H <= 16 kernel
+// Wide-head forward: 17 <= H <= 128 heads (HT = 2 or 4 tiles of 16 heads;
+// above 64 heads a row's heads form groups of 64, each its own unit), the
+// prefill and wide decode shapes.  Same method as the H <= 16 kernel
 // (vLLM API page "vllm.models.kimi_k3.amd.ops.flydsl_sparse_mla_gfx950",
 // module docstring; split chunks merged as on the K2-back page,
 // stage_combine), laid out so that every record is converted once per head
 // tile it meets and the MFMA units stay busy.
 //
-// One block of 8 waves (two per SIMD) per unit (row, chunk); tiles of 64
+// One block of 8 waves (two per SIMD) per unit (row, chunk, head group); tiles of 64
 // tokens, three LDS stages (records of tiles n+1 and n+2 are in flight while
 // tile n is computed).
 //   DMA: wave w brings in tokens 8w .. 8w+7 of a tile: their latent rows (token
@@ -54,7 +55,8 @@ struct Cfg {
   static constexpr int kMxOff = kSxOff + 4 * kPRow;               // maxima f32 [head][wave of the tile]
   static constexpr int kRingOff = kMxOff + kHeads * kWph * 4;
   static constexpr int kTabOff = kRingOff + kRingSlots * kTile * 4;  // record addresses [wave][8]
-  static constexpr int kBytes = kTabOff + kTile * 8;
+  static constexpr int kKeyOff = kTabOff + kTile * 8;  // key masks u64 [ring slot]: bit i = token i is a key
+  static constexpr int kBytes = kKeyOff + kRingSlots * 8;
   static_assert(kBytes <= 160 * 1024, "LDS budget");
   static_assert(kGpw >= 1 && kWph * kGpw * 16 == kTile, "QK covers the tile");
 };
@@ -91,9 +93,11 @@ __global__ __launch_bounds__(nw::kThreads, 1) void smla_fwdw_kernel(FwdParams p)
   const int ht = w % HT;        // QK head tile of this wave
   const int wi = w / HT;        // this wave's index among the waves of its head tile
 
-  int rank, chunk;
-  xcd_unit(p.S, rank, chunk);
+  int rank, sub;
+  xcd_unit(p.S * p.hg, rank, sub);
   if (rank >= p.T) return;
+  const int chunk = sub % p.S;
+  const int h0 = 64 * (sub / p.S);  // first head of this unit's head group
 
   const uint32_t base = lds_addr(s_lds);
   const int row = p.order ? p.order[rank] : rank;
@@ -106,17 +110,18 @@ __global__ __launch_bounds__(nw::kThreads, 1) void smla_fwdw_kernel(FwdParams p)
   const int unit = row * p.S + chunk;
   const bool split = p.S > 1;
   const int H = p.H;
+  const int Hl = min(H - h0, C::kHeads);  // heads of this group
 
   if (t0 >= t1) {  // nothing to attend: zero output and the sink's lse, or an empty partial
     if (split) {
-      for (int hh = tid; hh < H; hh += kThreads) p.part_lse[(int64_t)unit * H + hh] = -INFINITY;
+      for (int hh = h0 + tid; hh < h0 + Hl; hh += kThreads) p.part_lse[(int64_t)unit * H + hh] = -INFINITY;
     } else {
-      for (int e = tid; e < H * (kLat / 8); e += kThreads) {
-        const int hh = e / (kLat / 8), d = (e % (kLat / 8)) * 8;
+      for (int e = tid; e < Hl * (kLat / 8); e += kThreads) {
+        const int hh = h0 + e / (kLat / 8), d = (e % (kLat / 8)) * 8;
         *(v4i*)(p.out + row * p.o_st + hh * p.o_sh + d) = v4i{0, 0, 0, 0};
       }
       if (p.lse)
-        for (int hh = tid; hh < H; hh += kThreads)
+        for (int hh = h0 + tid; hh < h0 + Hl; hh += kThreads)
           p.lse[(int64_t)row * H + hh] = p.sink ? p.sink[hh] : -INFINITY;
     }
     return;
@@ -135,13 +140,18 @@ __global__ __launch_bounds__(nw::kThreads, 1) void smla_fwdw_kernel(FwdParams p)
     const uint32_t dst = __builtin_amdgcn_readfirstlane(ring_at(n) + 32 * w);
     if (lane < 8) buf_dma4(irs, (uint32_t)(beg + n * kTile + 8 * w + lane) * 4u, dst);
   };
-  // record addresses of this wave's 8 tokens of tile n (no key: the zero record)
+  // record addresses of this wave's 8 tokens of tile n (no key: the zero
+  // record), and their bits of the tile's key mask
+  const uint32_t keys = base + C::kKeyOff;
   auto fill_table = [&](int n) {
+    bool ok = false;
     if (lane < 8) {
       const int raw = *LDSP(int, ring_at(n) + 4 * (8 * w + lane));
-      const int ix = (n * kTile + 8 * w + lane < len) ? raw : -1;
-      *LDSP(uint64_t, tab + 8 * lane) = (uint64_t)(uintptr_t)(p.km.valid(ix) ? key_addr(p, ix) : zero);
+      ok = (n * kTile + 8 * w + lane < len) && p.km.valid(raw);
+      *LDSP(uint64_t, tab + 8 * lane) = (uint64_t)(uintptr_t)(ok ? key_addr(p, raw) : zero);
     }
+    const uint32_t bits = (uint32_t)__ballot(ok) & 0xFFu;
+    if (lane == 0) *LDSP(uint8_t, keys + 8 * (n & (kRingSlots - 1)) + w) = (uint8_t)bits;
   };
   // L: latent (4 token pairs; lanes 0..31 the even token, 32..63 the odd one,
   // whose lane position q loads chunk q ^ 8) and side data (scales + rope,
@@ -171,11 +181,11 @@ __global__ __launch_bounds__(nw::kThreads, 1) void smla_fwdw_kernel(FwdParams p)
   issue_idx(t0);
   if (t0 + 1 < t1) issue_idx(t0 + 1);
   if (t0 + 2 < t1) issue_idx(t0 + 2);
-  const int hq = 16 * ht + t;
-  const bool hq_ok = hq < H;
+  const int hq = 16 * ht + t;  // head of the group
+  const bool hq_ok = hq < Hl;
   v4i qr[kQLoads];
   {
-    const uint64_t qa = (uint64_t)(uintptr_t)(p.q + row * p.q_st + (int64_t)(hq_ok ? hq : 0) * p.q_sh);
+    const uint64_t qa = (uint64_t)(uintptr_t)(p.q + row * p.q_st + (int64_t)(h0 + (hq_ok ? hq : 0)) * p.q_sh);
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
       gload16(qr[2 * m], qa + 2 * (64 * m + 16 * g));
@@ -240,7 +250,7 @@ __global__ __launch_bounds__(nw::kThreads, 1) void smla_fwdw_kernel(FwdParams p)
     // ---- QK of this wave's groups: lane (t, g) gets head 16 ht + t, tokens 16j + 4g + r
     const uint32_t lat = lat_at(st);
     const uint32_t side = side_at(st);
-    const uint32_t ring = ring_at(n);
+    const uint64_t kmask = *LDSP(uint64_t, keys + 8 * (n & (kRingSlots - 1)));
     float x[C::kGpw][4];
     float tmax = -INFINITY;
 #pragma unroll
@@ -273,12 +283,11 @@ __global__ __launch_bounds__(nw::kThreads, 1) void smla_fwdw_kernel(FwdParams p)
         acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qlat[2 * m + 1], acc1, 0, 0, 0);
       }
       const v4f S = acc0 + acc1;
-      // which of tokens 16j + 4g + r are keys (the index ring of tile n)
-      const v4i ix = *LDSP(v4i, ring + 4 * (16 * j + 4 * g));
+      // which of tokens 16j + 4g + r are keys
+      const uint32_t kb = (uint32_t)(kmask >> (16 * j + 4 * g));
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const bool ok = (n * kTile + 16 * j + 4 * g + r < len) && p.km.valid(ix[r]);
-        x[gi][r] = ok ? S[r] * p.c_log2 : -INFINITY;
+        x[gi][r] = ((kb >> r) & 1u) ? S[r] * p.c_log2 : -INFINITY;
         tmax = fmax_(tmax, x[gi][r]);
       }
       // V scale of block g for token tok, clamped to 2^7, as f16 (one head tile writes it)
@@ -373,8 +382,8 @@ __global__ __launch_bounds__(nw::kThreads, 1) void smla_fwdw_kernel(FwdParams p)
   // (split: a partial without the sink, which the combine folds in)
 #pragma unroll
   for (int j = 0; j < HT; ++j) {
-    const int h = 16 * j + t;
-    const bool h_ok = h < H;
+    const int h = h0 + 16 * j + t;  // head of the row
+    const bool h_ok = 16 * j + t < Hl;
     const float l = xor_sum(l_run[j]);
     const Norm nm = finish_norm(l, m_ref[j], (split || !h_ok) ? -INFINITY : sink_log2(p.sink, h));
     if (w == 0 && g == 0 && h_ok) {
@@ -400,7 +409,7 @@ __global__ __launch_bounds__(nw::kThreads, 1) void smla_fwdw_kernel(FwdParams p)
 
 template <int HT>
 static hipError_t launch_fwdw_t(const FwdParams& p, Events ev, hipStream_t s) {
-  const int64_t blocks = xcd_grid(p.T, p.S);
+  const int64_t blocks = xcd_grid(p.T, p.S * p.hg);
   hipExtLaunchKernelGGL((smla_fwdw_kernel<HT>), dim3((unsigned)blocks), dim3(nw::kThreads), 0, s,
                         ev.start, ev.stop, 0, p);
   return hipGetLastError();
@@ -409,7 +418,7 @@ static hipError_t launch_fwdw_t(const FwdParams& p, Events ev, hipStream_t s) {
 hipError_t launch_fwd_wide(const FwdParams& p, Events ev, hipStream_t s) {
   const int ht = head_tiles(p.H);
   if (ht == 2) return launch_fwdw_t<2>(p, ev, s);
-  if (ht == 3 || ht == 4) return launch_fwdw_t<4>(p, ev, s);
+  if (ht >= 3 && ht <= 8) return launch_fwdw_t<4>(p, ev, s);  // above 64 heads: groups of 64
   return hipErrorInvalidValue;
 }
 

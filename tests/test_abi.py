@@ -36,8 +36,8 @@ def test_exports_every_declared_symbol(b):
 
 def test_supported_range(b):
     assert not b.supported(0)
-    assert b.supported(1) and b.supported(16) and b.supported(64)
-    assert not b.supported(65)
+    assert b.supported(1) and b.supported(16) and b.supported(64) and b.supported(128)
+    assert not b.supported(129)
 
 
 def test_workspace_bytes(b):
@@ -45,7 +45,7 @@ def test_workspace_bytes(b):
     small = b.workspace_bytes(4096, 64, 4096 * 2048)   # many rows: no split partials
     assert small < 1 << 20
     with pytest.raises(b.SmlaError) as e:
-        b.workspace_bytes(1, 65, 10)
+        b.workspace_bytes(1, 129, 10)
     assert e.value.status == b.SMLA_EUNSUPPORTED
     with pytest.raises(b.SmlaError) as e:
         b.workspace_bytes(-1, 16, 10)
@@ -67,7 +67,7 @@ def call(b, **over):
 
 
 @pytest.mark.parametrize("over,status", [
-    (dict(H=0), -2), (dict(H=65), -2), (dict(T=-1), -1), (dict(nnz=-1), -1),
+    (dict(H=0), -2), (dict(H=129), -2), (dict(T=-1), -1), (dict(nnz=-1), -1),
     (dict(nnz=(1 << 30) - 4095), -1), (dict(n_kv=-1), -1), (dict(scale=float("inf")), -1),
     (dict(q=None), -1), (dict(kv=None), -1), (dict(indptr=None), -1), (dict(out=None), -1),
     (dict(ws=None), -1), (dict(indices=None), -1), (dict(q=FAKE + 8), -1),
@@ -149,7 +149,7 @@ def test_fwd_paged_validation(b):
             assert lib.sparse_mla_last_error()
     assert paged(None) == -1
     assert paged([good, good], sink=FAKE + 2) == -1       # misaligned sink
-    assert paged([good, good], H=65) == -2
+    assert paged([good, good], H=129) == -2
     assert paged([good, good], wsb=100) == -3
     # absent pools and T = 0 are accepted without touching the device
     assert paged([(None, 0, 0), (None, 0, 0)], T=0, q=None, out=None, ws=None) == 0

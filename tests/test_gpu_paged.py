@@ -107,7 +107,7 @@ def test_paged_equals_contiguous_bitwise(smla, H):
     assert torch.equal(l_p, l_c)
 
 
-@pytest.mark.parametrize("H", [16, 64, 3])
+@pytest.mark.parametrize("H", [16, 64, 3, 128])
 @pytest.mark.parametrize("split", [0, 1, 3])
 def test_paged_sink_matches_oracle(smla, H, split):
     """Both pools, -1 entries, an empty row, a one-key row and trailing padding;

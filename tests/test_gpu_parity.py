@@ -140,7 +140,7 @@ def test_negative_length_rows(smla):
     compare(out, lse, ro, rl, label="neglen")
 
 
-@pytest.mark.parametrize("H", [1, 7, 16, 17, 32, 33, 48, 64])
+@pytest.mark.parametrize("H", [1, 7, 16, 17, 32, 33, 48, 64, 65, 96, 100, 128])
 def test_head_counts(smla, H):
     rng = np.random.default_rng(100 + H)
     N = 3000
@@ -165,7 +165,7 @@ def test_forced_split(smla, split):
     compare(out, lse, ro, rl, label=f"split{split}")
 
 
-@pytest.mark.parametrize("split,H", [(2, 16), (3, 7), (4, 16), (8, 16), (8, 1)])
+@pytest.mark.parametrize("split,H", [(2, 16), (3, 7), (4, 16), (8, 16), (8, 1), (3, 64), (2, 128), (5, 40)])
 def test_split_merge_back_to_back(smla, split, H):
     """Split rows: several forwards queued back to back on one stream (new
     inputs each time) must each match the oracle, so the partials of one call
@@ -274,21 +274,23 @@ def test_permutation_duplicates(smla):
     compare(o3, l3 - math.log(2), ro, rl, label="duplicated")
 
 
-def test_causal_ragged_longest_first(smla):
-    """Many ragged rows (row r has min(r + 1, 2048) keys): exercises the
-    longest-first order and has_invalid trimming at scale."""
+@pytest.mark.parametrize("H", [16, 64, 128])
+def test_causal_ragged_longest_first(smla, H):
+    """Many ragged rows (row r has min(3r + 1, 2048) keys): exercises the
+    longest-first order and has_invalid trimming at scale (above 64 heads,
+    with two head groups per row)."""
     T, N = 600, 32768
     rng = np.random.default_rng(14)
     sl = []
     for r in range(T):
         L = min(3 * r + 1, 2048)
         sl.append(np.concatenate([rng.integers(0, N, L), -np.ones(2048 - L, np.int64)]))
-    w = custom("causal", 16, N, sl, has_invalid=1)
-    note(f"causal ragged T={T}")
+    w = custom(f"causal_H{H}", H, N, sl, has_invalid=1)
+    note(f"causal ragged T={T} H={H}")
     out, lse = run_gpu(w)
-    rows = sample_rows(T, 40, seed=1)
+    rows = sample_rows(T, 40 if H == 16 else 12, seed=1)
     ro, rl = run_oracle(w, rows=rows)
-    compare(out, lse, ro, rl, rows=rows, label="causal")
+    compare(out, lse, ro, rl, rows=rows, label=f"causal_H{H}")
 
 
 def test_repeat_calls_bitwise_identical(smla):
