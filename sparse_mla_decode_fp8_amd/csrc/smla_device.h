@@ -28,8 +28,6 @@ typedef _Float16 v4h __attribute__((ext_vector_type(4)));
 constexpr int kLat = 512;
 constexpr int kScaleOff = 512;
 constexpr int kRopeOff = 528;
-constexpr int kWaveLatBytes = kTokensPerWave * kLat;  // 16 KiB per wave per stage
-constexpr float kPShift = 8.0f;
 constexpr float kScaleCap = 128.0f;  // 2^7: P' = P * scale <= 2^15 fits f16
 constexpr float kLn2 = 0.693147180559945309f;
 
@@ -56,12 +54,6 @@ __device__ __forceinline__ int load_idx(__amdgpu_buffer_rsrc_t r, uint32_t byte_
 __device__ __forceinline__ void dma16(const uint8_t* src, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                :: "v"(src), "s"(lds_base) : "memory", "m0");
-}
-// 16 bytes per lane from the SGPR address `base` plus a per-lane 32-bit
-// offset into LDS at lds_base + 16*lane (LDS DMA, scalar-base form).
-__device__ __forceinline__ void dma16_s(const uint8_t* base, uint32_t voff, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :: "v"(voff), "s"(base), "s"(lds_base) : "memory", "m0");
 }
 // 4 bytes per lane through a bounded buffer descriptor (reads past its size
 // return 0) into LDS at lds_base + 4*lane.
@@ -202,12 +194,8 @@ __device__ __forceinline__ void gload16(v4i& dst, uint64_t addr) {
   asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(dst) : "v"(addr) : "memory");
 }
 
-constexpr int kLatRow = kLat + 16;  // LDS row of a token's latent, padded: QK reads conflict-free
-constexpr int kWaveLatStage = kTokensPerWave * kLatRow;
 constexpr int kSideTok = 144;       // scales (16 B) + rope (128 B) of a record
 constexpr int kSideChunks = 9;
-constexpr int kRing = 8;            // index ring slots (tiles)
-constexpr int kIdxAhead = 5;        // tile n issues the index load of tile n + 5
 constexpr float kShift = 4.0f;      // P = exp2(x - m_ref + 4)
 constexpr float kTau = 4.0f;        // m_ref moves only when a head's max exceeds it by > 4
 

@@ -8,7 +8,6 @@
 namespace smla {
 
 constexpr int kRecordBytes = 656;  // 512 e4m3 | 4 x f32 scale | 64 x bf16 rope
-constexpr int kTokensPerWave = 32;  // tokens one wave owns in a tile
 constexpr int kPlanBuckets = 256;   // longest-first counting-sort buckets (tiles, capped)
 
 // Which index entries are keys.  Contiguous cache: entries >= 0.  Paged pools

@@ -9,24 +9,21 @@
 // ("vllm.models.deepseek_v41.amd.mono.attention.back", module docstring and
 // stage_combine).
 //
-// Design for MI355X (differs from the FlyDSL kernel; reasons in the design doc):
-//  * plan kernel: per-row tile counts (a bounded scan for the last valid entry
-//    when has_invalid) and a longest-first row order (counting sort).
-//  * forward kernel: a workgroup owns one (row, chunk) unit.  Waves are
-//    (head tile of 16, token group of 32 tokens).  Every wave runs QK, online
-//    softmax and PV over all 512 dims for its own 32 tokens, so tiles need no
-//    cross-wave exchange; token groups merge once per unit through LDS.
-//  * the latent tile arrives by LDS DMA (global_load_lds_dwordx4 from 64-bit
-//    per-lane record addresses), double-buffered per wave; scales and rope go
-//    straight to registers.  Masked positions read a zero record.
+// Design for MI355X (this file: plan, the H <= 16 forward, combine, record
+// writer and decode hook; the wide-head forward is smla_wide.hip):
+//  * plan kernels: per-row tile counts (a bounded scan for the last valid
+//    entry when has_invalid) and a longest-first row order (counting sort),
+//    launched only when there are more units than compute units.
+//  * forward kernel: a workgroup owns one (row, chunk) unit.  Records arrive
+//    by LDS DMA (global_load_lds_dwordx4 from 64-bit per-lane record
+//    addresses) two tiles deep; masked positions read a zero record.
 //  * QK: K dequantised exactly to bf16 by v_cvt_scalef32_pk_bf16_fp8 with the
 //    record's pow2 scale (the conversion applies the scale's exponent only),
-//    bf16 MFMA 16x16x32 against bf16 q (rope the same).
+//    bf16 MFMA 16x16x32 against bf16 q held in registers (rope the same).
 //  * PV: V read transposed from LDS (ds_read_b64_tr_b8), converted exactly
-//    e4m3 -> f16, f16 MFMA 16x16x32; the per-token V scale is folded into P.
-//    The QK output layout (lane = head, 4 token rows) is chosen so each lane's
-//    scores are already its PV B operand: P never moves between lanes.
-//  * combine kernel: LSE merge of the chunks of split rows.
+//    e4m3 -> f16, f16 MFMA 16x16x32; the per-token V scale is folded into P,
+//    which passes between waves through LDS.
+//  * combine kernel: LSE merge of the chunks of split rows (with the sink).
 //  * workgroup -> unit mapping is XCD-aware: all chunks of a row run on one XCD
 //    (dispatch is round-robin over the 8 XCDs), so partials and q stay in that
 //    XCD's L2.
@@ -34,7 +31,6 @@
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
-#include <type_traits>
 #include <math.h>
 
 #include "smla_device.h"
@@ -116,421 +112,6 @@ __global__ __launch_bounds__(1024) void smla_plan_sort_kernel(PlanParams p) {
   for (int r = tid; r < p.T; r += blockDim.x) {
     const int t = p.row_tiles[r];
     p.order[atomicAdd(&s_cnt[min(t, kPlanBuckets - 1)], 1)] = r;
-  }
-}
-
-// ---------------------------------------------------------------- forward
-
-template <int HT, int TG>
-struct FwdCfg {
-  static constexpr int kWaves = HT * TG;
-  static constexpr int kThreads = 64 * kWaves;
-  static constexpr int kTile = kTokensPerWave * TG;
-  static constexpr int kSideStages = TG == 4 ? 1 : 2;  // TG == 4 implies HT == 1 (wave-private)
-  static constexpr int kLatBytes = 2 * TG * kWaveLatStage;
-  static constexpr int kSideBytes = kSideStages * TG * kTokensPerWave * kSideTok;
-  static constexpr int kIdxBytes = kRing * TG * kTokensPerWave * 4;
-  static constexpr int kTabBytes = 2 * kWaves * kTokensPerWave * 8;  // per-wave record-address tables
-  static constexpr int kSideOff = kLatBytes;
-  static constexpr int kIdxOff = kSideOff + kSideBytes;
-  static constexpr int kTabOff = kIdxOff + kIdxBytes;
-  static constexpr int kStreamBytes = kTabOff + kTabBytes;
-  // merge area: per wave, its 32 accumulator slices (64 lanes x 16 B each)
-  static constexpr int kMergeBytes = TG > 1 ? kWaves * 32 * 64 * 16 : 0;
-  static constexpr int kBigBytes = kStreamBytes > kMergeBytes ? kStreamBytes : kMergeBytes;
-  // vector-memory instructions a wave issues after a tile's latent and side
-  // DMA and before the next tile's wait: one index load
-  static constexpr int kTrailingVm = 1;
-};
-
-template <int HT, int TG>
-__global__ __launch_bounds__(64 * HT * TG, 1) void smla_fwd_kernel(FwdParams p) {
-  using C = FwdCfg<HT, TG>;
-  static_assert(C::kBigBytes + 2 * C::kWaves * 16 * 4 <= 160 * 1024, "LDS budget");
-  __shared__ __attribute__((aligned(1024))) uint8_t s_big[C::kBigBytes];
-  __shared__ float s_m[C::kWaves][16];
-  __shared__ float s_l[C::kWaves][16];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int ht = wave % HT;
-  const int tg = wave / HT;
-  const int t = lane & 15;  // QK token row / PV dim row / C column = head
-  const int g = lane >> 4;  // lane group
-
-  int rank, chunk;
-  xcd_unit(p.S, rank, chunk);
-  if (rank >= p.T) return;
-  // Without a plan the rows run in their own order and a row's tiles follow
-  // from indptr; with one, order[] is longest first and row_tiles[] is the
-  // has_invalid scan's (trailing masked entries trimmed) or indptr's count.
-  const int row = p.order ? p.order[rank] : rank;
-  const int beg = p.indptr[row];
-  const int len = max(p.indptr[row + 1] - beg, 0);
-  const int tiles = unit_tiles<C::kThreads>(p, row, beg, len, C::kTile, (int*)&s_m[0][0]);
-  const int ct = (tiles + p.S - 1) / p.S;
-  const int t0 = min(chunk * ct, tiles);
-  const int t1 = min(t0 + ct, tiles);
-  const int unit = row * p.S + chunk;
-  const bool split = p.S > 1;
-
-  const int h = 16 * ht + t;
-  const bool h_ok = h < p.H;
-
-  if (t0 >= t1) {  // nothing to attend: zero output and the sink's lse, or an empty partial
-    if (split) {
-      for (int hh = tid; hh < p.H; hh += C::kThreads) p.part_lse[(int64_t)unit * p.H + hh] = -INFINITY;
-    } else {
-      for (int e = tid; e < p.H * (kLat / 8); e += C::kThreads) {
-        const int hh = e / (kLat / 8), d = (e % (kLat / 8)) * 8;
-        *(v4i*)(p.out + row * p.o_st + hh * p.o_sh + d) = v4i{0, 0, 0, 0};
-      }
-      if (p.lse)  // a row with no key: lse is the sink (-inf without one)
-        for (int hh = tid; hh < p.H; hh += C::kThreads)
-          p.lse[(int64_t)row * p.H + hh] = p.sink ? p.sink[hh] : -INFINITY;
-    }
-    return;
-  }
-
-  // ---- LDS addresses: latent rows and side data of this wave's token group,
-  // the group's index ring, this wave's record-address tables.
-  const uint32_t big = lds_addr(s_big);
-  auto lat_at = [&](int st) -> uint32_t { return big + (st * TG + tg) * kWaveLatStage; };
-  auto side_at = [&](int st) -> uint32_t {
-    return big + C::kSideOff + (st * TG + tg) * kTokensPerWave * kSideTok;
-  };
-  auto ring_at = [&](int n) -> uint32_t {
-    return big + C::kIdxOff + ((n & (kRing - 1)) * TG + tg) * kTokensPerWave * 4;
-  };
-  auto tab_at = [&](int n) -> uint32_t {
-    return big + C::kTabOff + ((n & 1) * C::kWaves + wave) * kTokensPerWave * 8;
-  };
-  const __amdgpu_buffer_rsrc_t irs = idx_rsrc(p.indices, p.idx_bytes);
-  const uint8_t* const kv = p.kv;
-  const uint8_t* const zero = p.zero;
-
-  // Index at slice position of token `tau` of this group in tile n (from the
-  // ring), -1 past the row.  Positions past nnz read 0 and are masked here.
-  auto ring_ix = [&](int n, int tau) -> int {
-    const int raw = *LDSP(int, ring_at(n) + 4 * tau);
-    return (n * C::kTile + kTokensPerWave * tg + tau < len) ? raw : -1;
-  };
-  auto rec_of = [&](int ix) -> const uint8_t* { return p.km.valid(ix) ? key_addr(p, ix) : zero; };
-  // C: index DMA of tile n (bounded buffer reads, 32 entries) into its ring slot.
-  auto issue_idx = [&](int n) {
-    const uint32_t base = __builtin_amdgcn_readfirstlane(ring_at(n));
-    if (lane < kTokensPerWave) {
-      const uint32_t off = (uint32_t)(beg + n * C::kTile + kTokensPerWave * tg + lane) * 4u;
-      buf_dma4(irs, off, base);
-    }
-  };
-  // Record addresses of tile n's 32 tokens into this wave's table (lane tau
-  // writes token tau's); tiles at or past t1 get the zero record.
-  auto fill_table = [&](int n) {
-    if (lane < kTokensPerWave) {
-      const int ix = n < t1 ? ring_ix(n, lane) : -1;
-      *LDSP(uint64_t, tab_at(n) + 8 * lane) = (uint64_t)(uintptr_t)rec_of(ix);
-    }
-  };
-  // A: latent DMA of tile n into stage st: one instruction per token, its
-  // record address in SGPRs, lanes 0..31 fetch its 16-byte chunks.
-  auto issue_latent = [&](int n, int st) {
-    const int ix = ring_ix(n, lane & 31);
-    const uint32_t base = lat_at(st);
-    if (lane < kTokensPerWave) {
-#pragma unroll
-      for (int tau = ht; tau < kTokensPerWave; tau += HT) {
-        const int v = __builtin_amdgcn_readlane(ix, tau);
-        dma16_s(rec_of(v), 16 * lane, __builtin_amdgcn_readfirstlane(base + kLatRow * tau));
-      }
-    }
-  };
-  // B: side DMA (scales + rope, 9 chunks per token) of tile n into stage st,
-  // addresses from this wave's table.
-  auto issue_side = [&](int n, int st) {
-    const uint32_t base = __builtin_amdgcn_readfirstlane(side_at(st));
-    const uint32_t tab = tab_at(n);
-#pragma unroll
-    for (int k = ht; k < 5; k += HT) {
-      const int piece = 64 * k + lane;
-      if (piece < kTokensPerWave * kSideChunks) {
-        const int tau = piece / kSideChunks, c = piece % kSideChunks;
-        const uint8_t* rec = (const uint8_t*)(uintptr_t)*LDSP(uint64_t, tab + 8 * tau);
-        dma16(rec + kScaleOff + 16 * c, base + 1024 * k);
-      }
-    }
-  };
-
-  // ---- prologue: indices of the first tiles, then tile t0's data
-#pragma unroll
-  for (int k = 0; k < kIdxAhead - 1; ++k) issue_idx(t0 + k);
-  wait_vm_all();
-  if (HT > 1) __syncthreads();
-  fill_table(t0);
-  fill_table(t0 + 1);
-  issue_latent(t0, 0);
-  issue_side(t0, 0);
-  issue_idx(t0 + kIdxAhead - 1);
-  // ---- q as bf16 B operands.  Loaded after tile t0's gather is queued, so
-  // they delay neither the index fetch nor the first records, and waited for
-  // together with tile t0 (so the loop sees them complete).  Latent K-step
-  // 2m / 2m+1: dims 64m + 16g + [0..7] / [8..15]; rope K-step i: dims
-  // 512 + 32i + 8g + [0..7].
-  v8bf qlat[16];
-  v8bf qrope[2];
-  {
-    const uint16_t* qr = p.q + row * p.q_st + (int64_t)(h_ok ? h : 0) * p.q_sh;
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      v4i a = *(const v4i*)(qr + 64 * m + 16 * g);
-      v4i b = *(const v4i*)(qr + 64 * m + 16 * g + 8);
-      if (!h_ok) a = b = v4i{0, 0, 0, 0};
-      qlat[2 * m] = __builtin_bit_cast(v8bf, a);
-      qlat[2 * m + 1] = __builtin_bit_cast(v8bf, b);
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      v4i a = *(const v4i*)(qr + kLat + 32 * i + 8 * g);
-      if (!h_ok) a = v4i{0, 0, 0, 0};
-      qrope[i] = __builtin_bit_cast(v8bf, a);
-    }
-  }
-  wait_vm_all();
-
-  float m_ref = -INFINITY;  // reference max (log2 units) of P and O
-  float l_run = 0.0f;       // this lane's share of sum P
-  v4f O[32];
-#pragma unroll
-  for (int i = 0; i < 32; ++i) O[i] = v4f{0, 0, 0, 0};
-
-  // PV transposed-read lane address: lane (t, g) reads token row j = t/2,
-  // tau_j = 16(j/4) + 4g + j%4, byte half t%2; dim chunk dt is an immediate offset.
-  const int jrow = t >> 1;
-  const int tau_v = 16 * (jrow >> 2) + 4 * g + (jrow & 3);
-  const uint32_t v_off = kLatRow * tau_v + 8 * (t & 1);
-
-  for (int n = t0; n < t1; ++n) {
-    const int st = (n - t0) & 1;
-    const int sst = C::kSideStages == 1 ? 0 : st;
-    // tile n's latent and side data have landed (the later index load may
-    // still be in flight); with several head tiles, for every wave
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(C::kTrailingVm));
-    if (HT > 1) __syncthreads();
-    const int ix_n = ring_ix(n, lane & 31);
-    const uint32_t vmask = (uint32_t)__ballot(p.km.valid(ix_n));  // bit tau: token tau is a key
-    const bool more = n + 1 < t1;
-    if (more) issue_latent(n + 1, st ^ 1);
-    fill_table(n + 2);
-
-    const uint32_t lat = lat_at(st);
-    const uint32_t side = side_at(sst);
-
-    // ---- QK: S^T tiles; lane (t, g) gets head t, tokens 16s + 4g + r.
-    v4f S[2];
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int tau = 16 * s + t;
-      const uint32_t kb = lat + kLatRow * tau + 16 * g;
-      const uint32_t sb = side + kSideTok * tau;
-      v4i kr[8];
-#pragma unroll
-      for (int m = 0; m < 8; ++m) kr[m] = *LDSP(v4i, kb + 64 * m);
-      const v4f ksc = *LDSP(v4f, sb);
-      const v4i rp0 = *LDSP(v4i, sb + 16 + 16 * g);
-      const v4i rp1 = *LDSP(v4i, sb + 80 + 16 * g);
-      v4f acc = v4f{0, 0, 0, 0};
-#pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        const float sc = ksc[m >> 1];
-        v2bf a0, a1, a2, a3, b0, b1, b2, b3;
-        cvt4_bf16(kr[m].x, sc, a0, a1);
-        cvt4_bf16(kr[m].y, sc, a2, a3);
-        cvt4_bf16(kr[m].z, sc, b0, b1);
-        cvt4_bf16(kr[m].w, sc, b2, b3);
-        const v8bf ka = {a0.x, a0.y, a1.x, a1.y, a2.x, a2.y, a3.x, a3.y};
-        const v8bf kb8 = {b0.x, b0.y, b1.x, b1.y, b2.x, b2.y, b3.x, b3.y};
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qlat[2 * m], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb8, qlat[2 * m + 1], acc, 0, 0, 0);
-      }
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, rp0), qrope[0], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, rp1), qrope[1], acc, 0, 0, 0);
-      S[s] = acc;
-    }
-
-    // ---- V scales of this lane's C-layout tokens 16s + 4g + r, clamped to
-    // 2^7 and kept as f16 (exact for the power-of-two scales).  psc[b][k/2]
-    // packs tokens k, k+1 of block b.
-    v2h psc[4][4];
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-      for (int r = 0; r < 4; r += 2) {
-        const v4f a = *LDSP(v4f, side + kSideTok * (16 * s + 4 * g + r));
-        const v4f b = *LDSP(v4f, side + kSideTok * (16 * s + 4 * g + r + 1));
-#pragma unroll
-        for (int blk = 0; blk < 4; ++blk)
-          psc[blk][(4 * s + r) / 2] = v2h{(_Float16)__builtin_fminf(a[blk], kScaleCap),
-                                          (_Float16)__builtin_fminf(b[blk], kScaleCap)};
-      }
-
-    // ---- next tile's side data (its buffer is free once this tile's side
-    // reads are done), index load five ahead
-    __builtin_amdgcn_sched_barrier(0);
-    if (more) {
-      if (C::kSideStages == 1) __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-      issue_side(n + 1, C::kSideStages == 1 ? 0 : (sst ^ 1));
-    }
-    issue_idx(n + kIdxAhead);
-    __builtin_amdgcn_sched_barrier(0);
-
-    // ---- first half of the V^T reads (independent of the softmax)
-    const uint32_t vaddr = lat + v_off;
-    v2i vr[16];
-#pragma unroll
-    for (int dt = 0; dt < 16; ++dt) vr[dt] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(LDSP(v2i, vaddr + 16 * dt));
-
-    // ---- online softmax (log2 domain).  m_ref only moves when some head's
-    // tile max exceeds it by more than kTau, so P = exp2(x - m_ref + kShift)
-    // stays <= 2^(kShift + kTau) = 2^8 and P' = P * scale (<= 2^7) fits f16.
-    float x[8];
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int tau = 16 * s + 4 * g + r;
-        const float v = ((vmask >> tau) & 1u) ? S[s][r] * p.c_log2 : -INFINITY;
-        x[4 * s + r] = v;
-        tmax = fmax_(tmax, v);
-      }
-    tmax = xor_max(tmax);
-    if (__builtin_amdgcn_ballot_w64(tmax > m_ref + kTau)) {
-      const float m_new = fmax_(m_ref, tmax);
-      const float alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_ref - m_new);
-      if (__builtin_amdgcn_ballot_w64(m_ref != -INFINITY)) {  // O and l are still zero otherwise
-        l_run *= alpha;
-#pragma unroll
-        for (int i = 0; i < 32; ++i) O[i] *= alpha;
-      }
-      m_ref = m_new;
-    }
-    const float m_use = (m_ref == -INFINITY) ? 0.0f : m_ref;
-    v2h ph[4];  // P as f16, token pairs
-#pragma unroll
-    for (int k = 0; k < 8; k += 2) {
-      const float p0 = __builtin_amdgcn_exp2f(x[k] - m_use + kShift);
-      const float p1 = __builtin_amdgcn_exp2f(x[k + 1] - m_use + kShift);
-      l_run += p0 + p1;
-      ph[k / 2] = v2h{(_Float16)p0, (_Float16)p1};
-    }
-    v8h pb[4];  // P' B operands, one per V scale block: f16(P) * scale (a power of two)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const v2h q0 = ph[0] * psc[b][0], q1 = ph[1] * psc[b][1];
-      const v2h q2 = ph[2] * psc[b][2], q3 = ph[3] * psc[b][3];
-      pb[b] = v8h{q0.x, q0.y, q1.x, q1.y, q2.x, q2.y, q3.x, q3.y};
-    }
-
-    // ---- PV: O^T[d, h] += V^T[d, tok] P'^T[tok, h] over the wave's 32 tokens
-    v2i vr2[16];
-#pragma unroll
-    for (int dt = 0; dt < 16; ++dt)
-      vr2[dt] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(LDSP(v2i, vaddr + 16 * (dt + 16)));
-#pragma unroll
-    for (int dt = 0; dt < 16; ++dt)
-      O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(cvt8_f16(vr[dt]), pb[dt >> 3], O[dt], 0, 0, 0);
-#pragma unroll
-    for (int dt = 0; dt < 16; ++dt)
-      O[16 + dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(cvt8_f16(vr2[dt]), pb[2 + (dt >> 3)], O[16 + dt], 0, 0, 0);
-  }
-  wait_vm_all();  // drain the trailing index DMA before LDS is reused
-
-  // ---- epilogue
-  l_run = xor_sum(l_run);  // lane (t, *) now holds head t's sum over this wave's tokens
-  if constexpr (TG == 1) {
-    // split: a partial without the sink (the combine folds it in)
-    const Norm nm = finish_norm(l_run, m_ref, (split || !h_ok) ? -INFINITY : sink_log2(p.sink, h));
-    const float inv = nm.scale;
-    const float l2 = nm.lse2;
-    if (h_ok) {
-      if (split) {
-        uint16_t* po = p.part_o + ((int64_t)unit * p.H + h) * kLat;
-#pragma unroll
-        for (int dt = 0; dt < 32; ++dt) st_half4(po + 16 * dt + 4 * g, O[dt] * inv);
-        if (g == 0) p.part_lse[(int64_t)unit * p.H + h] = l2;
-      } else {
-        uint16_t* po = p.out + row * p.o_st + h * p.o_sh;
-#pragma unroll
-        for (int dt = 0; dt < 32; ++dt) {
-          const v4f o = O[dt] * inv;
-          const uint32_t w0 = f32_to_bf16_rne(o.x) | ((uint32_t)f32_to_bf16_rne(o.y) << 16);
-          const uint32_t w1 = f32_to_bf16_rne(o.z) | ((uint32_t)f32_to_bf16_rne(o.w) << 16);
-          *(v2i*)(po + 16 * dt + 4 * g) = v2i{(int)w0, (int)w1};
-        }
-        if (g == 0 && p.lse) p.lse[(int64_t)row * p.H + h] = l2 * kLn2;
-      }
-    }
-  } else {
-    // token groups of a head tile merge through LDS.  Group tg owns the
-    // accumulator slices dt in [tg * 32/TG, (tg + 1) * 32/TG) of its heads:
-    // it writes its other slices (weighted by 2^(m_own - M) / L) for their
-    // owners, then adds the other groups' copies of its own slices.
-    if (g == 0) {
-      s_m[wave][t] = m_ref;
-      s_l[wave][t] = l_run;
-    }
-    __syncthreads();  // every wave is done with the stream buffers
-    // statistics of head t over the token groups (every lane, for its head)
-    float M = -INFINITY;
-#pragma unroll
-    for (int k = 0; k < TG; ++k) M = fmax_(M, s_m[k * HT + ht][t]);
-    float L = 0.0f;
-#pragma unroll
-    for (int k = 0; k < TG; ++k) {
-      const float mk = s_m[k * HT + ht][t];
-      if (mk != -INFINITY) L += s_l[k * HT + ht][t] * __builtin_amdgcn_exp2f(mk - M);
-    }
-    const float w_own = (m_ref == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_ref - M);
-    const Norm nm = finish_norm(L, M, (split || !h_ok) ? -INFINITY : sink_log2(p.sink, h));
-    const float l2_h = nm.lse2;
-    const float wsc = w_own * nm.scale;
-    constexpr int kOwn = 32 / TG;
-    v4f* const mrg = (v4f*)s_big;  // [HT][TG][32 slices][64 lanes]
-    auto slot = [&](int src, int dt) -> v4f* { return mrg + (((ht * TG + src) * 32 + dt) * 64 + lane); };
-#pragma unroll
-    for (int dt = 0; dt < 32; ++dt)
-      if (dt / kOwn != tg) *slot(tg, dt) = O[dt] * wsc;
-    // this wave's heads' lse (one token group writes it)
-    if (tg == 0 && g == 0 && h_ok) {
-      if (split) p.part_lse[(int64_t)unit * p.H + h] = l2_h;
-      else if (p.lse) p.lse[(int64_t)row * p.H + h] = l2_h * kLn2;
-    }
-    __syncthreads();
-    // owner: slice dt of head t holds dims 16 dt + 4 g + [0..3]
-    auto finish = [&](auto own) {
-      constexpr int q = decltype(own)::value;
-#pragma unroll
-      for (int j = 0; j < kOwn; ++j) {
-        const int dt = q * kOwn + j;
-        v4f acc = O[dt] * wsc;
-#pragma unroll
-        for (int src = 0; src < TG; ++src)
-          if (src != q) acc += *slot(src, dt);
-        if (!h_ok) continue;
-        if (split) {
-          st_half4(p.part_o + ((int64_t)unit * p.H + h) * kLat + 16 * dt + 4 * g, acc);
-        } else {
-          const uint32_t w0 = f32_to_bf16_rne(acc.x) | ((uint32_t)f32_to_bf16_rne(acc.y) << 16);
-          const uint32_t w1 = f32_to_bf16_rne(acc.z) | ((uint32_t)f32_to_bf16_rne(acc.w) << 16);
-          *(v2i*)(p.out + row * p.o_st + h * p.o_sh + 16 * dt + 4 * g) = v2i{(int)w0, (int)w1};
-        }
-      }
-    };
-    if (tg == 0) finish(std::integral_constant<int, 0>{});
-    else if (tg == 1) finish(std::integral_constant<int, 1 % TG>{});
-    else if (tg == 2) finish(std::integral_constant<int, 2 % TG>{});
-    else finish(std::integral_constant<int, 3 % TG>{});
   }
 }
 
@@ -1143,14 +724,6 @@ hipError_t launch_plan(const PlanParams& p, bool sort, Events ev, hipStream_t s)
     return hipGetLastError();
   }
   return hipSuccess;
-}
-
-template <int HT, int TG>
-static hipError_t launch_fwd_t(const FwdParams& p, Events ev, hipStream_t s) {
-  const int64_t blocks = xcd_grid(p.T, p.S);
-  hipExtLaunchKernelGGL((smla_fwd_kernel<HT, TG>), dim3((unsigned)blocks), dim3(FwdCfg<HT, TG>::kThreads), 0, s,
-                        ev.start, ev.stop, 0, p);
-  return hipGetLastError();
 }
 
 hipError_t launch_fwd(const FwdParams& p, Events ev, hipStream_t s) {
