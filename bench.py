@@ -41,13 +41,18 @@ METRIC = "gathered KV GB/s and query-rows/s (sparse MLA fwd, top-k 2048); % HBM 
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 RECORD_BYTES = 656
-KERNEL_SRC = os.path.join(ROOT, "sparse_mla_decode_fp8_amd", "csrc", "smla_kernels.hip")
+KERNEL_SRCS = [os.path.join(ROOT, "sparse_mla_decode_fp8_amd", "csrc", f)
+               for f in ("smla_kernels.hip", "smla_wide.hip", "smla_device.h", "smla_internal.h")]
 COUNTERS = os.path.join(ROOT, "profiles", "fwd_decode_T64_H16_counters.txt")
 
 
 def kernel_sha() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """First 16 hex digits of the SHA-256 of the kernel sources, concatenated."""
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def read_traffic(config_name: str):
@@ -400,9 +405,7 @@ def _fwd_kernel_name(H: int) -> str:
     """The forward kernel the library launches for H heads."""
     if H <= 16:
         return "smla_fwd16_kernel"
-    ht = (H + 15) // 16
-    tg = 1 if ht >= 3 else 4 // ht
-    return f"smla_fwd_kernel<{ht}, {tg}>"
+    return "smla_fwdw_kernel<2>" if H <= 32 else "smla_fwdw_kernel<4>"
 
 
 def _split_of(smla, w) -> int:

@@ -106,10 +106,31 @@ __device__ __forceinline__ v8h cvt8_f16(v2i w) {
 // Split partials of the output are stored as f16: a normalised partial is a
 // convex combination of V values, |V| <= 448 * 2^7 = 57344, so it fits f16's
 // range, and its 11-bit precision is finer than the bf16 of the result.
-__device__ __forceinline__ void st_half4(uint16_t* dst, v4f v) {
-  // nontemporal: the combine reads the partials once, later; nothing dirty is
-  // left in L2 for the end-of-kernel write-back
-  __builtin_nontemporal_store(v4h{(_Float16)v.x, (_Float16)v.y, (_Float16)v.z, (_Float16)v.w}, (v4h*)dst);
+//
+// Partial layout (the workspace's own): within each 64-dim block of a head,
+// the 4-dim pieces are stored in the order the MFMA accumulators hold them
+// per lane: dims 16 dt + 4 g + [0..3] at position 16 g + 4 dt + [0..3].  A
+// lane's 16 dims are then contiguous (32 B), and the combine, which reads
+// position 4x .. 4x+3 in thread x, maps it back with part_dim().
+__device__ __forceinline__ int part_dim(int pos) {  // dim held at a partial position
+  return (pos & ~63) | (((pos >> 2) & 3) << 4) | (((pos >> 4) & 3) << 2) | (pos & 3);
+}
+// One lane's four accumulator pieces (dims 16 dt + 4 g + [0..3], dt = 0..3) of
+// one head, normalised by `scale`, as f16 at block + 16 g.  Nontemporal: the
+// combine reads the partials once, later, and nothing dirty is left in L2 for
+// the end-of-kernel write-back.
+__device__ __forceinline__ void st_part16(uint16_t* block, int g, const v4f o[4], float scale) {
+  typedef _Float16 v8hh __attribute__((ext_vector_type(8)));
+  v8hh a, b;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    a[i] = (_Float16)(o[0][i] * scale);
+    a[4 + i] = (_Float16)(o[1][i] * scale);
+    b[i] = (_Float16)(o[2][i] * scale);
+    b[4 + i] = (_Float16)(o[3][i] * scale);
+  }
+  __builtin_nontemporal_store(a, (v8hh*)(block + 16 * g));
+  __builtin_nontemporal_store(b, (v8hh*)(block + 16 * g + 8));
 }
 __device__ __forceinline__ v4f half4_to_f32(v2i raw) {
   const v4h hv = __builtin_bit_cast(v4h, raw);

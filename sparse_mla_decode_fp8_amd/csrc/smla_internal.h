@@ -51,7 +51,7 @@ struct FwdParams {
   int32_t scan;        // no plan and has_invalid: each block finds its row's last entry >= 0
   int32_t stride;      // > 0: no plan and every slice may start at row * stride (a guess the kernel checks)
   const int32_t* order;      // nullable: rows in their own order
-  uint16_t* part_o;    // f16 bits [T*S, H, 512] when S > 1
+  uint16_t* part_o;    // f16 bits [T*S, H, 512] when S > 1 (dims permuted in 64-dim blocks: part_dim)
   float* part_lse;     // [T*S, H]  (log2 units) when S > 1
   KeyMode km;
   const uint8_t* pool[2];     // paged: page 0 of each pool

@@ -391,13 +391,13 @@ __global__ __launch_bounds__(nw::kThreads, 1) void smla_fwdw_kernel(FwdParams p)
       else if (p.lse) p.lse[(int64_t)row * H + h] = nm.lse2 * kLn2;
     }
     if (h_ok) {
+      if (split) {
+        st_part16(p.part_o + ((int64_t)unit * H + h) * kLat + 64 * w, g, O[j], nm.scale);
+      } else {
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        const v4f acc = O[j][dt] * nm.scale;
-        const int d = 64 * w + 16 * dt + 4 * g;
-        if (split) {
-          st_half4(p.part_o + ((int64_t)unit * H + h) * kLat + d, acc);
-        } else {
+        for (int dt = 0; dt < 4; ++dt) {
+          const v4f acc = O[j][dt] * nm.scale;
+          const int d = 64 * w + 16 * dt + 4 * g;
           const uint32_t w0 = f32_to_bf16_rne(acc.x) | ((uint32_t)f32_to_bf16_rne(acc.y) << 16);
           const uint32_t w1 = f32_to_bf16_rne(acc.z) | ((uint32_t)f32_to_bf16_rne(acc.w) << 16);
           *(v2i*)(p.out + row * p.o_st + h * p.o_sh + d) = v2i{(int)w0, (int)w1};
