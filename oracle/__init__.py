@@ -16,7 +16,13 @@ Sources (cited by page title and section, never by line):
   [K2-back page] vLLM API page "vllm.models.deepseek_v41.amd.mono.attention.back":
                  module docstring (split / combine stages), ``stage_combine``
                  (merge of chunk partials by their max and sum, the sink folded
-                 in) and ``key_rec`` (paged two-pool key addressing).
+                 in) and ``key_rec`` (paged two-pool key addressing); for the
+                 V4.1 key record and the fused epilogue also ``stage_split``
+                 and the bf16 / inverse GPT-J rotation / MXFP8 of
+                 ``stage_combine`` (oracle.v41).
+  [OCP MX]       OCP Microscaling (MX) v1.0: E8M0 shared scales and the shared
+                 exponent rule of MXFP8 (E4M3 elements), the reading taken
+                 for the page's unspecified "MXFP8".
   [OCP FP8]      OCP 8-bit floating point specification, E4M3 encoding
                  (the format the FlyDSL page's writer rule with its 448 bound
                  implies), with round-to-nearest-even conversion.
@@ -43,6 +49,19 @@ from .paged import (  # noqa: F401
     gather_records,
     row_attention_sink,
     sparse_mla_fwd_paged,
+)
+from .v41 import (  # noqa: F401
+    decode_v41,
+    resolve_v41,
+    gather_v41,
+    attention_v41,
+    sparse_mla_fwd_v41,
+    bf16_round,
+    inverse_rope_gptj,
+    mx_exponent,
+    mxfp8_quantize,
+    mxfp8_dequantize,
+    v41_epilogue,
 )
 from .writer import (  # noqa: F401
     pow2ceil,
