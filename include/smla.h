@@ -189,6 +189,74 @@ int sparse_mla_fwd_paged(const void* q, int64_t q_stride_t, int64_t q_stride_h,
                          void* stream);
 
 /*
+ * The DeepSeek V4.1 key record and its fused output epilogue (K2-back page:
+ * "key_rec" for the layout, "stage_split" for the attention, "stage_combine"
+ * for the merge, the sink and the epilogue).
+ *
+ * A key is 576 data bytes -- 448 e4m3 (OCP E4M3FN) "nope" values, then 64
+ * bf16 rope values -- and 8 scale bytes, of which byte c (c < 7) is the E8M0
+ * scale 2^(byte - 127) of nope dims 64c .. 64c+63.  K = [nope * scale, rope]
+ * (512 dims) and V is the same 512 values.  Keys live in two paged pools
+ * (smla_kv_pool, entries as in sparse_mla_fwd_paged): a page of R =
+ * page_records keys holds their data (R x 576 bytes) and then their scale
+ * words (R x 8 bytes), so key slot s is at
+ *   data:  base + (s / R) * page_stride + (s % R) * 576
+ *   scale: base + (s / R) * page_stride + R * 576 + (s % R) * 8,
+ * with page_stride >= R * 584 and a multiple of 16.
+ *
+ * The output of row r, head h (the attention result over the keys, with the
+ * sink folded in) is rounded to bf16, dims 448 + 2i and 448 + 2i + 1 (i < 32)
+ * are rotated back by the inverse GPT-J rotation at the row's position
+ * (e' = e cos_i + o sin_i, o' = o cos_i - e sin_i, cos_i = cos_sin[pos][i],
+ * sin_i = cos_sin[pos][32 + i]), and each 32 dims are quantised to MXFP8:
+ * E = floor(log2 amax) - 8 (at least -127; a zero block gives -127), the
+ * scale byte E + 127, and the E4M3 codes of the values / 2^E clamped to
+ * +-448, rounded to the nearest even.  (The pages name "vLLM's MXFP8"
+ * without its rule; this is the OCP Microscaling v1.0 one.)
+ */
+
+/* Workspace a V4.1 forward needs (every row writes partials); [1, 16] heads. */
+int64_t sparse_mla_v41_workspace_bytes(int32_t T, int32_t H, int64_t nnz);
+
+/*
+ * sparse_mla_fwd_v41 -- attention over V4.1 keys with the fused epilogue.
+ *   q          device, bf16 [T, H, 512] (the rotated query) at q + r*q_stride_t
+ *              + h*q_stride_h + d; 16-byte aligned, strides multiples of 8.
+ *   pools      host, smla_kv_pool[2] (window pool, compressed pool), as above.
+ *   indptr, indices, nnz, T, sm_scale, has_invalid, sink: as
+ *              sparse_mla_fwd_paged.  H in [1, 16].
+ *   pos        device, int32 [T]: each row's position (clamped to [0, n_pos)).
+ *   cos_sin    device, f32 [n_pos, 64]: 32 cos, then 32 sin per position.
+ *   xo         device, uint8 [T, H, 512] E4M3 codes, contiguous, 4-byte aligned.
+ *   xo_scales  device, uint8 [T, H, 16] E8M0 bytes (dims 32j .. 32j+31).
+ *   lse        device, f32 [T, H] natural log (sink included), or NULL.
+ *   y_out      device, f32 [T, H, 512] or NULL: the values the MXFP8 step
+ *              quantises (bf16-rounded output, rope dims rotated back), for
+ *              checking the epilogue.
+ *   workspace  >= sparse_mla_v41_workspace_bytes(T, H, nnz) bytes, 256-byte aligned.
+ * Preconditions the library cannot check: consumed slots lie inside their
+ * pool; scale bytes <= 134 (a scale above 2^7 is clamped to 2^7 in the P.V
+ * stage); |rope values| < 2^15 (the partials are f16).
+ * Queues the forward (partials) and the combine + epilogue on `stream` (and
+ * the plan, as sparse_mla_fwd does).  Returns SMLA_OK, or a negative status
+ * with nothing queued.
+ */
+int sparse_mla_fwd_v41(const void* q, int64_t q_stride_t, int64_t q_stride_h,
+                       const smla_kv_pool* pools,
+                       const int32_t* indptr, const int32_t* indices, int64_t nnz,
+                       int32_t T, int32_t H, float sm_scale, int32_t has_invalid,
+                       const float* sink, const int32_t* pos, const float* cos_sin, int32_t n_pos,
+                       void* xo, void* xo_scales, float* lse, float* y_out,
+                       void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * sparse_mla_mxfp8 -- test hook: the epilogue's MXFP8 quantiser (same device
+ * code) on n f32 values y (n a multiple of 64): codes uint8 [n] (8-byte
+ * aligned) and scales uint8 [n / 32], with the rule stated above.
+ */
+int sparse_mla_mxfp8(const float* y, int64_t n, void* codes, void* scales, void* stream);
+
+/*
  * sparse_mla_decode_rows -- test hook: decode records rows[0..n) of kv to f32
  * out[n, 576] (latent * scale, then rope) exactly as the forward's QK stage
  * sees them (scale applied through its exponent field), cross-checked on the

@@ -69,6 +69,21 @@ _lib.sparse_mla_fwd_paged.argtypes = [
     _vp,                    # stream
 ]
 _lib.sparse_mla_fwd_paged.restype = ctypes.c_int
+_lib.sparse_mla_v41_workspace_bytes.argtypes = [_i32, _i32, _i64]
+_lib.sparse_mla_v41_workspace_bytes.restype = _i64
+_lib.sparse_mla_fwd_v41.argtypes = [
+    _vp, _i64, _i64,        # q, strides
+    ctypes.POINTER(KvPool),  # pools[2] (host)
+    _vp, _vp, _i64,         # indptr, indices, nnz
+    _i32, _i32, _f32, _i32,  # T, H, sm_scale, has_invalid
+    _vp, _vp, _vp, _i32,    # sink, pos, cos_sin, n_pos
+    _vp, _vp, _vp, _vp,     # xo, xo_scales, lse, y_out
+    _vp, _i64,              # workspace, bytes
+    _vp,                    # stream
+]
+_lib.sparse_mla_fwd_v41.restype = ctypes.c_int
+_lib.sparse_mla_mxfp8.argtypes = [_vp, _i64, _vp, _vp, _vp]
+_lib.sparse_mla_mxfp8.restype = ctypes.c_int
 _lib.sparse_mla_cache_write.argtypes = [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp]
 _lib.sparse_mla_cache_write.restype = ctypes.c_int
 _lib.sparse_mla_decode_rows.argtypes = [_vp, _i64, _vp, _i64, _vp, _vp]
@@ -84,7 +99,8 @@ _lib.sparse_mla_profile_end.restype = ctypes.c_int
 
 EXPORTED = (
     "sparse_mla_supported", "sparse_mla_workspace_bytes", "sparse_mla_split_for", "sparse_mla_fwd",
-    "sparse_mla_fwd_paged", "sparse_mla_cache_write", "sparse_mla_decode_rows", "sparse_mla_last_error", "sparse_mla_set_option",
+    "sparse_mla_fwd_paged", "sparse_mla_v41_workspace_bytes", "sparse_mla_fwd_v41", "sparse_mla_mxfp8",
+    "sparse_mla_cache_write", "sparse_mla_decode_rows", "sparse_mla_last_error", "sparse_mla_set_option",
     "sparse_mla_profile_begin", "sparse_mla_profile_end",
 )
 
@@ -265,6 +281,89 @@ def fwd_paged(q: torch.Tensor, pools, indptr: torch.Tensor, indices: torch.Tenso
         _stream(dev))
     _check(rc)
     return out, lse
+
+
+def _pool_descs(pools, dev):
+    if len(pools) != 2:
+        raise ValueError("pools must hold two (bytes, page_stride, page_records) triples")
+    desc = (KvPool * 2)()
+    for i, pl in enumerate(pools):
+        buf, stride, per_page = pl
+        if buf is None:
+            desc[i] = KvPool(None, 0, 0)
+            continue
+        if buf.dtype != torch.uint8 or buf.dim() != 1 or not buf.is_contiguous() or buf.device != dev:
+            raise ValueError("a pool's bytes must be a contiguous 1-D uint8 tensor on q's device")
+        desc[i] = KvPool(buf.data_ptr(), int(stride), int(per_page))
+    return desc
+
+
+def v41_workspace_bytes(T: int, H: int, nnz: int) -> int:
+    n = int(_lib.sparse_mla_v41_workspace_bytes(int(T), int(H), int(nnz)))
+    if n < 0:
+        _check(n)
+    return n
+
+
+def fwd_v41(q: torch.Tensor, pools, indptr: torch.Tensor, indices: torch.Tensor, sm_scale: float,
+            pos: torch.Tensor, cos_sin: torch.Tensor, sink: Optional[torch.Tensor] = None,
+            has_invalid: bool = False, return_lse: bool = True, return_y: bool = False,
+            ws: Optional[torch.Tensor] = None):
+    """Attention over V4.1 keys (two paged pools: per page, R x 576 data bytes
+    then R x 8 scale bytes) with the fused epilogue (bf16, inverse GPT-J
+    rotation of dims 448.. at pos[r], MXFP8 of every 32 dims).
+    q bf16 [T, H <= 16, 512]; pos int32 [T]; cos_sin f32 [P, 64].
+    Returns (xo uint8 [T, H, 512] E4M3 codes, xos uint8 [T, H, 16] E8M0 bytes,
+    lse f32 [T, H] or None), plus y f32 [T, H, 512] (the values quantised)
+    when return_y."""
+    if q.dtype != torch.bfloat16 or q.dim() != 3 or q.shape[2] != 512 or q.stride(2) != 1:
+        raise ValueError("q must be bf16 [T, H, 512] with contiguous rows")
+    if indptr.dtype != torch.int32 or indices.dtype != torch.int32:
+        raise ValueError("indptr and indices must be int32")
+    dev = q.device
+    T, H, _ = q.shape
+    if indptr.numel() != T + 1:
+        raise ValueError("indptr must have T + 1 entries")
+    if pos.dtype != torch.int32 or pos.numel() != T or pos.device != dev:
+        raise ValueError("pos must be int32 [T] on q's device")
+    if cos_sin.dtype != torch.float32 or cos_sin.dim() != 2 or cos_sin.shape[1] != 64 or cos_sin.device != dev:
+        raise ValueError("cos_sin must be f32 [P, 64] on q's device")
+    desc = _pool_descs(pools, dev)
+    if sink is not None:
+        if sink.dtype != torch.float32 or sink.numel() != H or sink.device != dev:
+            raise ValueError("sink must be f32 [H] on q's device")
+        sink = sink.contiguous()
+    indptr = indptr.contiguous()
+    indices = indices.contiguous()
+    pos = pos.contiguous()
+    cos_sin = cos_sin.contiguous()
+    nnz = indices.numel()
+    xo = torch.empty(T, H, 512, dtype=torch.uint8, device=dev)
+    xos = torch.empty(T, H, 16, dtype=torch.uint8, device=dev)
+    lse = torch.empty(T, H, dtype=torch.float32, device=dev) if return_lse else None
+    y = torch.empty(T, H, 512, dtype=torch.float32, device=dev) if return_y else None
+    if ws is None:
+        ws = workspace(dev, v41_workspace_bytes(T, H, nnz))
+    _check(_lib.sparse_mla_fwd_v41(
+        _ptr(q), q.stride(0), q.stride(1), desc,
+        _ptr(indptr), _ptr(indices) if nnz else None, nnz,
+        T, H, float(sm_scale), 1 if has_invalid else 0,
+        _ptr(sink), _ptr(pos), _ptr(cos_sin), cos_sin.shape[0],
+        _ptr(xo), _ptr(xos), _ptr(lse), _ptr(y),
+        _ptr(ws), ws.numel(), _stream(dev)))
+    return (xo, xos, lse, y) if return_y else (xo, xos, lse)
+
+
+def mxfp8(y: torch.Tensor):
+    """Test hook: the epilogue's MXFP8 quantiser on f32 y [n] (n % 64 == 0)
+    -> (codes uint8 [n], E8M0 bytes uint8 [n / 32])."""
+    if y.dtype != torch.float32 or y.dim() != 1 or y.numel() % 64:
+        raise ValueError("y must be f32 [n] with n a multiple of 64")
+    y = y.contiguous()
+    codes = torch.empty(y.numel(), dtype=torch.uint8, device=y.device)
+    scales = torch.empty(y.numel() // 32, dtype=torch.uint8, device=y.device)
+    _check(_lib.sparse_mla_mxfp8(_ptr(y), y.numel(), _ptr(codes), _ptr(scales), _stream(y.device)))
+    return codes, scales
 
 
 def cache_write(latent: torch.Tensor, rope: torch.Tensor, slots: torch.Tensor, kv: torch.Tensor) -> torch.Tensor:

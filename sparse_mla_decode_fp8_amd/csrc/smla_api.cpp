@@ -96,7 +96,9 @@ struct Layout {
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-Layout layout(int32_t T, int32_t H, int64_t nnz) {
+// `partials`: the V4.1 path writes chunk partials for every row (its
+// epilogue runs in the combine), whatever the split.
+Layout layout(int32_t T, int32_t H, int64_t nnz, bool partials = false) {
   Layout L{};
   L.S = choose_split(T, H, nnz);
   size_t off = 0;
@@ -106,7 +108,7 @@ Layout layout(int32_t T, int32_t H, int64_t nnz) {
   off = align256(off + sizeof(int32_t) * (size_t)T);
   L.part_lse = off;
   L.part_o = off;
-  if (L.S > 1) {
+  if (L.S > 1 || partials) {
     off = align256(off + sizeof(float) * (size_t)T * L.S * H);
     L.part_o = off;
     off = align256(off + sizeof(uint16_t) * (size_t)T * L.S * H * 512);  // f16 partial outputs
@@ -176,27 +178,70 @@ struct KeySource {
   int32_t pool_shift[2];
 };
 
-// The forward shared by both entry points (keys already validated).
+// Pool descriptors of the paged entry points: a key's bytes in a page are
+// `key_bytes` (656 for fp8_ds_mla records, 576 + 8 for V4.1 keys).
+int parse_pools(const smla_kv_pool* pools, int64_t key_bytes, KeySource& ks) {
+  if (!pools) return fail(SMLA_EINVAL, "pools is null (two pool descriptors are required)");
+  ks.km.paged = 1;
+  for (int i = 0; i < 2; ++i) {
+    const smla_kv_pool& pl = pools[i];
+    if (!pl.base) {  // absent: its entries are not keys
+      ks.km.present[i] = 0;
+      continue;
+    }
+    const int64_t pr = pl.page_records;
+    if (pr < 1 || pr > (int64_t(1) << 30) || (pr & (pr - 1)) != 0)
+      return fail(SMLA_EINVAL, "pool %d: page_records must be a power of two in [1, 2^30], got %lld", i, (long long)pr);
+    if (!aligned(pl.base, 16)) return fail(SMLA_EINVAL, "pool %d: base must be 16-byte aligned", i);
+    if (pl.page_stride % 16 != 0 || pl.page_stride < pr * key_bytes)
+      return fail(SMLA_EINVAL, "pool %d: page_stride must be a multiple of 16 and >= page_records * %lld bytes, got %lld",
+                  i, (long long)key_bytes, (long long)pl.page_stride);
+    if (pl.page_stride > INT64_MAX / (int64_t(1) << 31))
+      return fail(SMLA_EINVAL, "pool %d: page_stride too large: %lld", i, (long long)pl.page_stride);
+    ks.km.present[i] = 1;
+    ks.pool[i] = (const uint8_t*)pl.base;
+    ks.pool_stride[i] = pl.page_stride;
+    int sh = 0;
+    while ((int64_t(1) << sh) < pr) ++sh;
+    ks.pool_shift[i] = sh;
+  }
+  return SMLA_OK;
+}
+
+// The V4.1 key record's outputs (the combine's epilogue).
+struct V41Out {
+  const int32_t* pos;
+  const float* cos_sin;
+  int32_t n_pos;
+  uint8_t* xo;
+  uint8_t* xos;
+  float* y_out;
+};
+
+// The forward shared by the entry points (keys already validated).  With
+// `v41`, the keys are V4.1 records (out unused; the combine writes xo, xos).
 int fwd_impl(const void* q, int64_t q_stride_t, int64_t q_stride_h, const KeySource& ks,
              const int32_t* indptr, const int32_t* indices, int64_t nnz,
              int32_t T, int32_t H, float sm_scale, int32_t has_invalid, const float* sink,
              void* out, int64_t o_stride_t, int64_t o_stride_h, float* lse,
-             void* workspace, int64_t workspace_bytes, void* stream) {
+             void* workspace, int64_t workspace_bytes, void* stream, const V41Out* v41 = nullptr) {
   if (!sparse_mla_supported(H)) return fail(SMLA_EUNSUPPORTED, "num_heads must be in [1, %d], got %d", SMLA_MAX_HEADS, H);
+  if (v41 && H > 16) return fail(SMLA_EUNSUPPORTED, "the V4.1 record path implements 1 to 16 heads, got %d", H);
   if (T < 0) return fail(SMLA_EINVAL, "T must be >= 0, got %d", T);
   if (nnz < 0) return fail(SMLA_EINVAL, "nnz must be >= 0, got %lld", (long long)nnz);
   if (nnz > kMaxNnz) return fail(SMLA_EINVAL, "nnz must be <= %lld (32-bit bounded index reads), got %lld", (long long)kMaxNnz, (long long)nnz);
   if (!isfinite(sm_scale)) return fail(SMLA_EINVAL, "sm_scale must be finite");
   if (T == 0) return SMLA_OK;
-  if (!q || !indptr || !out || !workspace) return fail(SMLA_EINVAL, "null pointer (q, indptr, out and workspace are required)");
+  if (!q || !indptr || !(out || v41) || !workspace) return fail(SMLA_EINVAL, "null pointer (q, indptr, out and workspace are required)");
   if (nnz > 0 && !indices) return fail(SMLA_EINVAL, "indices is null but nnz > 0");
   if (!aligned(q, 16) || !aligned(out, 16)) return fail(SMLA_EINVAL, "q and out must be 16-byte aligned");
+  if (lse && !aligned(lse, 4)) return fail(SMLA_EINVAL, "lse must be 4-byte aligned");
   if (sink && !aligned(sink, 4)) return fail(SMLA_EINVAL, "sink must be 4-byte aligned");
   if (!aligned(workspace, 256)) return fail(SMLA_EINVAL, "workspace must be 256-byte aligned");
   if (q_stride_t < 0 || q_stride_h < 0 || o_stride_t < 0 || o_stride_h < 0 ||
       (q_stride_t | q_stride_h | o_stride_t | o_stride_h) % 8 != 0)
     return fail(SMLA_EINVAL, "strides must be non-negative multiples of 8 elements");
-  const Layout L = layout(T, H, nnz);
+  const Layout L = layout(T, H, nnz, v41 != nullptr);
   if (workspace_bytes < (int64_t)L.total)
     return fail(SMLA_EWORKSPACE, "workspace has %lld bytes, needs %lld", (long long)workspace_bytes, (long long)L.total);
 
@@ -256,6 +301,16 @@ int fwd_impl(const void* q, int64_t q_stride_t, int64_t q_stride_h, const KeySou
   }
   fp.sink = sink;
   fp.hg = smla::head_groups(H);
+  if (v41) {
+    fp.sink = nullptr;  // partials never hold the sink: the combine folds it in
+    e = timed(1, [&](smla::Events ev) { return smla::launch_fwd41(fp, ev, s); });
+    if (e != hipSuccess) return hip_fail(e, "forward kernel launch");
+    smla::Combine41Params cp{T, H, L.S, sink, fp.order, fp.part_o, fp.part_lse,
+                             v41->pos, v41->cos_sin, v41->n_pos, v41->xo, v41->xos, lse, v41->y_out};
+    e = timed(2, [&](smla::Events ev) { return smla::launch_combine41(cp, ev, s); });
+    if (e != hipSuccess) return hip_fail(e, "combine kernel launch");
+    return SMLA_OK;
+  }
   e = timed(1, [&](smla::Events ev) { return smla::launch_fwd(fp, ev, s); });
   if (e != hipSuccess) return hip_fail(e, "forward kernel launch");
 
@@ -300,33 +355,51 @@ int sparse_mla_fwd_paged(const void* q, int64_t q_stride_t, int64_t q_stride_h,
                          void* workspace, int64_t workspace_bytes,
                          void* stream) {
   g_err.clear();
-  if (!pools) return fail(SMLA_EINVAL, "pools is null (two pool descriptors are required)");
   KeySource ks{};
-  ks.km.paged = 1;
-  for (int i = 0; i < 2; ++i) {
-    const smla_kv_pool& pl = pools[i];
-    if (!pl.base) {  // absent: its entries are not keys
-      ks.km.present[i] = 0;
-      continue;
-    }
-    const int64_t pr = pl.page_records;
-    if (pr < 1 || pr > (int64_t(1) << 30) || (pr & (pr - 1)) != 0)
-      return fail(SMLA_EINVAL, "pool %d: page_records must be a power of two in [1, 2^30], got %lld", i, (long long)pr);
-    if (!aligned(pl.base, 16)) return fail(SMLA_EINVAL, "pool %d: base must be 16-byte aligned", i);
-    if (pl.page_stride % 16 != 0 || pl.page_stride < pr * smla::kRecordBytes)
-      return fail(SMLA_EINVAL, "pool %d: page_stride must be a multiple of 16 and >= page_records * %d bytes, got %lld",
-                  i, smla::kRecordBytes, (long long)pl.page_stride);
-    if (pl.page_stride > INT64_MAX / (int64_t(1) << 31))
-      return fail(SMLA_EINVAL, "pool %d: page_stride too large: %lld", i, (long long)pl.page_stride);
-    ks.km.present[i] = 1;
-    ks.pool[i] = (const uint8_t*)pl.base;
-    ks.pool_stride[i] = pl.page_stride;
-    int sh = 0;
-    while ((int64_t(1) << sh) < pr) ++sh;
-    ks.pool_shift[i] = sh;
-  }
+  const int rc = parse_pools(pools, smla::kRecordBytes, ks);
+  if (rc != SMLA_OK) return rc;
   return fwd_impl(q, q_stride_t, q_stride_h, ks, indptr, indices, nnz, T, H, sm_scale, has_invalid, sink,
                   out, o_stride_t, o_stride_h, lse, workspace, workspace_bytes, stream);
+}
+
+int64_t sparse_mla_v41_workspace_bytes(int32_t T, int32_t H, int64_t nnz) {
+  if (T < 0 || nnz < 0) return fail(SMLA_EINVAL, "T and nnz must be >= 0 (T=%d nnz=%lld)", T, (long long)nnz);
+  if (H < 1 || H > 16) return fail(SMLA_EUNSUPPORTED, "the V4.1 record path implements 1 to 16 heads, got %d", H);
+  return (int64_t)layout(T, H, nnz, true).total;
+}
+
+int sparse_mla_fwd_v41(const void* q, int64_t q_stride_t, int64_t q_stride_h,
+                       const smla_kv_pool* pools,
+                       const int32_t* indptr, const int32_t* indices, int64_t nnz,
+                       int32_t T, int32_t H, float sm_scale, int32_t has_invalid,
+                       const float* sink, const int32_t* pos, const float* cos_sin, int32_t n_pos,
+                       void* xo, void* xo_scales, float* lse, float* y_out,
+                       void* workspace, int64_t workspace_bytes, void* stream) {
+  g_err.clear();
+  KeySource ks{};
+  const int rc = parse_pools(pools, 576 + 8, ks);
+  if (rc != SMLA_OK) return rc;
+  if (T > 0) {
+    if (!pos || !cos_sin || !xo || !xo_scales) return fail(SMLA_EINVAL, "null pointer (pos, cos_sin, xo and xo_scales are required)");
+    if (n_pos < 1) return fail(SMLA_EINVAL, "n_pos must be >= 1, got %d", n_pos);
+    if (!aligned(pos, 4) || !aligned(cos_sin, 4) || !aligned(xo, 4) || !aligned(y_out, 16))
+      return fail(SMLA_EINVAL, "pos, cos_sin and xo must be 4-byte aligned, y_out 16-byte aligned");
+  }
+  const V41Out v41{pos, cos_sin, n_pos, (uint8_t*)xo, (uint8_t*)xo_scales, y_out};
+  return fwd_impl(q, q_stride_t, q_stride_h, ks, indptr, indices, nnz, T, H, sm_scale, has_invalid, sink,
+                  nullptr, 0, 0, lse, workspace, workspace_bytes, stream, &v41);
+}
+
+int sparse_mla_mxfp8(const float* y, int64_t n, void* codes, void* scales, void* stream) {
+  g_err.clear();
+  if (n < 0 || n % 64 != 0) return fail(SMLA_EINVAL, "n must be a non-negative multiple of 64, got %lld", (long long)n);
+  if (n == 0) return SMLA_OK;
+  if (n / 512 + 1 > 0x7fffffff) return fail(SMLA_EINVAL, "n too large for one launch");
+  if (!y || !codes || !scales) return fail(SMLA_EINVAL, "null pointer");
+  if (!aligned(y, 4) || !aligned(codes, 8)) return fail(SMLA_EINVAL, "y must be 4-byte and codes 8-byte aligned");
+  hipError_t e = smla::launch_mxfp8(y, n, (uint8_t*)codes, (uint8_t*)scales, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "mxfp8 kernel launch");
+  return SMLA_OK;
 }
 
 int sparse_mla_decode_rows(const void* kv, int64_t n_kv, const int32_t* rows, int64_t n,

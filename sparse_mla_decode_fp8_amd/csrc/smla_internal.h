@@ -72,6 +72,22 @@ struct CombineParams {
   float* lse;
 };
 
+// The V4.1 record's combine and output epilogue (smla_v41.hip).
+struct Combine41Params {
+  int32_t T, H, S;
+  const float* sink;       // nullable: per-head sink logit [H] (natural log)
+  const int32_t* order;    // nullable: rank -> row
+  const uint16_t* part_o;  // f16 bits [T*S, H, 512] (every row has partials)
+  const float* part_lse;   // [T*S, H] log2 units
+  const int32_t* pos;      // [T] position of each row (clamped to [0, n_pos))
+  const float* cos_sin;    // [n_pos, 64]: 32 cos, then 32 sin
+  int32_t n_pos;
+  uint8_t* xo;             // [T, H, 512] E4M3 codes
+  uint8_t* xos;            // [T, H, 16] E8M0 bytes, one per 32 dims
+  float* lse;              // nullable: [T, H] natural log, sink included
+  float* y_out;            // nullable: [T, H, 512] the values quantised (checking)
+};
+
 struct CacheWriteParams {
   const uint16_t* latent;  // bf16 bits [n, 512], row stride latent_st elements
   int64_t latent_st;
@@ -107,6 +123,11 @@ hipError_t launch_fwd_wide(const FwdParams& p, Events ev, hipStream_t s);
 hipError_t zero_record_address(const uint8_t** out);
 hipError_t launch_combine(const CombineParams& p, Events ev, hipStream_t s);
 hipError_t launch_cache_write(const CacheWriteParams& p, Events ev, hipStream_t s);
+// V4.1 records (H <= 16): forward partials, then the combine + epilogue.
+hipError_t launch_fwd41(const FwdParams& p, Events ev, hipStream_t s);
+hipError_t launch_combine41(const Combine41Params& p, Events ev, hipStream_t s);
+// Test hook: MXFP8 of n f32 values (n a multiple of 64).
+hipError_t launch_mxfp8(const float* y, int64_t n, uint8_t* codes, uint8_t* scales, hipStream_t s);
 hipError_t launch_decode_rows(const uint8_t* kv, int64_t n_kv, const int32_t* rows, int64_t n,
                               float* out, hipStream_t s);
 

@@ -156,6 +156,40 @@ def test_fwd_paged_validation(b):
     assert paged([good, (None, 0, 0)], T=0) == 0
 
 
+def test_v41_validation(b):
+    """V4.1 entry points reject malformed arguments on the host: heads above
+    16, pools whose page stride cannot hold R x 584 bytes, missing pos /
+    cos_sin / outputs, n_pos < 1, misaligned y_out; the MXFP8 hook needs n a
+    multiple of 64."""
+    lib = b.lib()
+    good = (FAKE, 64 * 584, 64)
+
+    def v41(pools=(good, good), **over):
+        a = dict(q=FAKE, qst=512 * 16, qsh=512, indptr=FAKE, indices=FAKE, nnz=4, T=1, H=16,
+                 scale=0.04, inv=0, sink=None, pos=FAKE, cs=FAKE, npos=8, xo=FAKE, xos=FAKE,
+                 lse=None, y=None, ws=FAKE, wsb=1 << 40)
+        a.update(over)
+        desc = None if pools is None else (b.KvPool * 2)(*[b.KvPool(*pl) for pl in pools])
+        return lib.sparse_mla_fwd_v41(a["q"], a["qst"], a["qsh"], desc, a["indptr"], a["indices"], a["nnz"],
+                                      a["T"], a["H"], a["scale"], a["inv"], a["sink"], a["pos"], a["cs"],
+                                      a["npos"], a["xo"], a["xos"], a["lse"], a["y"], a["ws"], a["wsb"], None)
+    assert v41(H=17) == -2 and v41(H=0) == -2
+    assert v41(pools=((FAKE, 64 * 584 - 16, 64), good)) == -1      # stride below R x 584
+    assert v41(pools=((FAKE, 64 * 656, 3), good)) == -1            # R not a power of two
+    assert v41(pools=None) == -1
+    for over in (dict(pos=None), dict(cs=None), dict(xo=None), dict(xos=None), dict(npos=0),
+                 dict(y=FAKE + 4), dict(xo=FAKE + 2), dict(q=FAKE + 8)):
+        assert v41(**over) == -1, over
+        assert lib.sparse_mla_last_error()
+    assert v41(wsb=100) == -3
+    assert v41(T=0, q=None, pos=None, cs=None, xo=None, xos=None, ws=None) == 0
+    assert lib.sparse_mla_v41_workspace_bytes(4, 17, 10) == -2
+    assert lib.sparse_mla_v41_workspace_bytes(4, 16, 10) > 0
+    assert lib.sparse_mla_mxfp8(FAKE, 63, FAKE, FAKE, None) == -1
+    assert lib.sparse_mla_mxfp8(FAKE, 64, FAKE + 4, FAKE, None) == -1
+    assert lib.sparse_mla_mxfp8(None, 0, None, None, None) == 0
+
+
 def test_profile_state_machine(b):
     lib = b.lib()
     ms = (ctypes.c_double * 4)()
