@@ -152,9 +152,10 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run plain device copies of known size (counter scaling)")
-    ap.add_argument("--op", choices=("fwd", "fwd_paged", "cache_write"), default="fwd",
+    ap.add_argument("--op", choices=("fwd", "fwd_paged", "fwd_v41", "cache_write"), default="fwd",
                     help="fwd: the sparse MLA forward (default); fwd_paged: the same workload "
-                         "through two paged pools with a per-head sink; cache_write: the record writer")
+                         "through two paged pools with a per-head sink; fwd_v41: V4.1 keys (448 e4m3 + "
+                         "64 bf16 rope, E8M0 per 64) with the MXFP8 epilogue; cache_write: the record writer")
     ap.add_argument("--page-records", type=int, default=64, help="records per page (fwd_paged)")
     ap.add_argument("--records", type=int, default=65536, help="records written per call (cache_write)")
     args = ap.parse_args()
@@ -172,6 +173,8 @@ def main() -> int:
     torch.cuda.set_device(dev)
     if args.op == "cache_write":
         return bench_cache_write(args, torch, smla, dev)
+    if args.op == "fwd_v41":
+        return bench_v41(args, torch, smla, dev)
     cfg = synth.make_config(args.config)
     print(f"[bench] generating {cfg['name']}", file=sys.stderr, flush=True)
     w = synth.make_workload(args.config, device="cuda")
@@ -332,6 +335,102 @@ def paged_inputs(torch, w, per_page: int, seed: int):
     entries = torch.where(ix >= 0, entry_of[ix.clamp(min=0)], -1).to(torch.int32)
     sink = (torch.randn(w.H, generator=g, device=dev) * 3.0).float()
     return pools, entries, sink
+
+
+V41_KEY_BYTES = 576 + 8   # data + scale word per key
+
+
+def bench_v41(args, torch, smla, dev) -> int:
+    """The V4.1 key record at the decode shape of one rank: 64 rows x 16 heads,
+    2,048 distinct sorted keys per row out of 65,536, keys spread over a window
+    and a compressed pool of 64-key pages, a per-head sink, MXFP8 output.
+    Algorithmic bytes per gathered key: 576 data + 8 scale = 584."""
+    import numpy as np
+    import synth
+    import synth.v41 as sv
+    T, H, N, k, R = 64, 16, 65536, 2048, 64
+    print("[bench] generating v41 decode workload", file=sys.stderr, flush=True)
+    data, scales = sv.make_v41_keys(N, seed=41)
+    gen = torch.Generator()
+    gen.manual_seed(41)
+    rows = [np.sort(synth.distinct_uniform(gen, N, k)) for _ in range(T)]
+    rng = np.random.default_rng(41)
+    pool_of = rng.integers(0, 2, N)
+    entry_of = np.zeros(N, np.int64)
+    pools = []
+    for p in range(2):
+        ids = np.flatnonzero(pool_of == p)
+        slots = rng.permutation(len(ids)).astype(np.int64)
+        stride = R * V41_KEY_BYTES
+        npages = max((len(ids) + R - 1) // R, 1)
+        buf = np.zeros(npages * stride, np.uint8)
+        page, off = slots // R, slots % R
+        buf[(page * stride + off * 576)[:, None] + np.arange(576)[None, :]] = data[ids]
+        buf[(page * stride + R * 576 + off * 8)[:, None] + np.arange(8)[None, :]] = scales[ids]
+        entry_of[ids] = slots if p == 0 else slots - (1 << 31)
+        pools.append((torch.from_numpy(buf).to(dev), stride, R))
+    indices = torch.from_numpy(np.concatenate([entry_of[r] for r in rows]).astype(np.int32)).to(dev)
+    indptr = torch.arange(0, T * k + 1, k, dtype=torch.int32, device=dev)
+    q = sv.make_q(T, H, seed=42).to(dev)
+    cos_sin = torch.from_numpy(sv.make_cos_sin(4096)).to(dev)
+    pos = torch.from_numpy(rng.integers(0, 4096, T).astype(np.int32)).to(dev)
+    sink = (torch.randn(H, generator=gen) * 2.0).float().to(dev)
+    ws = smla.workspace(dev, smla.v41_workspace_bytes(T, H, T * k))
+    gathered = V41_KEY_BYTES * T * k
+
+    def step():
+        smla.fwd_v41(q, pools, indptr, indices, sv.sm_scale_v41(), pos, cos_sin, sink=sink, ws=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    with smla.KernelTimer(args.steps) as kt:
+        for _ in range(args.steps):
+            step()
+    torch.cuda.synchronize()
+    fwd_ms = kt.ms["fwd"] / max(kt.launches["fwd"], 1)
+    achieved = gathered / (fwd_ms * 1e-3) / 1e9
+    result = {
+        "metric": "gathered KV GB/s (V4.1 key record, MXFP8 epilogue)",
+        "value": round(gathered / (ms_per_step * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"v41_decode_T{T}_H{H}_N{N}_top{k}_page{R}", "T": T, "H": H, "N": N,
+                   "topk": k, "page_records": R, "key_bytes": V41_KEY_BYTES,
+                   "split": smla.split_for(T, H, T * k)},
+        "op": "fwd_v41",
+        "rows_per_s": round(T / (ms_per_step * 1e-3), 1),
+        "kernels_ms_per_call": {kk: round(kt.ms[kk] / max(kt.launches[kk], 1), 5) if kt.launches[kk] else 0.0
+                                for kk in kt.KINDS},
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "kernel": "smla_fwd41_kernel",
+            "bytes_per_launch": gathered,
+            "launch_ms": round(fwd_ms, 5),
+        },
+    }
+    print(json.dumps(result), flush=True)
+    return 0
 
 
 WRITE_READ_BYTES = 512 * 2 + 64 * 2 + 8   # bf16 latent + bf16 rope + int64 slot per token

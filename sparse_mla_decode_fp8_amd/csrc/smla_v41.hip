@@ -60,6 +60,7 @@ constexpr int kDataDma = 9;
 constexpr int kTileVm = kDataDma + 1;
 
 __device__ __forceinline__ int swz(int tau) { return (tau >> 2) & 3; }
+typedef short v4s16 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ void gload8(v2i& dst, uint64_t addr) {
   asm volatile("global_load_dwordx2 %0, %1, off" : "=v"(dst) : "v"(addr) : "memory");
@@ -216,8 +217,16 @@ __global__ __launch_bounds__(n41::kThreads, 1) void smla_fwd41_kernel(FwdParams 
   uint32_t pv_off[4];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) pv_off[dt] = pv_row + 16 * (4 * w + (dt ^ spv));
-  // rope P.V (wave 7): lane (t, g) reads rope dim 16dt + t of tokens 8g + j:
-  // byte 448 + 32dt + 2t = chunk 28 + 2dt + (t >> 3), byte 2(t & 7) in it
+  // rope P.V (wave 7): token 8g + 4h + t/4 of each 32-token step (swizzle
+  // (2g + h) & 3), chunk 28 + (t&3)/2 (+ 2dt), byte 8(t&1) in it
+  uint32_t rope_off[4][2];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    const int tau = 8 * g + 4 * hh + (t >> 2);
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+      rope_off[dt][hh] = tau * kRow + 16 * ((28 + 2 * dt + ((t & 3) >> 1)) ^ swz(tau)) + 8 * (t & 1);
+  }
   const v2h ones = v2h{(_Float16)1.0f, (_Float16)1.0f};
   const uint32_t mx = base + kMxOff;
   const uint32_t px = base + kPxOff;
@@ -330,8 +339,11 @@ __global__ __launch_bounds__(n41::kThreads, 1) void smla_fwd41_kernel(FwdParams 
           O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(cvt8_f16(vr[dt]), pb, O[dt], 0, 0, 0);
       }
     } else {
-      // rope dims: bf16 values read one by one (no scale fold), converted to f16
-#pragma unroll 1
+      // rope dims (bf16, no scale fold): 16-bit transposed reads, lane (t, g)
+      // loading token 32k + 8g + 4h + t/4, bytes 8(t&3) .. +7 of dims
+      // 16dt .. 16dt+15 (chunk 28 + 2dt + (t&3)/2), so that lane (i, g)
+      // receives dim 16dt + i of tokens 8g + 4h .. +3; bf16 -> f16 exactly.
+#pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int tok = 32 * k + 8 * g;
         const v8h pr = *LDSP(v8h, px + kPRow * t + 2 * tok);
@@ -339,16 +351,19 @@ __global__ __launch_bounds__(n41::kThreads, 1) void smla_fwd41_kernel(FwdParams 
         l_run = __builtin_amdgcn_fdot2(v2h{pr[2], pr[3]}, ones, l_run, false);
         l_run = __builtin_amdgcn_fdot2(v2h{pr[4], pr[5]}, ones, l_run, false);
         l_run = __builtin_amdgcn_fdot2(v2h{pr[6], pr[7]}, ones, l_run, false);
+        v4s16 rv[4][2];
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh)
+            rv[dt][hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                LDSP(v4s16, lat + 32 * kRow * k + rope_off[dt][hh]));
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
-          const int c = 28 + 2 * dt + (t >> 3);
           v8h vh;
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int tau = tok + j;
-            const uint16_t b = *LDSP(uint16_t, lat + tau * kRow + 16 * (c ^ swz(tau)) + 2 * (t & 7));
-            vh[j] = (_Float16)__builtin_bit_cast(float, (uint32_t)b << 16);
-          }
+          for (int j = 0; j < 8; ++j)
+            vh[j] = (_Float16)__builtin_bit_cast(float, (uint32_t)(uint16_t)rv[dt][j >> 2][j & 3] << 16);
           O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vh, pr, O[dt], 0, 0, 0);
         }
       }
@@ -418,6 +433,44 @@ __device__ __forceinline__ v2i mx_pack8(const float y[8], float mul) {
 // dims part_dim(8L) + [0..3] and part_dim(8L + 4) + [0..3].  Lanes with the
 // same 32-dim MXFP8 block sit at lane stride 2 (positions 16g + 4dt: dt in
 // {0, 1} or {2, 3} of one 64-dim block).
+// The merge of one (row, head): chunk statistics and partials are all loaded
+// before any is used (slots past S re-read chunk 0 and are ignored).
+template <int SMAX>
+__device__ __forceinline__ void merge41(const Combine41Params& p, int64_t u0, int h, int lane, float sink2,
+                                        float acc[8], float& M, float& L) {
+  float lc[SMAX];
+  v4i raw[SMAX];
+#pragma unroll
+  for (int c = 0; c < SMAX; ++c) {
+    const int64_t u = u0 + (c < p.S ? c : 0);
+    lc[c] = p.part_lse[u * p.H + h];
+    raw[c] = *(const v4i*)(p.part_o + (u * p.H + h) * kLat + 8 * lane);
+  }
+  M = sink2;
+#pragma unroll
+  for (int c = 0; c < SMAX; ++c)
+    if (c < p.S) M = fmax_(M, lc[c]);
+  L = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+  if (M == -INFINITY) return;
+  L = __builtin_amdgcn_exp2f(sink2 - M);
+#pragma unroll
+  for (int c = 0; c < SMAX; ++c) {
+    if (c < p.S && lc[c] != -INFINITY) {  // an empty chunk's partial was never written
+      const float wgt = __builtin_amdgcn_exp2f(lc[c] - M);
+      L += wgt;
+      const v4f lo = half4_to_f32(v2i{raw[c].x, raw[c].y});
+      const v4f hi = half4_to_f32(v2i{raw[c].z, raw[c].w});
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[i] += wgt * lo[i];
+        acc[4 + i] += wgt * hi[i];
+      }
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void smla_combine41_kernel(Combine41Params p) {
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
@@ -429,27 +482,11 @@ __global__ __launch_bounds__(256) void smla_combine41_kernel(Combine41Params p) 
   const int64_t u0 = (int64_t)row * p.S;
   // merge (K2-back page, stage_combine): M = max(max_c lse2_c, sink2)
   const float sink2 = p.sink ? p.sink[h] * 1.4426950408889634f : -INFINITY;
-  float M = sink2;
-  for (int c = 0; c < p.S; ++c) M = fmax_(M, p.part_lse[(u0 + c) * p.H + h]);
-  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  float L = 0.0f;
-  if (M != -INFINITY) {
-    L = __builtin_amdgcn_exp2f(sink2 - M);
-    for (int c = 0; c < p.S; ++c) {
-      const float lc = p.part_lse[(u0 + c) * p.H + h];
-      if (lc == -INFINITY) continue;  // an empty chunk's partial was never written
-      const float wgt = __builtin_amdgcn_exp2f(lc - M);
-      L += wgt;
-      const v4i raw = *(const v4i*)(p.part_o + ((u0 + c) * p.H + h) * kLat + 8 * lane);
-      const v4f lo = half4_to_f32(v2i{raw.x, raw.y});
-      const v4f hi = half4_to_f32(v2i{raw.z, raw.w});
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc[i] += wgt * lo[i];
-        acc[4 + i] += wgt * hi[i];
-      }
-    }
-  }
+  float acc[8], M, L;
+  if (p.S <= 4) merge41<4>(p, u0, h, lane, sink2, acc, M, L);
+  else if (p.S <= 8) merge41<8>(p, u0, h, lane, sink2, acc, M, L);
+  else if (p.S <= 16) merge41<16>(p, u0, h, lane, sink2, acc, M, L);
+  else merge41<32>(p, u0, h, lane, sink2, acc, M, L);
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
   // bf16, then the inverse GPT-J rotation of the rope dims (448 ..)
   float y[8];
