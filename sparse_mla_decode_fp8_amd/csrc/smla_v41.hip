@@ -61,6 +61,7 @@ constexpr int kTileVm = kDataDma + 1;
 
 __device__ __forceinline__ int swz(int tau) { return (tau >> 2) & 3; }
 typedef short v4s16 __attribute__((ext_vector_type(4)));
+typedef short v8s16 __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ void gload8(v2i& dst, uint64_t addr) {
   asm volatile("global_load_dwordx2 %0, %1, off" : "=v"(dst) : "v"(addr) : "memory");
@@ -86,7 +87,14 @@ __device__ __forceinline__ void key_addr41(const FwdParams& p, int e, uint64_t& 
   scale = (uint64_t)(uintptr_t)(page + ((int64_t)1 << sh) * n41::kRow + (int64_t)off * 8);
 }
 
-__global__ __launch_bounds__(n41::kThreads, 1) void smla_fwd41_kernel(FwdParams p) {
+// The fields the prologue needs first come as separate leading scalar
+// arguments (preloaded into SGPRs at wave launch); `stride` > 0 is the slice
+// stride nnz / T when there is no plan and nnz divides evenly, and lets each
+// block queue its first index tiles before indptr arrives (queued again from
+// the real start if the guess was wrong), as in the H <= 16 kernel.
+__global__ __launch_bounds__(n41::kThreads, 1) void smla_fwd41_kernel(
+    const int32_t* __restrict__ indptr, const int32_t* __restrict__ indices, const uint16_t* __restrict__ qbase,
+    int32_t T, int32_t S, uint32_t idx_bytes, int32_t stride, FwdParams p) {
   using namespace n41;
   __shared__ __attribute__((aligned(1024))) uint8_t s_lds[kBytes];
   const int tid = threadIdx.x;
@@ -96,37 +104,50 @@ __global__ __launch_bounds__(n41::kThreads, 1) void smla_fwd41_kernel(FwdParams 
   const int g = lane >> 4;
 
   int rank, chunk;
-  xcd_unit(p.S, rank, chunk);
-  if (rank >= p.T) return;
+  xcd_unit(S, rank, chunk);
+  if (rank >= T) return;
 
   const uint32_t base = lds_addr(s_lds);
+  const __amdgpu_buffer_rsrc_t irs = idx_rsrc(indices, idx_bytes);
+  auto ring_at = [&](int n) -> uint32_t { return base + kIdxRingOff + (n & (kIdxRing - 1)) * kTile * 4; };
+  // I: this wave's 16 index entries of tile n of the slice starting at b
+  // (bounded reads; positions past the row are masked in fill_table)
+  auto issue_idx_at = [&](int b, int n) {
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(ring_at(n) + 64 * w);
+    if (lane < 16) buf_dma4(irs, (uint32_t)(b + n * kTile + 16 * w + lane) * 4u, dst);
+  };
+  // speculative start (no plan: row = rank)
+  const int beg_g = rank * stride;
+  const int tiles_g = (stride + kTile - 1) / kTile;
+  const int t0_g = min(chunk * ((tiles_g + S - 1) / S), tiles_g);
+  if (stride > 0) {
+    issue_idx_at(beg_g, t0_g);
+    issue_idx_at(beg_g, t0_g + 1);
+    issue_idx_at(beg_g, t0_g + 2);
+  }
+
   const int row = p.order ? p.order[rank] : rank;
-  const int beg = p.indptr[row];
-  const int len = max(p.indptr[row + 1] - beg, 0);
+  const int beg = indptr[row];
+  const int len = max(indptr[row + 1] - beg, 0);
   const int tiles = unit_tiles<kThreads>(p, row, beg, len, kTile, (int*)(s_lds + kMxOff));
-  const int ct = (tiles + p.S - 1) / p.S;
+  const int ct = (tiles + S - 1) / S;
   const int t0 = min(chunk * ct, tiles);
   const int t1 = min(t0 + ct, tiles);
-  const int unit = row * p.S + chunk;
+  const int unit = row * S + chunk;
   const int H = p.H;
   const int h = t;
   const bool h_ok = h < H;
 
   if (t0 >= t1) {  // an empty partial: the combine gives the row out 0 and the sink's lse
+    if (stride > 0) wait_vm_all();  // the speculative index DMA lands before the block ends
     for (int hh = tid; hh < H; hh += kThreads) p.part_lse[(int64_t)unit * H + hh] = -INFINITY;
     return;
   }
 
-  const __amdgpu_buffer_rsrc_t irs = idx_rsrc(p.indices, p.idx_bytes);
   const uint64_t zero = (uint64_t)(uintptr_t)p.zero;  // 656 zero bytes: data, then a zero scale word
-  auto ring_at = [&](int n) -> uint32_t { return base + kIdxRingOff + (n & (kIdxRing - 1)) * kTile * 4; };
   auto lat_at = [&](int st) -> uint32_t { return base + kLatOff + st * kLatStage; };
   auto tab_at = [&](int n) -> uint32_t { return base + kTabOff + (n & 1) * kTile * 16; };
-  // I: this wave's 16 index entries of tile n (bounded reads)
-  auto issue_idx = [&](int n) {
-    const uint32_t dst = __builtin_amdgcn_readfirstlane(ring_at(n) + 64 * w);
-    if (lane < 16) buf_dma4(irs, (uint32_t)(beg + n * kTile + 16 * w + lane) * 4u, dst);
-  };
+  auto issue_idx = [&](int n) { issue_idx_at(beg, n); };
   // the data and scale addresses of this wave's 16 tokens of tile n (no key:
   // the zero record); returns the wave's valid-token mask
   auto fill_table = [&](int n) -> uint32_t {
@@ -144,16 +165,23 @@ __global__ __launch_bounds__(n41::kThreads, 1) void smla_fwd41_kernel(FwdParams 
   // DMA lane map: instruction i, lane L carries chunk c = 64 i + L of this
   // wave's 16 contiguous rows: token c / 36, LDS chunk position c % 36, which
   // holds source chunk (c % 36) ^ swz(token).
+  // per DMA i: the table byte offset of the lane's token (16 tk) in the high
+  // half, the source byte offset in its record in the low half (the token
+  // 16w + tk has the same swizzle as tk)
+  uint32_t dma_map[kDataDma];
+#pragma unroll
+  for (int i = 0; i < kDataDma; ++i) {
+    const uint32_t c = 64u * i + (uint32_t)lane;
+    const uint32_t tk = c / 36u;
+    dma_map[i] = ((16u * tk) << 16) | (16u * ((c - 36u * tk) ^ (uint32_t)swz((int)tk)));
+  }
   auto issue_data = [&](int n, int st) {
     const uint32_t tab = tab_at(n) + 16 * (16 * w);
     const uint32_t dst = lat_at(st) + (16 * w) * kRow;
 #pragma unroll
     for (int i = 0; i < kDataDma; ++i) {
-      const uint32_t c = 64u * i + (uint32_t)lane;
-      const uint32_t tk = c / 36u;  // the wave's token (16w + tk has the same swizzle as tk)
-      const uint64_t a = *LDSP(uint64_t, tab + 16 * tk);
-      const uint32_t src = 16u * ((c - 36u * tk) ^ (uint32_t)swz((int)tk));
-      dma16((const uint8_t*)(uintptr_t)(a + src), __builtin_amdgcn_readfirstlane(dst + 1024 * i));
+      const uint64_t a = *LDSP(uint64_t, tab + (dma_map[i] >> 16));
+      dma16((const uint8_t*)(uintptr_t)(a + (dma_map[i] & 0xFFFFu)), __builtin_amdgcn_readfirstlane(dst + 1024 * i));
     }
   };
   auto load_scales = [&](int n, v2i& sc) {
@@ -165,12 +193,15 @@ __global__ __launch_bounds__(n41::kThreads, 1) void smla_fwd41_kernel(FwdParams 
   // bf16 B operands: head t, latent K-step 2m / 2m+1 = dims 64m + 16g + [0..7]
   // / [8..15] for m < 7, rope K-step i = dims 448 + 32i + 8g + [0..7]); q of
   // heads >= H is loaded from head 0 and zeroed after.
-  issue_idx(t0);
-  if (t0 + 1 < t1) issue_idx(t0 + 1);
-  if (t0 + 2 < t1) issue_idx(t0 + 2);
+  if (!(stride > 0 && beg == beg_g && t0 == t0_g)) {
+    if (stride > 0) wait_vm_all();  // the guessed tiles land before the ring is refilled
+    issue_idx(t0);
+    if (t0 + 1 < t1) issue_idx(t0 + 1);
+    if (t0 + 2 < t1) issue_idx(t0 + 2);
+  }
   v4i qr[16];
   {
-    const uint64_t qa = (uint64_t)(uintptr_t)(p.q + row * p.q_st + (int64_t)(h_ok ? h : 0) * p.q_sh);
+    const uint64_t qa = (uint64_t)(uintptr_t)(qbase + row * p.q_st + (int64_t)(h_ok ? h : 0) * p.q_sh);
 #pragma unroll
     for (int m = 0; m < 7; ++m) {
       gload16(qr[2 * m], qa + 2 * (64 * m + 16 * g));
@@ -189,15 +220,12 @@ __global__ __launch_bounds__(n41::kThreads, 1) void smla_fwd41_kernel(FwdParams 
   v2i scA, scB;   // scale words of this lane's QK token: tiles t0, t0+2, ... / t0+1, t0+3, ...
   uint32_t vmA = fill_table(t0), vmB = 0;
   if (t0 + 1 < t1) vmB = fill_table(t0 + 1);
+  // tile t0's records alone, so that every block's first rows arrive as early
+  // as they can; tile t0+1 follows when they have.  From here on the issue
+  // order is ... L(n) I(n+3) L(n+1) I(n+4) ...
   issue_data(t0, 0);
   load_scales(t0, scA);
-  // from here on the issue order is ... L(n) I(n+3) L(n+1) I(n+4) ...
   if (t0 + 3 < t1) issue_idx(t0 + 3);
-  if (t0 + 1 < t1) {
-    issue_data(t0 + 1, 1);
-    load_scales(t0 + 1, scB);
-    if (t0 + 4 < t1) issue_idx(t0 + 4);
-  }
 
   float m_ref = -INFINITY;
   float l_run = 0.0f;
@@ -237,11 +265,27 @@ __global__ __launch_bounds__(n41::kThreads, 1) void smla_fwd41_kernel(FwdParams 
     const int left = t1 - n;
     // this wave's rows and scale word of tile n have landed (QK reads only the
     // rows this wave brought in); after them it queued at most I(n+3), L(n+1)
-    // and I(n+4)
-    if (left >= 5) wait_vm<2 + kTileVm>();
-    else if (left == 4) wait_vm<1 + kTileVm>();
-    else if (left >= 2) wait_vm<kTileVm>();
-    else wait_vm<0>();
+    // and I(n+4) -- for tile t0 only I(t0+3), then L(t0+1) and I(t0+4) here
+    if (n == t0) {
+      if (left >= 4) wait_vm<1>();
+      else wait_vm<0>();
+      if (left >= 2) {
+        issue_data(n + 1, st ^ 1);
+        load_scales(n + 1, scB);
+      }
+      if (left >= 5) {
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // ring slot t0 was read before I(t0+4) lands in it
+        issue_idx(n + 4);
+      }
+    } else if (left >= 5) {
+      wait_vm<2 + kTileVm>();
+    } else if (left == 4) {
+      wait_vm<1 + kTileVm>();
+    } else if (left >= 2) {
+      wait_vm<kTileVm>();
+    } else {
+      wait_vm<0>();
+    }
     asm volatile("" : "+v"(sc));
 
     // ---- QK: lane (t, g) gets head t, tokens 16w + 4g + r
@@ -342,7 +386,9 @@ __global__ __launch_bounds__(n41::kThreads, 1) void smla_fwd41_kernel(FwdParams 
       // rope dims (bf16, no scale fold): 16-bit transposed reads, lane (t, g)
       // loading token 32k + 8g + 4h + t/4, bytes 8(t&3) .. +7 of dims
       // 16dt .. 16dt+15 (chunk 28 + 2dt + (t&3)/2), so that lane (i, g)
-      // receives dim 16dt + i of tokens 8g + 4h .. +3; bf16 -> f16 exactly.
+      // receives dim 16dt + i of tokens 8g + 4h .. +3: the bf16 values are
+      // the A operand as stored, against P rounded to bf16 (a relative error
+      // of at most 2^-9 per weight; the softmax sum keeps the f16 P).
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int tok = 32 * k + 8 * g;
@@ -351,20 +397,19 @@ __global__ __launch_bounds__(n41::kThreads, 1) void smla_fwd41_kernel(FwdParams 
         l_run = __builtin_amdgcn_fdot2(v2h{pr[2], pr[3]}, ones, l_run, false);
         l_run = __builtin_amdgcn_fdot2(v2h{pr[4], pr[5]}, ones, l_run, false);
         l_run = __builtin_amdgcn_fdot2(v2h{pr[6], pr[7]}, ones, l_run, false);
+        v8bf pbf;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pbf[j] = (__bf16)(float)pr[j];
         v4s16 rv[4][2];
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh)
-            rv[dt][hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                LDSP(v4s16, lat + 32 * kRow * k + rope_off[dt][hh]));
+            rv[dt][hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDSP(v4s16, lat + 32 * kRow * k + rope_off[dt][hh]));
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
-          v8h vh;
-#pragma unroll
-          for (int j = 0; j < 8; ++j)
-            vh[j] = (_Float16)__builtin_bit_cast(float, (uint32_t)(uint16_t)rv[dt][j >> 2][j & 3] << 16);
-          O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vh, pr, O[dt], 0, 0, 0);
+          const v8s16 a = __builtin_shufflevector(rv[dt][0], rv[dt][1], 0, 1, 2, 3, 4, 5, 6, 7);
+          O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a), pbf, O[dt], 0, 0, 0);
         }
       }
     }
@@ -558,7 +603,8 @@ __global__ __launch_bounds__(64) void smla_mxfp8_kernel(const float* y, int64_t 
 
 hipError_t launch_fwd41(const FwdParams& p, Events ev, hipStream_t s) {
   const int64_t blocks = xcd_grid(p.T, p.S);
-  hipExtLaunchKernelGGL(smla_fwd41_kernel, dim3((unsigned)blocks), dim3(n41::kThreads), 0, s, ev.start, ev.stop, 0, p);
+  hipExtLaunchKernelGGL(smla_fwd41_kernel, dim3((unsigned)blocks), dim3(n41::kThreads), 0, s, ev.start, ev.stop, 0,
+                        p.indptr, p.indices, p.q, p.T, p.S, p.idx_bytes, p.stride, p);
   return hipGetLastError();
 }
 
