@@ -509,7 +509,7 @@ def _fwd_kernel_name(H: int) -> str:
 
 def _split_of(smla, w) -> int:
     from sparse_mla_decode_fp8_amd import binding
-    return binding.split_for(w.T, w.H, w.nnz)
+    return binding.split_for(w.T, w.H, w.nnz, bool(w.has_invalid))
 
 
 if __name__ == "__main__":

@@ -61,18 +61,21 @@ int sparse_mla_supported(int32_t num_heads);
  * H heads and nnz CSR entries needs on the current device (per-row tile
  * counts, the longest-first row order and, when rows are split, chunk
  * partials).  Returns the byte count, or a negative smla_status for invalid
- * arguments.  The workspace needs no initialisation; it must not be shared by
- * forwards that may run concurrently.
+ * arguments; the size covers either has_invalid.  The workspace needs no
+ * initialisation; it must not be shared by forwards that may run concurrently.
  */
 int64_t sparse_mla_workspace_bytes(int32_t T, int32_t H, int64_t nnz);
 
 /*
- * sparse_mla_split_for -- chunks per row (>= 1) a forward of T rows, H heads
- * and nnz entries uses on the current device: rows are split, and the chunks
- * merged by their log-sum-exp, only when there are too few rows to give every
- * compute unit work.  Negative smla_status for invalid arguments.
+ * sparse_mla_split_for -- chunks per row (>= 1) a forward of T rows, H heads,
+ * nnz entries and the given has_invalid uses on the current device: rows are
+ * split, and the chunks merged by their log-sum-exp, when there are too few
+ * rows to give every compute unit work; a padded batch (has_invalid) of about
+ * one row per compute unit is also split in two, so that its longest rows
+ * (queued first) can use two compute units.  Negative smla_status for invalid
+ * arguments.
  */
-int32_t sparse_mla_split_for(int32_t T, int32_t H, int64_t nnz);
+int32_t sparse_mla_split_for(int32_t T, int32_t H, int64_t nnz, int32_t has_invalid);
 
 /*
  * sparse_mla_fwd -- sparse MLA forward over fp8_ds_mla records.
@@ -306,6 +309,9 @@ const char* sparse_mla_last_error(void);
  * against concurrent forwards.  Names:
  *   "split"  chunks per row when rows are split (0 = automatic, 1 = never,
  *            2..SMLA_MAX_SPLIT forced); the workspace size accounts for it.
+ *   "plan"   the plan kernels (has_invalid scan, longest-first order):
+ *            0 = automatic (when units outnumber compute units), 1 = never
+ *            (each forward block scans its own slice), 2 = always.
  * Returns SMLA_OK or SMLA_EINVAL for an unknown name or value.
  */
 #define SMLA_MAX_SPLIT 32

@@ -37,7 +37,7 @@ _lib.sparse_mla_supported.argtypes = [_i32]
 _lib.sparse_mla_supported.restype = ctypes.c_int
 _lib.sparse_mla_workspace_bytes.argtypes = [_i32, _i32, _i64]
 _lib.sparse_mla_workspace_bytes.restype = _i64
-_lib.sparse_mla_split_for.argtypes = [_i32, _i32, _i64]
+_lib.sparse_mla_split_for.argtypes = [_i32, _i32, _i64, _i32]
 _lib.sparse_mla_split_for.restype = _i32
 _lib.sparse_mla_fwd.argtypes = [
     _vp, _i64, _i64,        # q, strides
@@ -131,9 +131,9 @@ def workspace_bytes(T: int, H: int, nnz: int) -> int:
     return int(n)
 
 
-def split_for(T: int, H: int, nnz: int) -> int:
+def split_for(T: int, H: int, nnz: int, has_invalid: bool = False) -> int:
     """Chunks per row the forward uses for this shape on the current device."""
-    n = _lib.sparse_mla_split_for(int(T), int(H), int(nnz))
+    n = _lib.sparse_mla_split_for(int(T), int(H), int(nnz), 1 if has_invalid else 0)
     if n < 0:
         _check(int(n))
     return int(n)

@@ -37,6 +37,7 @@ int hip_fail(hipError_t e, const char* what) {
 }
 
 int64_t g_split_override = 0;  // 0 = automatic
+int64_t g_plan_override = 0;   // 0 = automatic, 1 = never plan, 2 = always plan
 
 // Index reads use 32-bit byte offsets; the kernels read up to a few tiles past
 // a row's end, so leave headroom below 2^32 bytes.
@@ -74,15 +75,18 @@ int device_cus() {
 }
 
 // Chunks per row.  Rows are independent, so split only when there are too few
-// rows to give every CU a unit; never split below one tile per chunk.
-int choose_split(int32_t T, int32_t H, int64_t nnz) {
+// rows to give every CU a unit; never split below one tile per chunk.  With
+// padded slices (has_invalid) the rows' real lengths differ, and a batch of
+// about one row per CU is bounded by its longest rows: two chunks per row,
+// queued longest first, let those rows use two CUs.
+int choose_split(int32_t T, int32_t H, int64_t nnz, bool has_invalid = true) {
   if (g_split_override > 0) return (int)g_split_override;
   if (T <= 0) return 1;
   const int tile = smla::tile_tokens(H);
   const int64_t avg_tiles = (nnz / T + tile - 1) / tile;
   const int cus = device_cus();
   const int64_t units = (int64_t)T * smla::head_groups(H);  // unsplit units
-  if (units >= cus) return 1;
+  if (units >= cus) return (has_invalid && 2 * units <= 3 * (int64_t)cus && avg_tiles >= 2) ? 2 : 1;
   int64_t s = (cus + units - 1) / units;
   if (s > avg_tiles) s = avg_tiles;
   if (s > SMLA_MAX_SPLIT) s = SMLA_MAX_SPLIT;
@@ -97,10 +101,12 @@ struct Layout {
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // `partials`: the V4.1 path writes chunk partials for every row (its
-// epilogue runs in the combine), whatever the split.
-Layout layout(int32_t T, int32_t H, int64_t nnz, bool partials = false) {
+// epilogue runs in the combine), whatever the split.  The size is that of
+// the larger split (a padded batch's), so one workspace serves both.
+Layout layout(int32_t T, int32_t H, int64_t nnz, bool partials = false, bool has_invalid = true) {
   Layout L{};
-  L.S = choose_split(T, H, nnz);
+  const int s_max = choose_split(T, H, nnz, true);
+  L.S = choose_split(T, H, nnz, has_invalid);
   size_t off = 0;
   L.row_tiles = off;
   off = align256(off + sizeof(int32_t) * (size_t)T);
@@ -108,10 +114,10 @@ Layout layout(int32_t T, int32_t H, int64_t nnz, bool partials = false) {
   off = align256(off + sizeof(int32_t) * (size_t)T);
   L.part_lse = off;
   L.part_o = off;
-  if (L.S > 1 || partials) {
-    off = align256(off + sizeof(float) * (size_t)T * L.S * H);
+  if (s_max > 1 || partials) {
+    off = align256(off + sizeof(float) * (size_t)T * s_max * H);
     L.part_o = off;
-    off = align256(off + sizeof(uint16_t) * (size_t)T * L.S * H * 512);  // f16 partial outputs
+    off = align256(off + sizeof(uint16_t) * (size_t)T * s_max * H * 512);  // f16 partial outputs
   }
   L.total = off;
   return L;
@@ -159,10 +165,10 @@ int64_t sparse_mla_workspace_bytes(int32_t T, int32_t H, int64_t nnz) {
   return (int64_t)layout(T, H, nnz).total;
 }
 
-int32_t sparse_mla_split_for(int32_t T, int32_t H, int64_t nnz) {
+int32_t sparse_mla_split_for(int32_t T, int32_t H, int64_t nnz, int32_t has_invalid) {
   if (T < 0 || nnz < 0) return fail(SMLA_EINVAL, "T and nnz must be >= 0 (T=%d nnz=%lld)", T, (long long)nnz);
   if (!sparse_mla_supported(H)) return fail(SMLA_EUNSUPPORTED, "num_heads must be in [1, %d], got %d", SMLA_MAX_HEADS, H);
-  return choose_split(T, H, nnz);
+  return choose_split(T, H, nnz, has_invalid != 0);
 }
 
 }  // extern "C"
@@ -241,7 +247,7 @@ int fwd_impl(const void* q, int64_t q_stride_t, int64_t q_stride_h, const KeySou
   if (q_stride_t < 0 || q_stride_h < 0 || o_stride_t < 0 || o_stride_h < 0 ||
       (q_stride_t | q_stride_h | o_stride_t | o_stride_h) % 8 != 0)
     return fail(SMLA_EINVAL, "strides must be non-negative multiples of 8 elements");
-  const Layout L = layout(T, H, nnz, v41 != nullptr);
+  const Layout L = layout(T, H, nnz, v41 != nullptr, has_invalid != 0);
   if (workspace_bytes < (int64_t)L.total)
     return fail(SMLA_EWORKSPACE, "workspace has %lld bytes, needs %lld", (long long)workspace_bytes, (long long)L.total);
 
@@ -259,7 +265,9 @@ int fwd_impl(const void* q, int64_t q_stride_t, int64_t q_stride_h, const KeySou
   // order cannot shorten the slowest.  Without an order there is nothing to
   // plan: each forward block takes its row's length from indptr and, with
   // has_invalid, trims the trailing masked entries by a scan of its own row.
-  const bool sort = (int64_t)T * L.S * smla::head_groups(H) > device_cus();
+  const bool sort = g_plan_override == 1   ? false
+                    : g_plan_override == 2 ? true
+                                           : (int64_t)T * L.S * smla::head_groups(H) > device_cus();
   hipError_t e = hipSuccess;
   if (sort) {
     smla::PlanParams pp{indptr, indices, idx_bytes, T, smla::tile_tokens(H), has_invalid ? 1 : 0,
@@ -443,6 +451,11 @@ const char* sparse_mla_last_error(void) { return g_err.c_str(); }
 int sparse_mla_set_option(const char* name, int64_t value) {
   g_err.clear();
   if (!name) return fail(SMLA_EINVAL, "null option name");
+  if (!strcmp(name, "plan")) {
+    if (value < 0 || value > 2) return fail(SMLA_EINVAL, "plan must be 0, 1 or 2");
+    g_plan_override = value;
+    return SMLA_OK;
+  }
   if (!strcmp(name, "split")) {
     if (value < 0 || value > SMLA_MAX_SPLIT) return fail(SMLA_EINVAL, "split must be in [0, %d]", SMLA_MAX_SPLIT);
     g_split_override = value;

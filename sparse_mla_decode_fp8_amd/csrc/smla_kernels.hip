@@ -43,29 +43,32 @@ __device__ __attribute__((aligned(256))) uint8_t g_zero_record[kRecordBytes];
 
 // ---------------------------------------------------------------- plan
 
-// has_invalid only: one wave per row finds 1 + the last slice position whose
-// entry is >= 0 (bounded index reads) and stores the row's tile count.
+// has_invalid only: one 256-thread block per row finds 1 + the last slice
+// position whose entry is a key (bounded index reads, 2048 entries a round
+// with every load issued before any is used) and stores the row's tile count.
 __global__ __launch_bounds__(256) void smla_plan_scan_kernel(PlanParams p) {
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= p.T) return;
+  __shared__ int s_red[4];
+  const int tid = threadIdx.x;
+  const int row = blockIdx.x;
   const int beg = p.indptr[row];
   const int len = max(p.indptr[row + 1] - beg, 0);
   const __amdgpu_buffer_rsrc_t r = idx_rsrc(p.indices, p.idx_bytes);
   int lastp = 0;
-  for (int base = 0; base < len; base += 256) {
-    int v[4];
+  for (int base = 0; base < len; base += 8 * 256) {
+    int v[8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) v[j] = load_idx(r, (uint32_t)(beg + base + 4 * lane + j) * 4u);
+    for (int j = 0; j < 8; ++j) v[j] = load_idx(r, (uint32_t)(beg + base + 256 * j + tid) * 4u);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int pos = base + 4 * lane + j;
-      if (pos < len && p.km.valid(v[j])) lastp = pos + 1;
+    for (int j = 0; j < 8; ++j) {
+      const int pos = base + 256 * j + tid;
+      if (pos < len && p.km.valid(v[j])) lastp = max(lastp, pos + 1);
     }
   }
 #pragma unroll
   for (int sh = 32; sh >= 1; sh >>= 1) lastp = max(lastp, __shfl_xor(lastp, sh));
-  if (lane == 0) p.row_tiles[row] = tiles_of(lastp, p.tile);
+  if ((tid & 63) == 0) s_red[tid >> 6] = lastp;
+  __syncthreads();
+  if (tid == 0) p.row_tiles[row] = tiles_of(max(max(s_red[0], s_red[1]), max(s_red[2], s_red[3])), p.tile);
 }
 
 // One block: tile counts of every row (from the scan, or from indptr) and a
@@ -713,7 +716,7 @@ hipError_t zero_record_address(const uint8_t** out) {
 
 hipError_t launch_plan(const PlanParams& p, bool sort, Events ev, hipStream_t s) {
   if (p.has_invalid) {
-    hipExtLaunchKernelGGL(smla_plan_scan_kernel, dim3((p.T + 3) / 4), dim3(256), 0, s, ev.start,
+    hipExtLaunchKernelGGL(smla_plan_scan_kernel, dim3(p.T), dim3(256), 0, s, ev.start,
                           sort ? nullptr : ev.stop, 0, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -88,6 +88,9 @@ def test_options(b):
     assert b.lib().sparse_mla_set_option(b"split", 0) == 0
     assert b.lib().sparse_mla_set_option(b"split", 33) == -1
     assert b.lib().sparse_mla_set_option(b"nope", 1) == -1
+    for v in (1, 2, 0):
+        assert b.lib().sparse_mla_set_option(b"plan", v) == 0
+    assert b.lib().sparse_mla_set_option(b"plan", 3) == -1
 
 
 def test_decode_rows_validation(b):
