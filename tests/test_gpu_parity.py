@@ -187,6 +187,22 @@ def test_split_merge_back_to_back(smla, split, H):
         compare(out, lse, ro, rl, label=f"b2b{k} split{split} H{H}")
 
 
+@pytest.mark.parametrize("H", [16, 64])
+def test_long_rows_max_split(smla, H):
+    """Two rows of 65,536 keys each (512 tiles of 128 / 1024 of 64): the
+    automatic split reaches its cap of 32 chunks, and the combine merges 32
+    partials per row; plus a one-key row in between."""
+    rng = np.random.default_rng(40 + H)
+    N = 65536
+    sl = [rng.permutation(N), np.array([N - 1]), rng.permutation(N)]
+    w = custom(f"long_rows_H{H}", H, N, sl, seed=41 + H)
+    assert smla.split_for(w.T, w.H, w.nnz) == 32
+    note(f"long rows H={H} nnz={w.nnz}")
+    out, lse = run_gpu(w)
+    ro, rl = run_oracle(w)
+    compare(out, lse, ro, rl, label=f"long_rows_H{H}")
+
+
 def test_workspace_reuse_across_shapes(smla):
     """One uninitialised workspace serves a split forward, a larger unsplit one
     and the split one again."""
