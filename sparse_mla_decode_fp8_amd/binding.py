@@ -241,18 +241,8 @@ def fwd_paged(q: torch.Tensor, pools, indptr: torch.Tensor, indices: torch.Tenso
     key, >= 0 a window-pool slot, other negative values a compressed-pool slot
     with bit 31 set.  sink: f32 [H] natural-log logits or None."""
     _check_fwd_args(q, indptr, indices)
-    if len(pools) != 2:
-        raise ValueError("pools must hold two (bytes, page_stride, page_records) triples")
     dev = q.device
-    desc = (KvPool * 2)()
-    for i, pl in enumerate(pools):
-        buf, stride, per_page = pl
-        if buf is None:
-            desc[i] = KvPool(None, 0, 0)
-            continue
-        if buf.dtype != torch.uint8 or buf.dim() != 1 or not buf.is_contiguous() or buf.device != dev:
-            raise ValueError("a pool's bytes must be a contiguous 1-D uint8 tensor on q's device")
-        desc[i] = KvPool(buf.data_ptr(), int(stride), int(per_page))
+    desc = _pool_descs(pools, dev)
     if sink is not None:
         if sink.dtype != torch.float32 or sink.numel() != q.shape[1] or sink.device != dev:
             raise ValueError("sink must be f32 [H] on q's device")
