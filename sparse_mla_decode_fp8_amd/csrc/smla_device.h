@@ -71,13 +71,43 @@ __device__ __forceinline__ void wait_vm_all() {
 
 __device__ __forceinline__ float fmax_(float a, float b) { return __builtin_fmaxf(a, b); }
 
+// Max / sum over the four lanes t, t+16, t+32, t+48.  v_permlane16_swap
+// exchanges the odd 16-lane rows of its first operand with the even rows of
+// its second; given two copies of one value, every lane ends with its own
+// value in one result and that of lane ^ 16 in the other.  v_permlane32_swap
+// does the same for the two 32-lane halves (lane ^ 32).  Both are VALU
+// operations, with no LDS round trip.  Max and sum of the two results are
+// symmetric, so partner lanes agree bit for bit.
+// The two results pass through an empty asm before they are used as floats:
+// the ROCm 7.2 compiler otherwise folds the second result of the swap into
+// the first when both feed one float operation (f(r[0]) + f(r[1]) is emitted
+// as r[0] + r[0]).
+__device__ __forceinline__ float2 swap_pair(__attribute__((ext_vector_type(2))) uint32_t r) {
+  uint32_t a = r[0], b = r[1];
+  asm volatile("" : "+v"(a), "+v"(b));
+  return float2{__builtin_bit_cast(float, a), __builtin_bit_cast(float, b)};
+}
+__device__ __forceinline__ float2 swap16(float v) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  return swap_pair(__builtin_amdgcn_permlane16_swap(u, u, false, false));
+}
+__device__ __forceinline__ float2 swap32(float v) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  return swap_pair(__builtin_amdgcn_permlane32_swap(u, u, false, false));
+}
 __device__ __forceinline__ float xor_max(float v) {
-  v = fmax_(v, __shfl_xor(v, 16));
-  return fmax_(v, __shfl_xor(v, 32));
+  // the maxima in asm: on values the compiler cannot see it would first
+  // canonicalise each operand (two more dependent instructions per step)
+  float2 a = swap16(v);
+  asm("v_max_f32 %0, %1, %2" : "=v"(v) : "v"(a.x), "v"(a.y));
+  a = swap32(v);
+  asm("v_max_f32 %0, %1, %2" : "=v"(v) : "v"(a.x), "v"(a.y));
+  return v;
 }
 __device__ __forceinline__ float xor_sum(float v) {
-  v += __shfl_xor(v, 16);
-  return v + __shfl_xor(v, 32);
+  const float2 a = swap16(v);
+  const float2 b = swap32(a.x + a.y);
+  return b.x + b.y;
 }
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {

@@ -424,6 +424,9 @@ __global__ __launch_bounds__(n16::kThreads, 1) void smla_fwd16_kernel(
       v4i kr[8];
 #pragma unroll
       for (int m = 0; m < 8; ++m) kr[m] = *LDSP(v4i, lat + ((m & 2) ? qk_b : qk_a) + 64 * m);
+      // all eight reads are issued before the first conversion waits for one
+      // (left to itself the scheduler issues them in pairs, each pair waited for)
+      __builtin_amdgcn_sched_barrier(0);
       // two independent accumulation chains (K-steps 2m and 2m+1), summed at the end
       v4f acc0 = v4f{0, 0, 0, 0}, acc1 = v4f{0, 0, 0, 0};
       acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, sd.rp0), qrope[0], acc0, 0, 0, 0);
@@ -490,24 +493,33 @@ __global__ __launch_bounds__(n16::kThreads, 1) void smla_fwd16_kernel(
 
     // ---- PV: O^T[d, h] += V^T[d, tok] P'^T[tok, h] over the tile's 128 tokens;
     // l sums the same f16 P (so numerator and denominator share the rounding)
+    // K-step k's reads are issued before K-step k-1's conversions and MFMAs,
+    // so one K-step's LDS latency hides behind the previous one's work.
     const uint32_t vaddr = lat + pv_off;
+    v8h pr[2], sr[2];
+    v2i vr[2][4];
+    auto pv_load = [&](int k) __attribute__((always_inline)) {
+      const int tok = 32 * k + 8 * g;
+      pr[k & 1] = *LDSP(v8h, px + kPRow * t + 2 * tok);
+      sr[k & 1] = *LDSP(v8h, sx + kPRow * (w >> 1) + 2 * tok);
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+        vr[k & 1][dt] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(LDSP(v2i, vaddr + 16 * kPair * k + 16 * dt));
+    };
+    pv_load(0);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const int tok = 32 * k + 8 * g;
-      const v8h pr = *LDSP(v8h, px + kPRow * t + 2 * tok);
-      const v8h sr = *LDSP(v8h, sx + kPRow * (w >> 1) + 2 * tok);
-      const v8h pb = pr * sr;
-      l_run = __builtin_amdgcn_fdot2(v2h{pr[0], pr[1]}, ones, l_run, false);
-      l_run = __builtin_amdgcn_fdot2(v2h{pr[2], pr[3]}, ones, l_run, false);
-      l_run = __builtin_amdgcn_fdot2(v2h{pr[4], pr[5]}, ones, l_run, false);
-      l_run = __builtin_amdgcn_fdot2(v2h{pr[6], pr[7]}, ones, l_run, false);
-      v2i vr[4];
+      if (k < 3) pv_load(k + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      const v8h pk = pr[k & 1];
+      const v8h pb = pk * sr[k & 1];
+      l_run = __builtin_amdgcn_fdot2(v2h{pk[0], pk[1]}, ones, l_run, false);
+      l_run = __builtin_amdgcn_fdot2(v2h{pk[2], pk[3]}, ones, l_run, false);
+      l_run = __builtin_amdgcn_fdot2(v2h{pk[4], pk[5]}, ones, l_run, false);
+      l_run = __builtin_amdgcn_fdot2(v2h{pk[6], pk[7]}, ones, l_run, false);
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
-        vr[dt] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(LDSP(v2i, vaddr + 16 * kPair * k + 16 * dt));
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-        O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(cvt8_f16(vr[dt]), pb, O[dt], 0, 0, 0);
+        O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(cvt8_f16(vr[k & 1][dt]), pb, O[dt], 0, 0, 0);
     }
     if (left == 1) return;  // the last tile: nothing reuses the stage or P
 
