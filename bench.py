@@ -19,6 +19,18 @@ Figures:
                on the launch stream) against 8 TB/s HBM peak; `traffic` is the
                HBM bytes per launch from the committed rocprofv3 counter summary
                (null if that summary was taken from other kernel source)
+  timing       how the timed loops were run.  Each loop is queued behind a GPU
+               spin kernel long enough to cover the host's submission of the
+               whole loop, so its launches run back to back on the GPU, as in
+               a GPU-bound serving loop; `covered` says whether the spin did
+               cover it.  This matters for the per-kernel times: an event pair
+               per launch costs the host several times the launch itself, and
+               without the spin the GPU idles between calls and each forward
+               starts from an idle chip, whose XCDs begin the grid up to ~2 us
+               apart.
+  graph        (--graph-replays R) the op captured into a HIP graph of 20 calls
+               and replayed R times; every replay's outputs must equal the eager
+               call's bit for bit.
   cpu_baseline the fp64 CPU oracle on the same workload on this host's cores
 """
 
@@ -141,6 +153,119 @@ def _cpu_model() -> str:
     return "unknown"
 
 
+class LoopTimer:
+    """Runs timed loops with their launches queued behind a GPU spin (see
+    `timing` in the module docstring)."""
+
+    def __init__(self, torch, step):
+        self.torch = torch
+        self.step = step
+        cuda = torch.cuda
+        cuda._sleep(1000)
+        a, b = cuda.Event(enable_timing=True), cuda.Event(enable_timing=True)
+        a.record()
+        cuda._sleep(2_000_000)
+        b.record()
+        cuda.synchronize()
+        self.cycles_per_ms = 2_000_000 / max(a.elapsed_time(b), 1e-3)
+        # host cost of one plain call (the queue is empty, so nothing blocks)
+        n = 20
+        cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n):
+            step()
+        self.host_us = (time.perf_counter() - t0) / n * 1e6
+        cuda.synchronize()
+        self.covered = True
+
+    def _spin(self, calls: int, factor: float):
+        """Queues a spin covering `calls` launches at `factor` x the plain host
+        cost each (+5 ms); returns the events around it and its planned ms."""
+        cuda = self.torch.cuda
+        ms = min(calls * self.host_us * factor / 1e3 + 5.0, 5000.0)
+        s0, s1 = cuda.Event(enable_timing=True), cuda.Event(enable_timing=True)
+        s0.record()
+        cuda._sleep(int(self.cycles_per_ms * ms))
+        s1.record()
+        return s0, s1
+
+    def _check(self, s0, s1, host_ms: float):
+        self.covered = self.covered and host_ms <= s0.elapsed_time(s1)
+
+    def op_ms(self, steps: int) -> float:
+        """Mean device time per call over `steps` back-to-back calls."""
+        cuda = self.torch.cuda
+        cuda.synchronize()
+        s0, s1 = self._spin(steps, 2.0)
+        e0, e1 = cuda.Event(enable_timing=True), cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record()
+        for _ in range(steps):
+            self.step()
+        e1.record()
+        host_ms = (time.perf_counter() - t0) * 1e3
+        cuda.synchronize()
+        self._check(s0, s1, host_ms)
+        return e0.elapsed_time(e1) / steps
+
+    def kernel_times(self, smla, steps: int):
+        """The library's per-launch event times over `steps` calls (a
+        KernelTimer with its .ms and .launches)."""
+        cuda = self.torch.cuda
+        cuda.synchronize()
+        with smla.KernelTimer(steps) as kt:
+            s0, s1 = self._spin(steps, 8.0)   # an event pair per launch costs the host more
+            t0 = time.perf_counter()
+            for _ in range(steps):
+                self.step()
+            host_ms = (time.perf_counter() - t0) * 1e3
+        cuda.synchronize()
+        self._check(s0, s1, host_ms)
+        return kt
+
+    def report(self) -> dict:
+        return {"queued_behind_spin": True, "covered": self.covered,
+                "host_us_per_call": round(self.host_us, 2)}
+
+
+def graph_replays(torch, step, outputs, replays: int, calls: int = 20) -> dict:
+    """The op captured `calls` times into one HIP graph and replayed; each
+    replay's outputs must equal the eager call's.  Eager calls run between the
+    replays.  Returns the mean device time per call over the replays."""
+    cuda = torch.cuda
+    step()
+    cuda.synchronize()
+    ref = [t.clone() for t in outputs]
+    side = cuda.Stream()
+    side.wait_stream(cuda.current_stream())
+    with cuda.stream(side):
+        for _ in range(3):
+            step()
+    cuda.current_stream().wait_stream(side)
+    cuda.synchronize()
+    g = cuda.CUDAGraph()
+    with cuda.graph(g):
+        for _ in range(calls):
+            step()
+    cuda.synchronize()
+    total, ok = 0.0, True
+    for _ in range(replays):
+        for t in outputs:
+            t.zero_()
+        e0, e1 = cuda.Event(enable_timing=True), cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        cuda.synchronize()
+        total += e0.elapsed_time(e1)
+        ok = ok and all(torch.equal(t, r) for t, r in zip(outputs, ref))
+        step()
+        cuda.synchronize()
+    del g
+    return {"ms_per_step": round(total / (replays * calls), 5), "replays": replays,
+            "calls_per_graph": calls, "matches_eager": ok}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -158,6 +283,8 @@ def main() -> int:
                          "64 bf16 rope, E8M0 per 64) with the MXFP8 epilogue; cache_write: the record writer")
     ap.add_argument("--page-records", type=int, default=64, help="records per page (fwd_paged)")
     ap.add_argument("--records", type=int, default=65536, help="records written per call (cache_write)")
+    ap.add_argument("--graph-replays", type=int, default=0,
+                    help="also replay the op from a captured HIP graph this many times (fwd, fwd_paged)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -202,23 +329,14 @@ def main() -> int:
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    lt = LoopTimer(torch, step)
 
     # ---- warm: K back-to-back steps
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(args.steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
-    ms_per_step = e0.elapsed_time(e1) / args.steps
+    ms_per_step = lt.op_ms(args.steps)
 
     # ---- per-kernel device time (events around each launch, on its stream)
-    with smla.KernelTimer(args.steps) as kt:
-        for _ in range(args.steps):
-            step()
-    torch.cuda.synchronize()
+    kt = lt.kernel_times(smla, args.steps)
     fwd_ms = kt.ms["fwd"] / max(kt.launches["fwd"], 1)
 
     # ---- cold: flush caches between calls
@@ -234,6 +352,11 @@ def main() -> int:
         cold.append(a.elapsed_time(b))
     cold_ms = statistics.median(cold)
     del scratch
+
+    graph = None
+    if args.graph_replays > 0:
+        print(f"[bench] graph replays ({args.graph_replays})", file=sys.stderr, flush=True)
+        graph = graph_replays(torch, step, [out, lse], args.graph_replays)
 
     if args.calibrate_copy:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(3)
@@ -277,6 +400,7 @@ def main() -> int:
         },
         "kernels_ms_per_call": {k: round(kt.ms[k] / max(kt.launches[k], 1), 5) if kt.launches[k] else 0.0
                                 for k in kt.KINDS},
+        "timing": lt.report(),
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 2),
@@ -289,6 +413,8 @@ def main() -> int:
             "launch_ms": round(fwd_ms, 5),
         },
     }
+    if graph is not None:
+        result["graph"] = graph
     if paged is not None:
         result["metric"] = METRIC + ", paged two-pool keys + sink"
         result["config"]["workload"] = cfg["name"] + f"_paged{args.page_records}_sink"
@@ -384,17 +510,9 @@ def bench_v41(args, torch, smla, dev) -> int:
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(args.steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
-    ms_per_step = e0.elapsed_time(e1) / args.steps
-    with smla.KernelTimer(args.steps) as kt:
-        for _ in range(args.steps):
-            step()
-    torch.cuda.synchronize()
+    lt = LoopTimer(torch, step)
+    ms_per_step = lt.op_ms(args.steps)
+    kt = lt.kernel_times(smla, args.steps)
     fwd_ms = kt.ms["fwd"] / max(kt.launches["fwd"], 1)
     achieved = gathered / (fwd_ms * 1e-3) / 1e9
     result = {
@@ -417,6 +535,7 @@ def bench_v41(args, torch, smla, dev) -> int:
         "rows_per_s": round(T / (ms_per_step * 1e-3), 1),
         "kernels_ms_per_call": {kk: round(kt.ms[kk] / max(kt.launches[kk], 1), 5) if kt.launches[kk] else 0.0
                                 for kk in kt.KINDS},
+        "timing": lt.report(),
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 2),
@@ -455,17 +574,9 @@ def bench_cache_write(args, torch, smla, dev) -> int:
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(args.steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
-    ms_per_step = e0.elapsed_time(e1) / args.steps
-    with smla.KernelTimer(args.steps) as kt:
-        for _ in range(args.steps):
-            step()
-    torch.cuda.synchronize()
+    lt = LoopTimer(torch, step)
+    ms_per_step = lt.op_ms(args.steps)
+    kt = lt.kernel_times(smla, args.steps)
     kms = kt.ms["cache_write"] / max(kt.launches["cache_write"], 1)
     achieved = per_call / (kms * 1e-3) / 1e9
     result = {
@@ -484,6 +595,7 @@ def bench_cache_write(args, torch, smla, dev) -> int:
         "config": {"workload": f"cache_write_N{n}", "records": n,
                    "bytes_per_token": WRITE_READ_BYTES + WRITE_WRITTEN_BYTES},
         "records_per_s": round(n / (ms_per_step * 1e-3), 1),
+        "timing": lt.report(),
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 2),

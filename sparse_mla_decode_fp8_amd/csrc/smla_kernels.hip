@@ -191,7 +191,7 @@ __device__ __forceinline__ void pin(Side& s) { asm volatile("" : "+v"(s.ksc), "+
 // real start if the guess was wrong.
 __global__ __launch_bounds__(n16::kThreads, 1) void smla_fwd16_kernel(
     const int32_t* __restrict__ indptr, const int32_t* __restrict__ indices, const uint16_t* __restrict__ qbase,
-    int32_t T, int32_t S, uint32_t idx_bytes, int32_t stride, FwdParams p) {
+    const int32_t* __restrict__ order, int32_t T, int32_t S, uint32_t idx_bytes, int32_t stride, FwdParams p) {
   using namespace n16;
   __shared__ __attribute__((aligned(1024))) uint8_t s_lds[kBytes];
 
@@ -225,7 +225,7 @@ __global__ __launch_bounds__(n16::kThreads, 1) void smla_fwd16_kernel(
     issue_idx_at(beg_g, t0_g + 2);
   }
 
-  const int row = p.order ? p.order[rank] : rank;
+  const int row = order ? order[rank] : rank;
   const int beg = indptr[row];
   const int len = max(indptr[row + 1] - beg, 0);
   const int tiles = unit_tiles<kThreads>(p, row, beg, len, kTile, (int*)(s_lds + kMxOff));
@@ -292,6 +292,31 @@ __global__ __launch_bounds__(n16::kThreads, 1) void smla_fwd16_kernel(
     gload16(s.ksc, rec + kScaleOff);
     gload16(s.rp0, rec + kRopeOff + 16 * g);
     gload16(s.rp1, rec + kRopeOff + 64 + 16 * g);
+  };
+  // Tile n's loads with every address already in registers: fill_table(n)
+  // and the table reads run while an earlier tile is processed, so that the
+  // refill after a tile only issues loads.
+  struct Next {
+    uint64_t lat[8];  // latent DMA source rows (issue_latent's a[])
+    uint64_t rec;     // the side loads' record (load_side's rec)
+    uint32_t vmask;
+  };
+  auto prep = [&](int n, Next& nx) {
+    nx.vmask = fill_table(n);
+    const uint32_t tab = tab_at(n) + 8 * (16 * w + (lane >> 5));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) nx.lat[i] = *LDSP(uint64_t, tab + 16 * i);
+    nx.rec = *LDSP(uint64_t, tab_at(n) + 8 * (16 * w + t));
+  };
+  auto issue_next = [&](const Next& nx, int st, Side& s) {
+    const uint32_t dst = lat_at(st) + 8 * w * kPair;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      dma16((const uint8_t*)(uintptr_t)(nx.lat[i] + src_chunk), __builtin_amdgcn_readfirstlane(dst + i * kPair));
+    gload16(s.ksc, nx.rec + kScaleOff);
+    gload16(s.rp0, nx.rec + kRopeOff + 16 * g);
+    gload16(s.rp1, nx.rec + kRopeOff + 64 + 16 * g);
+    s.vmask = nx.vmask;
   };
 
   // ---- prologue.  q of the row into LDS (each wave an eighth, once per
@@ -386,6 +411,7 @@ __global__ __launch_bounds__(n16::kThreads, 1) void smla_fwd16_kernel(
   const uint32_t mx = base + kMxOff;
   const uint32_t px = base + kPxOff;
   const uint32_t sx = base + kSxOff;
+  Next nx;
 
   // One tile: n, its stage st (= (n - t0) & 1) and its side registers.
   auto tile = [&](int n, int st, Side& sd) __attribute__((always_inline)) {
@@ -468,6 +494,11 @@ __global__ __launch_bounds__(n16::kThreads, 1) void smla_fwd16_kernel(
     write_p(m_ref == -INFINITY ? 0.0f : m_ref);
     // V scale of block g for token 16w + t, clamped to 2^7, as f16
     *LDSP(_Float16, sx + kPRow * g + 2 * (16 * w + t)) = (_Float16)__builtin_fminf(sd.ksc[g], kScaleCap);
+    // tile n+2's addresses, while the other waves' records may still be
+    // landing: its index tile was queued before tile n's records (which have
+    // landed), table slot n & 1 was last read by tile n's own loads, and each
+    // wave touches only its own entries of the ring and the table
+    if (left >= 3) prep(n + 2, nx);
     // every wave's records of tile n have landed (each waited for its own
     // above) and its P, scales and maxima are written
     __syncthreads();
@@ -527,11 +558,7 @@ __global__ __launch_bounds__(n16::kThreads, 1) void smla_fwd16_kernel(
     __syncthreads();
 
     // ---- tile n+2 into stage st and this side set, then index tile n+5
-    if (left >= 3) {
-      sd.vmask = fill_table(n + 2);
-      issue_latent(n + 2, st);
-      load_side(n + 2, sd);
-    }
+    if (left >= 3) issue_next(nx, st, sd);
     if (left >= 6) {
       __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // ring slot n+1 was read (fill_table) before its reload lands
       issue_idx(n + 5);
@@ -746,7 +773,7 @@ hipError_t launch_fwd(const FwdParams& p, Events ev, hipStream_t s) {
     case 1: {
       const int64_t blocks = xcd_grid(p.T, p.S);
       hipExtLaunchKernelGGL(smla_fwd16_kernel, dim3((unsigned)blocks), dim3(n16::kThreads), 0, s,
-                            ev.start, ev.stop, 0, p.indptr, p.indices, p.q, p.T, p.S, p.idx_bytes, p.stride, p);
+                            ev.start, ev.stop, 0, p.indptr, p.indices, p.q, p.order, p.T, p.S, p.idx_bytes, p.stride, p);
       return hipGetLastError();
     }
     default: return launch_fwd_wide(p, ev, s);
