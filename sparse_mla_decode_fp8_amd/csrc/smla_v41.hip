@@ -94,7 +94,7 @@ __device__ __forceinline__ void key_addr41(const FwdParams& p, int e, uint64_t& 
 // the real start if the guess was wrong), as in the H <= 16 kernel.
 __global__ __launch_bounds__(n41::kThreads, 1) void smla_fwd41_kernel(
     const int32_t* __restrict__ indptr, const int32_t* __restrict__ indices, const uint16_t* __restrict__ qbase,
-    int32_t T, int32_t S, uint32_t idx_bytes, int32_t stride, FwdParams p) {
+    const int32_t* __restrict__ order, int32_t T, int32_t S, uint32_t idx_bytes, int32_t stride, FwdParams p) {
   using namespace n41;
   __shared__ __attribute__((aligned(1024))) uint8_t s_lds[kBytes];
   const int tid = threadIdx.x;
@@ -126,7 +126,7 @@ __global__ __launch_bounds__(n41::kThreads, 1) void smla_fwd41_kernel(
     issue_idx_at(beg_g, t0_g + 2);
   }
 
-  const int row = p.order ? p.order[rank] : rank;
+  const int row = order ? order[rank] : rank;
   const int beg = indptr[row];
   const int len = max(indptr[row + 1] - beg, 0);
   const int tiles = unit_tiles<kThreads>(p, row, beg, len, kTile, (int*)(s_lds + kMxOff));
@@ -297,6 +297,8 @@ __global__ __launch_bounds__(n41::kThreads, 1) void smla_fwd41_kernel(
       for (int m = 0; m < 7; ++m) kr[m] = *LDSP(v4i, lat + qk_row + 16 * ((4 * m + g) ^ sq));
       const v4i rp0 = *LDSP(v4i, lat + qk_row + 16 * ((28 + g) ^ sq));
       const v4i rp1 = *LDSP(v4i, lat + qk_row + 16 * ((32 + g) ^ sq));
+      // all nine reads are issued before the first conversion waits for one
+      __builtin_amdgcn_sched_barrier(0);
       v4f acc0 = v4f{0, 0, 0, 0}, acc1 = v4f{0, 0, 0, 0};
       acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, rp0), qk_b[14], acc0, 0, 0, 0);
       acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, rp1), qk_b[15], acc1, 0, 0, 0);
@@ -342,6 +344,12 @@ __global__ __launch_bounds__(n41::kThreads, 1) void smla_fwd41_kernel(
         *LDSP(_Float16, sx + kPRow * (g + 4) + 2 * (16 * w + t)) = (_Float16)__builtin_fminf(e8m0_f32(b1), kScaleCap);
       }
     }
+    // tile n+2's table, while the other waves' rows may still be landing: its
+    // index tile was queued before tile n's rows (which have landed), table
+    // slot n & 1 was last read by tile n's own loads, and each wave touches
+    // only its own entries of the ring and the table
+    uint32_t vm_next = 0;
+    if (left >= 3) vm_next = fill_table(n + 2);
     __syncthreads();
 
     // ---- tile max of head t over all waves; lazy reference move
@@ -418,7 +426,7 @@ __global__ __launch_bounds__(n41::kThreads, 1) void smla_fwd41_kernel(
     __syncthreads();  // every wave is done with stage st, P, the scales and the maxima
     // ---- tile n+2 into stage st and these registers, then index tile n+5
     if (left >= 3) {
-      vmask = fill_table(n + 2);
+      vmask = vm_next;
       issue_data(n + 2, st);
       load_scales(n + 2, sc);
     }
@@ -604,7 +612,7 @@ __global__ __launch_bounds__(64) void smla_mxfp8_kernel(const float* y, int64_t 
 hipError_t launch_fwd41(const FwdParams& p, Events ev, hipStream_t s) {
   const int64_t blocks = xcd_grid(p.T, p.S);
   hipExtLaunchKernelGGL(smla_fwd41_kernel, dim3((unsigned)blocks), dim3(n41::kThreads), 0, s, ev.start, ev.stop, 0,
-                        p.indptr, p.indices, p.q, p.T, p.S, p.idx_bytes, p.stride, p);
+                        p.indptr, p.indices, p.q, p.order, p.T, p.S, p.idx_bytes, p.stride, p);
   return hipGetLastError();
 }
 
