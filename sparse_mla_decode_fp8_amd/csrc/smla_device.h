@@ -264,7 +264,11 @@ __device__ __forceinline__ Norm finish_norm(float l, float m, float sink2) {
   if (mm == -INFINITY) return Norm{0.0f, -INFINITY};
   const float a = l > 0.0f ? __builtin_amdgcn_exp2f(mo - mm) : 0.0f;
   const float L = l * a + __builtin_amdgcn_exp2f(sink2 - mm);
-  return Norm{a / L, mm + __builtin_log2f(L)};
+  // L >= 1: a non-empty row's largest weight is at least 2^kShift (the lazy
+  // reference never exceeds the running max), and a dominating sink adds 1.
+  // So the hardware reciprocal and log2 (about 1 ulp, no denormal handling
+  // needed) serve; the result is rounded to f16 or bf16 after.
+  return Norm{a * __builtin_amdgcn_rcpf(L), mm + __builtin_amdgcn_logf(L)};
 }
 __device__ __forceinline__ float sink_log2(const float* sink, int h) {
   return sink ? sink[h] * 1.4426950408889634f : -INFINITY;
