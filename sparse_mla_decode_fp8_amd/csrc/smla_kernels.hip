@@ -607,28 +607,29 @@ __global__ __launch_bounds__(n16::kThreads, 1) void smla_fwd16_kernel(
 // (chunk slots past S re-read chunk 0 and are ignored), and the f16 partials
 // are converted only after the last load.
 template <int SMAX>
-__device__ __forceinline__ void combine_row(const CombineParams& p, int row, int h) {
-  const int64_t u0 = (int64_t)row * p.S;
+__device__ __forceinline__ void combine_row(const float* __restrict__ part_lse, const uint16_t* __restrict__ part_o,
+                                            int H, int S, const CombineParams& p, int row, int h) {
+  const int64_t u0 = (int64_t)row * S;
   float lc[SMAX];
   v2i raw[SMAX];
 #pragma unroll
   for (int c = 0; c < SMAX; ++c) {
-    const int64_t u = u0 + (c < p.S ? c : 0);
-    lc[c] = p.part_lse[u * p.H + h];
-    raw[c] = *(const v2i*)(p.part_o + (u * p.H + h) * kLat + 4 * threadIdx.x);
+    const int64_t u = u0 + (c < S ? c : 0);
+    lc[c] = part_lse[u * H + h];
+    raw[c] = *(const v2i*)(part_o + (u * H + h) * kLat + 4 * threadIdx.x);
   }
   const float sink2 = p.sink ? p.sink[h] * 1.4426950408889634f : -INFINITY;
   float M = sink2;
 #pragma unroll
   for (int c = 0; c < SMAX; ++c)
-    if (c < p.S) M = fmax_(M, lc[c]);
+    if (c < S) M = fmax_(M, lc[c]);
   v4f acc = v4f{0, 0, 0, 0};
   float L = 0.0f;
   if (M != -INFINITY) {
     L = __builtin_amdgcn_exp2f(sink2 - M);
 #pragma unroll
     for (int c = 0; c < SMAX; ++c) {
-      if (c < p.S && lc[c] != -INFINITY) {  // an empty chunk's o_c was never written
+      if (c < S && lc[c] != -INFINITY) {  // an empty chunk's o_c was never written
         const float w = __builtin_amdgcn_exp2f(lc[c] - M);
         L += w;
         acc += w * half4_to_f32(raw[c]);
@@ -644,15 +645,20 @@ __device__ __forceinline__ void combine_row(const CombineParams& p, int row, int
     p.lse[(int64_t)row * p.H + h] = L > 0.0f ? (M + __builtin_log2f(L)) * kLn2 : -INFINITY;
 }
 
-__global__ __launch_bounds__(128) void smla_combine_kernel(CombineParams p) {
+// The partials, the row order and the sizes come as separate leading
+// arguments, preloaded into SGPRs at wave launch: the partial loads do not
+// wait for a scalar load of the parameter block.
+__global__ __launch_bounds__(128) void smla_combine_kernel(
+    const float* __restrict__ part_lse, const uint16_t* __restrict__ part_o, const int32_t* __restrict__ order,
+    int32_t T, int32_t H, int32_t S, CombineParams p) {
   int rank, h;
-  xcd_unit(p.H, rank, h);
-  if (rank >= p.T) return;
-  const int row = p.order ? p.order[rank] : rank;
-  if (p.S <= 4) combine_row<4>(p, row, h);
-  else if (p.S <= 8) combine_row<8>(p, row, h);
-  else if (p.S <= 16) combine_row<16>(p, row, h);
-  else combine_row<32>(p, row, h);
+  xcd_unit(H, rank, h);
+  if (rank >= T) return;
+  const int row = order ? order[rank] : rank;
+  if (S <= 4) combine_row<4>(part_lse, part_o, H, S, p, row, h);
+  else if (S <= 8) combine_row<8>(part_lse, part_o, H, S, p, row, h);
+  else if (S <= 16) combine_row<16>(part_lse, part_o, H, S, p, row, h);
+  else combine_row<32>(part_lse, part_o, H, S, p, row, h);
 }
 
 // ---------------------------------------------------------------- decode hook
@@ -782,7 +788,8 @@ hipError_t launch_fwd(const FwdParams& p, Events ev, hipStream_t s) {
 
 hipError_t launch_combine(const CombineParams& p, Events ev, hipStream_t s) {
   const int64_t blocks = xcd_grid(p.T, p.H);
-  hipExtLaunchKernelGGL(smla_combine_kernel, dim3((unsigned)blocks), dim3(128), 0, s, ev.start, ev.stop, 0, p);
+  hipExtLaunchKernelGGL(smla_combine_kernel, dim3((unsigned)blocks), dim3(128), 0, s, ev.start, ev.stop, 0,
+                        p.part_lse, p.part_o, p.order, p.T, p.H, p.S, p);
   return hipGetLastError();
 }
 

@@ -489,20 +489,21 @@ __device__ __forceinline__ v2i mx_pack8(const float y[8], float mul) {
 // The merge of one (row, head): chunk statistics and partials are all loaded
 // before any is used (slots past S re-read chunk 0 and are ignored).
 template <int SMAX>
-__device__ __forceinline__ void merge41(const Combine41Params& p, int64_t u0, int h, int lane, float sink2,
+__device__ __forceinline__ void merge41(const float* __restrict__ part_lse, const uint16_t* __restrict__ part_o,
+                                        int H, int S, int64_t u0, int h, int lane, float sink2,
                                         float acc[8], float& M, float& L) {
   float lc[SMAX];
   v4i raw[SMAX];
 #pragma unroll
   for (int c = 0; c < SMAX; ++c) {
-    const int64_t u = u0 + (c < p.S ? c : 0);
-    lc[c] = p.part_lse[u * p.H + h];
-    raw[c] = *(const v4i*)(p.part_o + (u * p.H + h) * kLat + 8 * lane);
+    const int64_t u = u0 + (c < S ? c : 0);
+    lc[c] = part_lse[u * H + h];
+    raw[c] = *(const v4i*)(part_o + (u * H + h) * kLat + 8 * lane);
   }
   M = sink2;
 #pragma unroll
   for (int c = 0; c < SMAX; ++c)
-    if (c < p.S) M = fmax_(M, lc[c]);
+    if (c < S) M = fmax_(M, lc[c]);
   L = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
@@ -510,7 +511,7 @@ __device__ __forceinline__ void merge41(const Combine41Params& p, int64_t u0, in
   L = __builtin_amdgcn_exp2f(sink2 - M);
 #pragma unroll
   for (int c = 0; c < SMAX; ++c) {
-    if (c < p.S && lc[c] != -INFINITY) {  // an empty chunk's partial was never written
+    if (c < S && lc[c] != -INFINITY) {  // an empty chunk's partial was never written
       const float wgt = __builtin_amdgcn_exp2f(lc[c] - M);
       L += wgt;
       const v4f lo = half4_to_f32(v2i{raw[c].x, raw[c].y});
@@ -524,22 +525,26 @@ __device__ __forceinline__ void merge41(const Combine41Params& p, int64_t u0, in
   }
 }
 
-__global__ __launch_bounds__(256) void smla_combine41_kernel(Combine41Params p) {
+// The partials, the row order and the sizes come as separate leading
+// arguments, preloaded into SGPRs at wave launch.
+__global__ __launch_bounds__(256) void smla_combine41_kernel(
+    const float* __restrict__ part_lse, const uint16_t* __restrict__ part_o, const int32_t* __restrict__ order,
+    int32_t T, int32_t H, int32_t S, Combine41Params p) {
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
   int rank, hq;
-  xcd_unit((p.H + 3) / 4, rank, hq);
+  xcd_unit((H + 3) / 4, rank, hq);
   const int h = 4 * hq + wv;
-  if (rank >= p.T || h >= p.H) return;
-  const int row = p.order ? p.order[rank] : rank;
-  const int64_t u0 = (int64_t)row * p.S;
+  if (rank >= T || h >= H) return;
+  const int row = order ? order[rank] : rank;
+  const int64_t u0 = (int64_t)row * S;
   // merge (K2-back page, stage_combine): M = max(max_c lse2_c, sink2)
   const float sink2 = p.sink ? p.sink[h] * 1.4426950408889634f : -INFINITY;
   float acc[8], M, L;
-  if (p.S <= 4) merge41<4>(p, u0, h, lane, sink2, acc, M, L);
-  else if (p.S <= 8) merge41<8>(p, u0, h, lane, sink2, acc, M, L);
-  else if (p.S <= 16) merge41<16>(p, u0, h, lane, sink2, acc, M, L);
-  else merge41<32>(p, u0, h, lane, sink2, acc, M, L);
+  if (S <= 4) merge41<4>(part_lse, part_o, H, S, u0, h, lane, sink2, acc, M, L);
+  else if (S <= 8) merge41<8>(part_lse, part_o, H, S, u0, h, lane, sink2, acc, M, L);
+  else if (S <= 16) merge41<16>(part_lse, part_o, H, S, u0, h, lane, sink2, acc, M, L);
+  else merge41<32>(part_lse, part_o, H, S, u0, h, lane, sink2, acc, M, L);
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
   // bf16, then the inverse GPT-J rotation of the rope dims (448 ..)
   float y[8];
@@ -618,7 +623,8 @@ hipError_t launch_fwd41(const FwdParams& p, Events ev, hipStream_t s) {
 
 hipError_t launch_combine41(const Combine41Params& p, Events ev, hipStream_t s) {
   const int64_t blocks = xcd_grid(p.T, (p.H + 3) / 4);
-  hipExtLaunchKernelGGL(smla_combine41_kernel, dim3((unsigned)blocks), dim3(256), 0, s, ev.start, ev.stop, 0, p);
+  hipExtLaunchKernelGGL(smla_combine41_kernel, dim3((unsigned)blocks), dim3(256), 0, s, ev.start, ev.stop, 0,
+                        p.part_lse, p.part_o, p.order, p.T, p.H, p.S, p);
   return hipGetLastError();
 }
 
