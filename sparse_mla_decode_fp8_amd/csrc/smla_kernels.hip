@@ -46,13 +46,15 @@ __device__ __attribute__((aligned(256))) uint8_t g_zero_record[kRecordBytes];
 // has_invalid only: one 256-thread block per row finds 1 + the last slice
 // position whose entry is a key (bounded index reads, 2048 entries a round
 // with every load issued before any is used) and stores the row's tile count.
-__global__ __launch_bounds__(256) void smla_plan_scan_kernel(PlanParams p) {
+// (indptr, indices and their size are preloaded leading arguments)
+__global__ __launch_bounds__(256) void smla_plan_scan_kernel(
+    const int32_t* __restrict__ indptr, const int32_t* __restrict__ indices, uint32_t idx_bytes, PlanParams p) {
   __shared__ int s_red[4];
   const int tid = threadIdx.x;
   const int row = blockIdx.x;
-  const int beg = p.indptr[row];
-  const int len = max(p.indptr[row + 1] - beg, 0);
-  const __amdgpu_buffer_rsrc_t r = idx_rsrc(p.indices, p.idx_bytes);
+  const int beg = indptr[row];
+  const int len = max(indptr[row + 1] - beg, 0);
+  const __amdgpu_buffer_rsrc_t r = idx_rsrc(indices, idx_bytes);
   int lastp = 0;
   for (int base = 0; base < len; base += 8 * 256) {
     int v[8];
@@ -74,19 +76,22 @@ __global__ __launch_bounds__(256) void smla_plan_scan_kernel(PlanParams p) {
 // One block: tile counts of every row (from the scan, or from indptr) and a
 // counting sort of the rows by tile count, longest first (the FlyDSL page
 // issues long rows first so the long tail starts early).
-__global__ __launch_bounds__(1024) void smla_plan_sort_kernel(PlanParams p) {
+// (the row tiles, indptr, T and has_invalid are preloaded leading arguments)
+__global__ __launch_bounds__(1024) void smla_plan_sort_kernel(
+    int32_t* __restrict__ row_tiles, const int32_t* __restrict__ indptr, int32_t T, int32_t has_invalid,
+    PlanParams p) {
   __shared__ int s_cnt[kPlanBuckets];
   __shared__ int s_wsum[kPlanBuckets / 64];
   const int tid = threadIdx.x;
   for (int i = tid; i < kPlanBuckets; i += blockDim.x) s_cnt[i] = 0;
   __syncthreads();
-  for (int r = tid; r < p.T; r += blockDim.x) {
+  for (int r = tid; r < T; r += blockDim.x) {
     int t;
-    if (p.has_invalid) {
-      t = p.row_tiles[r];
+    if (has_invalid) {
+      t = row_tiles[r];
     } else {
-      t = tiles_of(max(p.indptr[r + 1] - p.indptr[r], 0), p.tile);
-      p.row_tiles[r] = t;
+      t = tiles_of(max(indptr[r + 1] - indptr[r], 0), p.tile);
+      row_tiles[r] = t;
     }
     atomicAdd(&s_cnt[min(t, kPlanBuckets - 1)], 1);
   }
@@ -112,8 +117,8 @@ __global__ __launch_bounds__(1024) void smla_plan_sort_kernel(PlanParams p) {
     s_cnt[b] = off + incl - c;
   }
   __syncthreads();
-  for (int r = tid; r < p.T; r += blockDim.x) {
-    const int t = p.row_tiles[r];
+  for (int r = tid; r < T; r += blockDim.x) {
+    const int t = row_tiles[r];
     p.order[atomicAdd(&s_cnt[min(t, kPlanBuckets - 1)], 1)] = r;
   }
 }
@@ -762,13 +767,14 @@ hipError_t zero_record_address(const uint8_t** out) {
 hipError_t launch_plan(const PlanParams& p, bool sort, Events ev, hipStream_t s) {
   if (p.has_invalid) {
     hipExtLaunchKernelGGL(smla_plan_scan_kernel, dim3(p.T), dim3(256), 0, s, ev.start,
-                          sort ? nullptr : ev.stop, 0, p);
+                          sort ? nullptr : ev.stop, 0, p.indptr, p.indices, p.idx_bytes, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (sort) {
     hipExtLaunchKernelGGL(smla_plan_sort_kernel, dim3(1), dim3(1024), 0, s,
-                          p.has_invalid ? nullptr : ev.start, ev.stop, 0, p);
+                          p.has_invalid ? nullptr : ev.start, ev.stop, 0, p.row_tiles, p.indptr, p.T,
+                          p.has_invalid, p);
     return hipGetLastError();
   }
   return hipSuccess;
