@@ -9,7 +9,7 @@ indices[indptr[r] : indptr[r+1]], with K the 576-value decoded record, V its
 512 latent values and the logits scaled by sm_scale.  The kernel also returns
 the natural-log log-sum-exp of the scaled logits.
 
-Readings taken where the pages leave a point open (each listed in the design doc):
+Readings taken where the pages leave a point open:
   * an entry < 0 is "no key" whether or not the caller sets has_invalid
     (has_invalid only lets the kernel skip trailing tiles), so the oracle has
     no has_invalid argument;

@@ -12,7 +12,7 @@ Written from the K2-back page ("vllm.models.deepseek_v41.amd.mono.attention.back
     maximum is max(m, sink) and the sum gains exp(sink - that maximum), i.e.
     the sink acts as one more key whose logit is sink_h and whose value is 0.
 
-Readings taken (listed in the design doc):
+Readings taken where the pages leave a point open:
   * the record stays the 656-byte fp8_ds_mla record, whole, at page + offset
     * 656 (the page's layout that stores a page's scales after its data is
     part of its own V4.1 record format, not of this record);

@@ -19,7 +19,7 @@ Written from the K2-back page ("vllm.models.deepseek_v41.amd.mono.attention.back
     "vLLM's MXFP8" of every 32 values.
 Key entries, pools, the sink and empty rows are as in ``oracle.paged``.
 
-Readings taken (listed in the design doc):
+Readings taken where the pages leave a point open:
   * MXFP8 is not defined on the pages.  This is the OCP Microscaling (MX) v1.0
     rule for E4M3 elements: the block's shared scale is 2^E with
     E = floor(log2(amax)) - 8 (8 = the exponent of E4M3's largest normal,
