@@ -23,6 +23,9 @@
  *     frees or retains them.  `stream` is a hipStream_t (NULL = the null
  *     stream).  Work is queued asynchronously; no entry point synchronises
  *     the host unless stated.
+ *   - The kernels run on the stream's device (the current device for the
+ *     null stream), whatever device is current; every device pointer must be
+ *     on that device.
  *   - Every entry point returns SMLA_OK (0) or a negative smla_status.  On a
  *     negative status nothing was queued, and sparse_mla_last_error() returns
  *     a message for the calling thread.

@@ -47,15 +47,35 @@ constexpr int64_t kMaxNnz = (int64_t(1) << 30) - 4096;
 std::mutex g_zero_mu;
 const uint8_t* g_zero_ptr[64] = {};
 
-hipError_t zero_record(const uint8_t** out) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
+// The device a stream belongs to (the current device for the null stream):
+// the kernels run there, so per-device addresses are that device's.
+hipError_t stream_device(hipStream_t s, int* dev) {
+  if (!s) return hipGetDevice(dev);
+  hipDevice_t d = 0;
+  const hipError_t e = hipStreamGetDevice(s, &d);
+  if (e == hipSuccess) *dev = (int)d;
+  return e;
+}
+
+// The zero record's address on device dev (the symbol is looked up with dev
+// current, once per device; the calling thread's current device is restored).
+hipError_t zero_record(int dev, const uint8_t** out) {
   if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
   std::lock_guard<std::mutex> lk(g_zero_mu);
   if (!g_zero_ptr[dev]) {
-    e = smla::zero_record_address(&g_zero_ptr[dev]);
+    int cur = 0;
+    hipError_t e = hipGetDevice(&cur);
     if (e != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    e = smla::zero_record_address(&g_zero_ptr[dev]);
+    if (cur != dev) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) {
+      g_zero_ptr[dev] = nullptr;
+      return e;
+    }
   }
   *out = g_zero_ptr[dev];
   return hipSuccess;
@@ -64,9 +84,9 @@ hipError_t zero_record(const uint8_t** out) {
 // Compute units of the current device (queried once per device).
 std::atomic<int> g_cus[64];
 
-int device_cus() {
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 256;
+int device_cus(int dev = -1) {
+  int cus = 0;
+  if (dev < 0 && hipGetDevice(&dev) != hipSuccess) return 256;
   if (dev >= 0 && dev < 64 && (cus = g_cus[dev].load(std::memory_order_relaxed)) > 0) return cus;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
     return 256;
@@ -251,10 +271,13 @@ int fwd_impl(const void* q, int64_t q_stride_t, int64_t q_stride_h, const KeySou
   if (workspace_bytes < (int64_t)L.total)
     return fail(SMLA_EWORKSPACE, "workspace has %lld bytes, needs %lld", (long long)workspace_bytes, (long long)L.total);
 
-  const uint8_t* zero = nullptr;
-  hipError_t ez = zero_record(&zero);
-  if (ez != hipSuccess) return hip_fail(ez, "zero record lookup");
   hipStream_t s = (hipStream_t)stream;
+  int dev = 0;
+  hipError_t ez = stream_device(s, &dev);
+  if (ez != hipSuccess) return hip_fail(ez, "stream device");
+  const uint8_t* zero = nullptr;
+  ez = zero_record(dev, &zero);
+  if (ez != hipSuccess) return hip_fail(ez, "zero record lookup");
   uint8_t* ws = (uint8_t*)workspace;
   int32_t* row_tiles = (int32_t*)(ws + L.row_tiles);
   int32_t* order = (int32_t*)(ws + L.order);
@@ -267,7 +290,7 @@ int fwd_impl(const void* q, int64_t q_stride_t, int64_t q_stride_h, const KeySou
   // has_invalid, trims the trailing masked entries by a scan of its own row.
   const bool sort = g_plan_override == 1   ? false
                     : g_plan_override == 2 ? true
-                                           : (int64_t)T * L.S * smla::head_groups(H) > device_cus();
+                                           : (int64_t)T * L.S * smla::head_groups(H) > device_cus(dev);
   hipError_t e = hipSuccess;
   if (sort) {
     smla::PlanParams pp{indptr, indices, idx_bytes, T, smla::tile_tokens(H), has_invalid ? 1 : 0,
