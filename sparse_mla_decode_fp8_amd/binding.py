@@ -155,10 +155,11 @@ _ws_cache = {}
 
 
 def workspace(device: torch.device, nbytes: int) -> torch.Tensor:
-    """A device workspace of at least nbytes, reused per device.  Calls on one
-    device share it, so they must not overlap in time (they are ordered on one
-    stream in normal use)."""
-    key = (device.type, device.index)
+    """A device workspace of at least nbytes, reused per device and stream (the
+    current stream of `device`, the one the call is queued on): calls on one
+    stream are ordered, so they can share it, and calls on other streams get
+    their own."""
+    key = (device.type, device.index, torch.cuda.current_stream(device).cuda_stream)
     ws = _ws_cache.get(key)
     if ws is None or ws.numel() < nbytes:
         ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
