@@ -10,7 +10,8 @@ that wrote nothing would fail.
 
 Cases: the decode shape (split + combine), a ragged batch with masked entries
 and more units than compute units (plan scan and sort kernels), the paged
-pools with a sink, and the V4.1 record with its MXFP8 epilogue.
+pools with a sink, and the V4.1 record with its MXFP8 epilogue.  A last test
+runs two problems on two streams at once.
 """
 
 import sys
@@ -180,3 +181,48 @@ def test_graph_v41(smla):
         step()
         torch.cuda.synchronize()
     del g
+
+
+def test_concurrent_streams(smla):
+    """Two streams, each with its own workspace, run different problems with
+    their calls interleaved and no synchronisation between them; each result
+    equals that problem's result run alone, bit for bit (the library keeps no
+    state shared between calls besides what the caller passes)."""
+    N = 16384
+    a = synth.build_workload("streams_a", 32, 16, N, lambda g, r, m: synth.distinct_uniform(g, N, 700),
+                             seed=21, device="cuda")
+    rng = np.random.default_rng(22)
+    lens = rng.integers(1, 600, 280)
+
+    def rows(g, r, m):
+        s = synth.distinct_uniform(g, N, int(lens[r]))
+        return np.concatenate([s, -np.ones(600 - len(s), np.int64)])
+
+    b = synth.build_workload("streams_b", 280, 16, N, rows, seed=23, device="cuda", has_invalid=1)
+    note("concurrent streams: decode 32 x 700 keys (split + combine) and ragged 280 rows (plan kernels)")
+    outs = {}
+    for name, w, hi in (("a", a, False), ("b", b, True)):
+        o = torch.empty(w.T, w.H, 512, dtype=torch.bfloat16, device=DEV)
+        l = torch.empty(w.T, w.H, dtype=torch.float32, device=DEV)
+        ws = torch.empty(smla.workspace_bytes(w.T, w.H, w.nnz), dtype=torch.uint8, device=DEV)
+        outs[name] = (w, hi, o, l, ws)
+    ref = {}
+    for name, (w, hi, o, l, ws) in outs.items():
+        smla.fwd(w.q, w.kv, w.indptr, w.indices, w.sm_scale, has_invalid=hi, out=o, lse=l, ws=ws)
+        torch.cuda.synchronize()
+        ref[name] = (o.clone(), l.clone())
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    s1.wait_stream(torch.cuda.current_stream())
+    s2.wait_stream(torch.cuda.current_stream())
+    for name, _, _, o, l, _ in [(k, *v) for k, v in outs.items()]:
+        o.fill_(7)
+        l.fill_(7)
+    torch.cuda.synchronize()
+    for _ in range(6):
+        for name, st in (("a", s1), ("b", s2)):
+            w, hi, o, l, ws = outs[name]
+            with torch.cuda.stream(st):
+                smla.fwd(w.q, w.kv, w.indptr, w.indices, w.sm_scale, has_invalid=hi, out=o, lse=l, ws=ws)
+    torch.cuda.synchronize()
+    for name, (w, hi, o, l, ws) in outs.items():
+        assert torch.equal(o, ref[name][0]) and torch.equal(l, ref[name][1]), f"problem {name} differs"
