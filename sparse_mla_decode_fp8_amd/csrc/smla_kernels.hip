@@ -720,11 +720,12 @@ __global__ __launch_bounds__(256) void smla_cache_write_kernel(CacheWriteParams 
   const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (i >= p.n) return;
   const int lane = threadIdx.x & 63;
+  const v4i raw = *(const v4i*)(p.latent + i * p.latent_st + 8 * lane);  // 8 bf16
+  const v2i rp = lane < 16 ? *(const v2i*)(p.rope + i * p.rope_st + 4 * lane) : v2i{0, 0};
   const int64_t slot = p.slots[i];
   if (slot < 0 || slot >= p.n_kv) return;  // padding tokens; out-of-range slots are never written
   uint8_t* rec = p.kv + slot * kRecordBytes;
 
-  const v4i raw = *(const v4i*)(p.latent + i * p.latent_st + 8 * lane);  // 8 bf16
   float x[8];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
@@ -734,8 +735,16 @@ __global__ __launch_bounds__(256) void smla_cache_write_kernel(CacheWriteParams 
   float amax = 0.0f;
 #pragma unroll
   for (int k = 0; k < 8; ++k) amax = fmax_(amax, __builtin_fabsf(x[k]));
-#pragma unroll
-  for (int sh = 1; sh < 16; sh <<= 1) amax = fmax_(amax, __shfl_xor(amax, sh));
+  // max over the 16 lanes of the scale block, by DPP: quad_perm xor 1 and
+  // xor 2 (quads), row_half_mirror (lanes i <-> 7 - i: pairs the quads of a
+  // half row), row_mirror (i <-> 15 - i: pairs the half rows)
+#define SMLA_DPP_MAX(ctrl) \
+  amax = fmax_(amax, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, amax), ctrl, 0xF, 0xF, false)))
+  SMLA_DPP_MAX(0xB1);
+  SMLA_DPP_MAX(0x4E);
+  SMLA_DPP_MAX(0x141);
+  SMLA_DPP_MAX(0x140);
+#undef SMLA_DPP_MAX
   // pow2ceil of v = max(amax, 1e-4) / 448 (a positive normal f32): v itself if
   // its mantissa is zero, else the next power of two.  The f32 quotient is a
   // power of two exactly when the exact one is (amax has 8 significant bits),
@@ -752,7 +761,7 @@ __global__ __launch_bounds__(256) void smla_cache_write_kernel(CacheWriteParams 
   w1 = __builtin_amdgcn_cvt_pk_fp8_f32(x[6] * inv, x[7] * inv, w1, true);
   *(v2i*)(rec + 8 * lane) = v2i{w0, w1};
   if ((lane & 15) == 0) *(float*)(rec + kScaleOff + 4 * (lane >> 4)) = scale;
-  if (lane < 16) *(v2i*)(rec + kRopeOff + 8 * lane) = *(const v2i*)(p.rope + i * p.rope_st + 4 * lane);
+  if (lane < 16) *(v2i*)(rec + kRopeOff + 8 * lane) = rp;
 }
 
 // ---------------------------------------------------------------- launchers
