@@ -58,6 +58,11 @@ static_assert(kBytes <= 160 * 1024, "LDS budget");
 // 36 chunks) and 1 scale-word load; an index DMA besides.
 constexpr int kDataDma = 9;
 constexpr int kTileVm = kDataDma + 1;
+// q of the row is staged once per block in stage 1 (free until tile t0+1's
+// records are queued): head hh's 512 bf16 at 1040 hh, the 16-byte pad putting
+// the 16 heads a lane column reads in one instruction on distinct banks.
+constexpr int kQPitch = 2 * 512 + 16;
+static_assert(16 * kQPitch <= kLatStage, "q staging fits a stage");
 
 __device__ __forceinline__ int swz(int tau) { return (tau >> 2) & 3; }
 typedef short v4s16 __attribute__((ext_vector_type(4)));
@@ -189,33 +194,32 @@ __global__ __launch_bounds__(n41::kThreads, 1) void smla_fwd41_kernel(
     gload8(sc, a);
   };
 
-  // ---- prologue: index tiles t0 .. t0+2 and q (every wave all 16 heads, as
-  // bf16 B operands: head t, latent K-step 2m / 2m+1 = dims 64m + 16g + [0..7]
-  // / [8..15] for m < 7, rope K-step i = dims 448 + 32i + 8g + [0..7]); q of
-  // heads >= H is loaded from head 0 and zeroed after.
+  // ---- prologue: index tiles t0 .. t0+2, and q of the row into stage 1
+  // (wave w DMAs heads 2w and 2w+1, one 1 KB row each; heads >= H are not
+  // loaded and their lanes use zeros)
   if (!(stride > 0 && beg == beg_g && t0 == t0_g)) {
     if (stride > 0) wait_vm_all();  // the guessed tiles land before the ring is refilled
     issue_idx(t0);
     if (t0 + 1 < t1) issue_idx(t0 + 1);
     if (t0 + 2 < t1) issue_idx(t0 + 2);
   }
-  v4i qr[16];
+  const uint32_t q_lds = lat_at(1);
+  const int nq = (2 * w < H) + (2 * w + 1 < H);
   {
-    const uint64_t qa = (uint64_t)(uintptr_t)(qbase + row * p.q_st + (int64_t)(h_ok ? h : 0) * p.q_sh);
+    const uint16_t* qrow = qbase + row * p.q_st;
 #pragma unroll
-    for (int m = 0; m < 7; ++m) {
-      gload16(qr[2 * m], qa + 2 * (64 * m + 16 * g));
-      gload16(qr[2 * m + 1], qa + 2 * (64 * m + 16 * g + 8));
+    for (int j = 0; j < 2; ++j) {
+      const int hh = 2 * w + j;
+      if (hh < H)
+        dma16((const uint8_t*)(qrow + (int64_t)hh * p.q_sh + 8 * lane),
+              __builtin_amdgcn_readfirstlane(q_lds + kQPitch * hh));
     }
-    gload16(qr[14], qa + 2 * (kNope + 8 * g));
-    gload16(qr[15], qa + 2 * (kNope + 32 + 8 * g));
   }
-  wait_vm<0>();
-#pragma unroll
-  for (int i = 0; i < 16; ++i) asm volatile("" : "+v"(qr[i]));
-  v8bf qk_b[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) qk_b[i] = __builtin_bit_cast(v8bf, h_ok ? qr[i] : v4i{0, 0, 0, 0});
+  // this wave's index tiles have landed (its q rows, queued after them, may
+  // not have: vector memory loads complete in issue order)
+  if (nq == 2) wait_vm<2>();
+  else if (nq == 1) wait_vm<1>();
+  else wait_vm<0>();
 
   v2i scA, scB;   // scale words of this lane's QK token: tiles t0, t0+2, ... / t0+1, t0+3, ...
   uint32_t vmA = fill_table(t0), vmB = 0;
@@ -225,7 +229,32 @@ __global__ __launch_bounds__(n41::kThreads, 1) void smla_fwd41_kernel(
   // order is ... L(n) I(n+3) L(n+1) I(n+4) ...
   issue_data(t0, 0);
   load_scales(t0, scA);
+  wait_vm<kDataDma + 1>();  // this wave's q rows have landed (tile t0's rows may not)
+  __syncthreads();          // every wave's have
+  // q as bf16 B operands: head t, latent K-step 2m / 2m+1 = dims 64m + 16g +
+  // [0..7] / [8..15] for m < 7, rope K-step i = dims 448 + 32i + 8g + [0..7]
+  v8bf qk_b[16];
+  {
+    const uint32_t qr = q_lds + kQPitch * t;
+#pragma unroll
+    for (int m = 0; m < 7; ++m) {
+      v4i a = *LDSP(v4i, qr + 2 * (64 * m + 16 * g));
+      v4i b = *LDSP(v4i, qr + 2 * (64 * m + 16 * g + 8));
+      if (!h_ok) a = b = v4i{0, 0, 0, 0};
+      qk_b[2 * m] = __builtin_bit_cast(v8bf, a);
+      qk_b[2 * m + 1] = __builtin_bit_cast(v8bf, b);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      v4i a = *LDSP(v4i, qr + 2 * (kNope + 32 * i + 8 * g));
+      if (!h_ok) a = v4i{0, 0, 0, 0};
+      qk_b[14 + i] = __builtin_bit_cast(v8bf, a);
+    }
+  }
   if (t0 + 3 < t1) issue_idx(t0 + 3);
+  // every wave has read q before tile t0+1's records are queued into stage 1
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  __syncthreads();
 
   float m_ref = -INFINITY;
   float l_run = 0.0f;
