@@ -517,10 +517,13 @@ __device__ __forceinline__ v2i mx_pack8(const float y[8], float mul) {
 // {0, 1} or {2, 3} of one 64-dim block).
 // The merge of one (row, head): chunk statistics and partials are all loaded
 // before any is used (slots past S re-read chunk 0 and are ignored).
+// The rope lanes' cos / sin (4 pairs) are loaded right behind the partials,
+// so that their dependent loads (position, then table) overlap the partials'.
 template <int SMAX>
 __device__ __forceinline__ void merge41(const float* __restrict__ part_lse, const uint16_t* __restrict__ part_o,
                                         int H, int S, int64_t u0, int h, int lane, float sink2,
-                                        float acc[8], float& M, float& L) {
+                                        const Combine41Params& p, int row, bool rope, int d0, int d1,
+                                        float acc[8], float& M, float& L, float cr[4], float sr[4]) {
   float lc[SMAX];
   v4i raw[SMAX];
 #pragma unroll
@@ -528,6 +531,19 @@ __device__ __forceinline__ void merge41(const float* __restrict__ part_lse, cons
     const int64_t u = u0 + (c < S ? c : 0);
     lc[c] = part_lse[u * H + h];
     raw[c] = *(const v4i*)(part_o + (u * H + h) * kLat + 8 * lane);
+  }
+  {
+    const int pos = min(max(p.pos[row], 0), p.n_pos - 1);
+    const float* cs = p.cos_sin + (int64_t)pos * 64;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int pr0 = rope ? ((half ? d1 : d0) - n41::kNope) >> 1 : 0;  // first pair index of the piece
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        cr[2 * half + j] = cs[pr0 + j];
+        sr[2 * half + j] = cs[32 + pr0 + j];
+      }
+    }
   }
   M = sink2;
 #pragma unroll
@@ -569,26 +585,24 @@ __global__ __launch_bounds__(256) void smla_combine41_kernel(
   const int64_t u0 = (int64_t)row * S;
   // merge (K2-back page, stage_combine): M = max(max_c lse2_c, sink2)
   const float sink2 = p.sink ? p.sink[h] * 1.4426950408889634f : -INFINITY;
-  float acc[8], M, L;
-  if (S <= 4) merge41<4>(part_lse, part_o, H, S, u0, h, lane, sink2, acc, M, L);
-  else if (S <= 8) merge41<8>(part_lse, part_o, H, S, u0, h, lane, sink2, acc, M, L);
-  else if (S <= 16) merge41<16>(part_lse, part_o, H, S, u0, h, lane, sink2, acc, M, L);
-  else merge41<32>(part_lse, part_o, H, S, u0, h, lane, sink2, acc, M, L);
+  const int d0 = part_dim(8 * lane), d1 = part_dim(8 * lane + 4);
+  const bool rope = d0 >= n41::kNope;  // both pieces of this lane are rope dims (one 64-dim block)
+  float acc[8], M, L, cr[4], sr[4];
+  if (S <= 4) merge41<4>(part_lse, part_o, H, S, u0, h, lane, sink2, p, row, rope, d0, d1, acc, M, L, cr, sr);
+  else if (S <= 8) merge41<8>(part_lse, part_o, H, S, u0, h, lane, sink2, p, row, rope, d0, d1, acc, M, L, cr, sr);
+  else if (S <= 16) merge41<16>(part_lse, part_o, H, S, u0, h, lane, sink2, p, row, rope, d0, d1, acc, M, L, cr, sr);
+  else merge41<32>(part_lse, part_o, H, S, u0, h, lane, sink2, p, row, rope, d0, d1, acc, M, L, cr, sr);
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
   // bf16, then the inverse GPT-J rotation of the rope dims (448 ..)
   float y[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) y[i] = __builtin_bit_cast(float, (uint32_t)f32_to_bf16_rne(acc[i] * inv) << 16);
-  const int d0 = part_dim(8 * lane), d1 = part_dim(8 * lane + 4);
-  if (d0 >= n41::kNope) {  // both pieces of this lane are rope dims (one 64-dim block)
-    const int pos = min(max(p.pos[row], 0), p.n_pos - 1);
-    const float* cs = p.cos_sin + (int64_t)pos * 64;
+  if (rope) {
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      const int pr0 = ((half ? d1 : d0) - n41::kNope) >> 1;  // first pair index of the piece
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const float c = cs[pr0 + j], s = cs[32 + pr0 + j];
+        const float c = cr[2 * half + j], s = sr[2 * half + j];
         const float e = y[4 * half + 2 * j], o = y[4 * half + 2 * j + 1];
         y[4 * half + 2 * j] = e * c + o * s;
         y[4 * half + 2 * j + 1] = o * c - e * s;
