@@ -118,11 +118,11 @@ def make_case(T, H, N, lens, seed, per_page=(32, 16), pad=(32, 0), invalid_p=0.0
     return c
 
 
-def run_gpu(smla, c, pos=None):
+def run_gpu(smla, c, pos=None, q_dev=None):
     pools_d = [(torch.from_numpy(b).to(DEV), st, pr) for b, st, pr in c.pools]
     sk = None if c.sink is None else torch.from_numpy(np.asarray(c.sink, np.float32)).to(DEV)
     xo, xos, lse, y = smla.fwd_v41(
-        c.q.to(DEV), pools_d, torch.from_numpy(c.indptr).to(DEV), torch.from_numpy(c.indices).to(DEV),
+        c.q.to(DEV) if q_dev is None else q_dev, pools_d, torch.from_numpy(c.indptr).to(DEV), torch.from_numpy(c.indices).to(DEV),
         c.sm_scale, torch.from_numpy(c.pos if pos is None else pos).to(DEV),
         torch.from_numpy(c.cos_sin).to(DEV), sink=sk, has_invalid=c.has_invalid, return_y=True)
     torch.cuda.synchronize()
@@ -225,6 +225,21 @@ def test_v41_position_clamped(smla):
     clamped = run_gpu(smla, c, pos=np.array([63, 5000, -7], np.int32))
     for a, b in zip(base, clamped):
         assert np.array_equal(a, b)
+
+
+def test_v41_strided_q(smla):
+    """q as a strided device view (head pitch 520 elements, row pitch 19
+    heads, starting one head in): the same bytes out as the contiguous q."""
+    c = make_case(5, 16, 3000, [700, 1, 300, 2048, 129], seed=97)
+    note("v41 strided q")
+    base = run_gpu(smla, c)
+    big = torch.zeros(c.T, c.H + 3, 520, dtype=torch.bfloat16, device=DEV)
+    big[:, 1:c.H + 1, :512] = c.q.to(DEV)
+    qv = big[:, 1:c.H + 1, :512]
+    assert qv.stride() == ((c.H + 3) * 520, 520, 1)
+    strided = run_gpu(smla, c, q_dev=qv)
+    for a, b in zip(base, strided):
+        assert np.array_equal(a, b, equal_nan=True)
 
 
 def test_v41_decode_full_size(smla):
