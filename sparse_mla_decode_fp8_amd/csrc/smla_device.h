@@ -176,6 +176,33 @@ __device__ __forceinline__ void xcd_unit(int per_row, int& rank, int& sub) {
   sub = i % per_row;
 }
 
+// Unit mapping of the split forward.  A row's keys in chunk order cover the
+// record index range in order when its slice is sorted, so chunk c of every
+// row touches about the same records at about the same time; putting those
+// units on the same XCDs lets that XCD's L2 serve the records several rows
+// share instead of fetching them once per row.  With `ranged`: S dividing 8,
+// chunk c runs on XCDs [c 8/S, (c+1) 8/S) (rows spread over that group);
+// S = 16 or 32, chunk c on XCD c mod 8.  Otherwise all chunks of a row run on
+// one XCD (xcd_unit).  `ranged` is set only when every unit gets a CU of its
+// own (no longest-first plan): with more units than CUs, the chunks of ragged
+// rows differ in length, and grouping them by chunk would load some XCDs more
+// than others.  The launch grid is fwd_grid(T, S, ranged).
+__device__ __forceinline__ void fwd_unit(int S, bool ranged, int& rank, int& chunk) {
+  const int x = blockIdx.x & 7;
+  const int i = blockIdx.x >> 3;
+  if (ranged && (S == 2 || S == 4 || S == 8)) {
+    const int G = 8 / S;  // XCDs per chunk
+    chunk = x / G;
+    rank = (x % G) + G * i;
+  } else if (ranged && (S == 16 || S == 32)) {
+    const int k = S >> 3;  // chunks of a row on one XCD
+    chunk = x + 8 * (i % k);
+    rank = i / k;
+  } else {
+    xcd_unit(S, rank, chunk);
+  }
+}
+
 // Record address of an index entry that is a key (KeyMode::valid).
 __device__ __forceinline__ const uint8_t* key_addr(const FwdParams& p, int e) {
   if (!p.km.paged) return p.kv + (int64_t)e * kRecordBytes;

@@ -133,5 +133,14 @@ hipError_t launch_decode_rows(const uint8_t* kv, int64_t n_kv, const int32_t* ro
 
 // Blocks a launch of T rows x `per_row` blocks uses with the XCD-aware mapping.
 inline int64_t xcd_grid(int32_t T, int32_t per_row) { return 8LL * ((T + 7) / 8) * per_row; }
+// Blocks of the split forward's unit mapping (fwd_unit, smla_device.h).
+inline int64_t fwd_grid(int32_t T, int32_t S, bool ranged) {
+  if (ranged && (S == 2 || S == 4 || S == 8)) {
+    const int G = 8 / S;
+    return 8LL * ((T + G - 1) / G);
+  }
+  if (ranged && (S == 16 || S == 32)) return (int64_t)T * S;
+  return xcd_grid(T, S);
+}
 
 }  // namespace smla

@@ -24,9 +24,9 @@
 //    e4m3 -> f16, f16 MFMA 16x16x32; the per-token V scale is folded into P,
 //    which passes between waves through LDS.
 //  * combine kernel: LSE merge of the chunks of split rows (with the sink).
-//  * workgroup -> unit mapping is XCD-aware: all chunks of a row run on one XCD
-//    (dispatch is round-robin over the 8 XCDs), so partials and q stay in that
-//    XCD's L2.
+//  * workgroup -> unit mapping is XCD-aware (dispatch is round-robin over the
+//    8 XCDs): chunk c of every split row runs on the same XCDs, so rows whose
+//    sorted slices share records share them through that XCD's L2 (fwd_unit).
 
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
@@ -207,7 +207,7 @@ __global__ __launch_bounds__(n16::kThreads, 1) void smla_fwd16_kernel(
   const int g = lane >> 4;
 
   int rank, chunk;
-  xcd_unit(S, rank, chunk);
+  fwd_unit(S, order == nullptr, rank, chunk);
   if (rank >= T) return;
 
   const uint32_t base = lds_addr(s_lds);
@@ -792,7 +792,7 @@ hipError_t launch_plan(const PlanParams& p, bool sort, Events ev, hipStream_t s)
 hipError_t launch_fwd(const FwdParams& p, Events ev, hipStream_t s) {
   switch (head_tiles(p.H)) {
     case 1: {
-      const int64_t blocks = xcd_grid(p.T, p.S);
+      const int64_t blocks = fwd_grid(p.T, p.S, p.order == nullptr);
       hipExtLaunchKernelGGL(smla_fwd16_kernel, dim3((unsigned)blocks), dim3(n16::kThreads), 0, s,
                             ev.start, ev.stop, 0, p.indptr, p.indices, p.q, p.order, p.T, p.S, p.idx_bytes, p.stride, p);
       return hipGetLastError();

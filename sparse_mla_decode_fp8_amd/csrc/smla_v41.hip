@@ -109,7 +109,7 @@ __global__ __launch_bounds__(n41::kThreads, 1) void smla_fwd41_kernel(
   const int g = lane >> 4;
 
   int rank, chunk;
-  xcd_unit(S, rank, chunk);
+  fwd_unit(S, order == nullptr, rank, chunk);
   if (rank >= T) return;
 
   const uint32_t base = lds_addr(s_lds);
@@ -658,7 +658,7 @@ __global__ __launch_bounds__(64) void smla_mxfp8_kernel(const float* y, int64_t 
 // ---------------------------------------------------------------- launchers
 
 hipError_t launch_fwd41(const FwdParams& p, Events ev, hipStream_t s) {
-  const int64_t blocks = xcd_grid(p.T, p.S);
+  const int64_t blocks = fwd_grid(p.T, p.S, p.order == nullptr);
   hipExtLaunchKernelGGL(smla_fwd41_kernel, dim3((unsigned)blocks), dim3(n41::kThreads), 0, s, ev.start, ev.stop, 0,
                         p.indptr, p.indices, p.q, p.order, p.T, p.S, p.idx_bytes, p.stride, p);
   return hipGetLastError();

@@ -94,7 +94,8 @@ __global__ __launch_bounds__(nw::kThreads, 1) void smla_fwdw_kernel(FwdParams p)
   const int wi = w / HT;        // this wave's index among the waves of its head tile
 
   int rank, sub;
-  xcd_unit(p.S * p.hg, rank, sub);
+  if (p.hg == 1) fwd_unit(p.S, p.order == nullptr, rank, sub);  // one head group: sub is the chunk
+  else xcd_unit(p.S * p.hg, rank, sub);
   if (rank >= p.T) return;
   const int chunk = sub % p.S;
   const int h0 = 64 * (sub / p.S);  // first head of this unit's head group
@@ -409,7 +410,7 @@ __global__ __launch_bounds__(nw::kThreads, 1) void smla_fwdw_kernel(FwdParams p)
 
 template <int HT>
 static hipError_t launch_fwdw_t(const FwdParams& p, Events ev, hipStream_t s) {
-  const int64_t blocks = xcd_grid(p.T, p.S * p.hg);
+  const int64_t blocks = p.hg == 1 ? fwd_grid(p.T, p.S, p.order == nullptr) : xcd_grid(p.T, p.S * p.hg);
   hipExtLaunchKernelGGL((smla_fwdw_kernel<HT>), dim3((unsigned)blocks), dim3(nw::kThreads), 0, s,
                         ev.start, ev.stop, 0, p);
   return hipGetLastError();
