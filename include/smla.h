@@ -140,6 +140,36 @@ int sparse_mla_fwd(const void* q, int64_t q_stride_t, int64_t q_stride_h,
                    void* stream);
 
 /*
+ * sparse_mla_fwd_noalloc -- sparse_mla_fwd without a workspace argument, for
+ * callers that cannot allocate device memory: code being captured into a HIP
+ * graph, tight serving loops, harnesses that forbid allocation.
+ *
+ * Every argument but the workspace, the semantics and the result are those of
+ * sparse_mla_fwd (the same kernels on the same split).  The scratch that the
+ * workspace would hold lives in a static device array of
+ * SMLA_NOALLOC_SCRATCH_BYTES bytes: each device the library runs on holds its
+ * own copy until the process ends.  The first call on a device looks its
+ * address up (no allocation); no call allocates device or host memory.
+ *
+ * Calls on one device share that device's array and leave the last call's
+ * contents in it (nothing in it needs to start at zero).  Calls that may
+ * overlap on one device race on it: queue them on one stream, or use
+ * sparse_mla_fwd with a workspace per stream.
+ *
+ * Returns SMLA_EWORKSPACE, with nothing queued, when the forward needs more
+ * scratch than the array holds (sparse_mla_workspace_bytes(T, H, nnz) >
+ * SMLA_NOALLOC_SCRATCH_BYTES: split partials of many long rows with many
+ * heads); otherwise the statuses of sparse_mla_fwd.
+ */
+#define SMLA_NOALLOC_SCRATCH_BYTES (64LL << 20)
+int sparse_mla_fwd_noalloc(const void* q, int64_t q_stride_t, int64_t q_stride_h,
+                           const void* kv, int64_t n_kv,
+                           const int32_t* indptr, const int32_t* indices, int64_t nnz,
+                           int32_t T, int32_t H, float sm_scale, int32_t has_invalid,
+                           void* out, int64_t o_stride_t, int64_t o_stride_h,
+                           float* lse, void* stream);
+
+/*
  * smla_kv_pool -- one paged pool of 656-byte records (K2-back page of the
  * DeepSeek V4.1 AMD attention module, "key_rec": a key-table entry names a
  * slot of the window pool or of the compressed pool; a pool is a run of

@@ -50,6 +50,17 @@ _lib.sparse_mla_fwd.argtypes = [
     _vp,                    # stream
 ]
 _lib.sparse_mla_fwd.restype = ctypes.c_int
+_lib.sparse_mla_fwd_noalloc.argtypes = [
+    _vp, _i64, _i64,        # q, strides
+    _vp, _i64,              # kv, n_kv
+    _vp, _vp, _i64,         # indptr, indices, nnz
+    _i32, _i32, _f32, _i32,  # T, H, sm_scale, has_invalid
+    _vp, _i64, _i64,        # out, strides
+    _vp,                    # lse
+    _vp,                    # stream
+]
+_lib.sparse_mla_fwd_noalloc.restype = ctypes.c_int
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class KvPool(ctypes.Structure):
@@ -99,6 +110,7 @@ _lib.sparse_mla_profile_end.restype = ctypes.c_int
 
 EXPORTED = (
     "sparse_mla_supported", "sparse_mla_workspace_bytes", "sparse_mla_split_for", "sparse_mla_fwd",
+    "sparse_mla_fwd_noalloc",
     "sparse_mla_fwd_paged", "sparse_mla_v41_workspace_bytes", "sparse_mla_fwd_v41", "sparse_mla_mxfp8",
     "sparse_mla_cache_write", "sparse_mla_decode_rows", "sparse_mla_last_error", "sparse_mla_set_option",
     "sparse_mla_profile_begin", "sparse_mla_profile_end",
@@ -213,6 +225,38 @@ def fwd(q: torch.Tensor, kv: torch.Tensor, indptr: torch.Tensor, indices: torch.
         _stream(dev))
     _check(rc)
     return out, lse
+
+
+def fwd_noalloc(q: torch.Tensor, kv: torch.Tensor, indptr: torch.Tensor, indices: torch.Tensor,
+                sm_scale: float, out: torch.Tensor, lse: Optional[torch.Tensor] = None,
+                has_invalid: bool = False) -> None:
+    """sparse_mla_fwd_noalloc: the forward into the caller's out (bf16 [T, H, 512])
+    and lse (f32 [T, H] or None), with the library's static per-device scratch
+    in place of a workspace; nothing is allocated.  Calls that overlap on one
+    device race on that scratch."""
+    _check_fwd_args(q, indptr, indices)
+    if kv.dtype != torch.uint8 or kv.dim() != 2 or kv.shape[1] != RECORD_BYTES or not kv.is_contiguous():
+        raise ValueError(f"kv must be contiguous uint8 [N, {RECORD_BYTES}]")
+    T, H, _ = q.shape
+    if out.dtype != torch.bfloat16 or tuple(out.shape) != (T, H, 512) or out.stride(2) != 1:
+        raise ValueError("out must be bf16 [T, H, 512] with a contiguous last dimension")
+    if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (T, H) or not lse.is_contiguous()):
+        raise ValueError("lse must be contiguous f32 [T, H]")
+    for t in (kv, out) + ((lse,) if lse is not None else ()):
+        if t.device != q.device:
+            raise ValueError("all tensors must be on q's device")
+    if not (indptr.is_contiguous() and indices.is_contiguous()):
+        raise ValueError("indptr and indices must be contiguous (no copy is made)")
+    nnz = indices.numel()
+    rc = _lib.sparse_mla_fwd_noalloc(
+        _ptr(q), q.stride(0), q.stride(1),
+        _ptr(kv), kv.shape[0],
+        _ptr(indptr), _ptr(indices) if nnz else None, nnz,
+        T, H, float(sm_scale), 1 if has_invalid else 0,
+        _ptr(out), out.stride(0), out.stride(1),
+        _ptr(lse),
+        _stream(q.device))
+    _check(rc)
 
 
 def _check_fwd_args(q, indptr, indices):

@@ -20,15 +20,17 @@
 
 namespace {
 
-thread_local std::string g_err;
+// The last failing call's message (a fixed buffer: reporting an error
+// allocates nothing).
+thread_local char g_err[512];
+
+void clear_err() { g_err[0] = 0; }
 
 int fail(int code, const char* fmt, ...) {
-  char buf[512];
   va_list ap;
   va_start(ap, fmt);
-  vsnprintf(buf, sizeof buf, fmt, ap);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
   va_end(ap);
-  g_err = buf;
   return code;
 }
 
@@ -250,7 +252,8 @@ int fwd_impl(const void* q, int64_t q_stride_t, int64_t q_stride_h, const KeySou
              const int32_t* indptr, const int32_t* indices, int64_t nnz,
              int32_t T, int32_t H, float sm_scale, int32_t has_invalid, const float* sink,
              void* out, int64_t o_stride_t, int64_t o_stride_h, float* lse,
-             void* workspace, int64_t workspace_bytes, void* stream, const V41Out* v41 = nullptr) {
+             void* workspace, int64_t workspace_bytes, void* stream, const V41Out* v41 = nullptr,
+             bool noalloc = false) {
   if (!sparse_mla_supported(H)) return fail(SMLA_EUNSUPPORTED, "num_heads must be in [1, %d], got %d", SMLA_MAX_HEADS, H);
   if (v41 && H > 16) return fail(SMLA_EUNSUPPORTED, "the V4.1 record path implements 1 to 16 heads, got %d", H);
   if (T < 0) return fail(SMLA_EINVAL, "T must be >= 0, got %d", T);
@@ -258,7 +261,8 @@ int fwd_impl(const void* q, int64_t q_stride_t, int64_t q_stride_h, const KeySou
   if (nnz > kMaxNnz) return fail(SMLA_EINVAL, "nnz must be <= %lld (32-bit bounded index reads), got %lld", (long long)kMaxNnz, (long long)nnz);
   if (!isfinite(sm_scale)) return fail(SMLA_EINVAL, "sm_scale must be finite");
   if (T == 0) return SMLA_OK;
-  if (!q || !indptr || !(out || v41) || !workspace) return fail(SMLA_EINVAL, "null pointer (q, indptr, out and workspace are required)");
+  if (!q || !indptr || !(out || v41) || !(workspace || noalloc))
+    return fail(SMLA_EINVAL, "null pointer (q, indptr, out and workspace are required)");
   if (nnz > 0 && !indices) return fail(SMLA_EINVAL, "indices is null but nnz > 0");
   if (!aligned(q, 16) || !aligned(out, 16)) return fail(SMLA_EINVAL, "q and out must be 16-byte aligned");
   if (lse && !aligned(lse, 4)) return fail(SMLA_EINVAL, "lse must be 4-byte aligned");
@@ -268,7 +272,10 @@ int fwd_impl(const void* q, int64_t q_stride_t, int64_t q_stride_h, const KeySou
       (q_stride_t | q_stride_h | o_stride_t | o_stride_h) % 8 != 0)
     return fail(SMLA_EINVAL, "strides must be non-negative multiples of 8 elements");
   const Layout L = layout(T, H, nnz, v41 != nullptr, has_invalid != 0);
-  if (workspace_bytes < (int64_t)L.total)
+  if (noalloc && (int64_t)L.total > SMLA_NOALLOC_SCRATCH_BYTES)
+    return fail(SMLA_EWORKSPACE, "this forward needs %lld bytes of scratch; the static scratch holds %lld "
+                "(call sparse_mla_fwd with a workspace)", (long long)L.total, (long long)SMLA_NOALLOC_SCRATCH_BYTES);
+  if (!noalloc && workspace_bytes < (int64_t)L.total)
     return fail(SMLA_EWORKSPACE, "workspace has %lld bytes, needs %lld", (long long)workspace_bytes, (long long)L.total);
 
   hipStream_t s = (hipStream_t)stream;
@@ -278,6 +285,10 @@ int fwd_impl(const void* q, int64_t q_stride_t, int64_t q_stride_h, const KeySou
   const uint8_t* zero = nullptr;
   ez = zero_record(dev, &zero);
   if (ez != hipSuccess) return hip_fail(ez, "zero record lookup");
+  if (noalloc) {  // the device's static scratch stands in for the workspace
+    ez = smla::noalloc_scratch(dev, &workspace);
+    if (ez != hipSuccess) return hip_fail(ez, "static scratch lookup");
+  }
   uint8_t* ws = (uint8_t*)workspace;
   int32_t* row_tiles = (int32_t*)(ws + L.row_tiles);
   int32_t* order = (int32_t*)(ws + L.order);
@@ -365,7 +376,7 @@ int sparse_mla_fwd(const void* q, int64_t q_stride_t, int64_t q_stride_h,
                    float* lse,
                    void* workspace, int64_t workspace_bytes,
                    void* stream) {
-  g_err.clear();
+  clear_err();
   if (n_kv < 0 || n_kv > INT64_MAX / smla::kRecordBytes) return fail(SMLA_EINVAL, "n_kv out of range: %lld", (long long)n_kv);
   if (T > 0 && !kv) return fail(SMLA_EINVAL, "null pointer (kv is required)");
   if (!aligned(kv, 16)) return fail(SMLA_EINVAL, "kv must be 16-byte aligned");
@@ -374,6 +385,23 @@ int sparse_mla_fwd(const void* q, int64_t q_stride_t, int64_t q_stride_h,
   ks.kv = (const uint8_t*)kv;
   return fwd_impl(q, q_stride_t, q_stride_h, ks, indptr, indices, nnz, T, H, sm_scale, has_invalid, nullptr,
                   out, o_stride_t, o_stride_h, lse, workspace, workspace_bytes, stream);
+}
+
+int sparse_mla_fwd_noalloc(const void* q, int64_t q_stride_t, int64_t q_stride_h,
+                           const void* kv, int64_t n_kv,
+                           const int32_t* indptr, const int32_t* indices, int64_t nnz,
+                           int32_t T, int32_t H, float sm_scale, int32_t has_invalid,
+                           void* out, int64_t o_stride_t, int64_t o_stride_h,
+                           float* lse, void* stream) {
+  clear_err();
+  if (n_kv < 0 || n_kv > INT64_MAX / smla::kRecordBytes) return fail(SMLA_EINVAL, "n_kv out of range: %lld", (long long)n_kv);
+  if (T > 0 && !kv) return fail(SMLA_EINVAL, "null pointer (kv is required)");
+  if (!aligned(kv, 16)) return fail(SMLA_EINVAL, "kv must be 16-byte aligned");
+  KeySource ks{};
+  ks.km = smla::KeyMode{0, {1, 1}};
+  ks.kv = (const uint8_t*)kv;
+  return fwd_impl(q, q_stride_t, q_stride_h, ks, indptr, indices, nnz, T, H, sm_scale, has_invalid, nullptr,
+                  out, o_stride_t, o_stride_h, lse, nullptr, 0, stream, nullptr, /*noalloc=*/true);
 }
 
 int sparse_mla_fwd_paged(const void* q, int64_t q_stride_t, int64_t q_stride_h,
@@ -385,7 +413,7 @@ int sparse_mla_fwd_paged(const void* q, int64_t q_stride_t, int64_t q_stride_h,
                          float* lse,
                          void* workspace, int64_t workspace_bytes,
                          void* stream) {
-  g_err.clear();
+  clear_err();
   KeySource ks{};
   const int rc = parse_pools(pools, smla::kRecordBytes, ks);
   if (rc != SMLA_OK) return rc;
@@ -406,7 +434,7 @@ int sparse_mla_fwd_v41(const void* q, int64_t q_stride_t, int64_t q_stride_h,
                        const float* sink, const int32_t* pos, const float* cos_sin, int32_t n_pos,
                        void* xo, void* xo_scales, float* lse, float* y_out,
                        void* workspace, int64_t workspace_bytes, void* stream) {
-  g_err.clear();
+  clear_err();
   KeySource ks{};
   const int rc = parse_pools(pools, 576 + 8, ks);
   if (rc != SMLA_OK) return rc;
@@ -422,7 +450,7 @@ int sparse_mla_fwd_v41(const void* q, int64_t q_stride_t, int64_t q_stride_h,
 }
 
 int sparse_mla_mxfp8(const float* y, int64_t n, void* codes, void* scales, void* stream) {
-  g_err.clear();
+  clear_err();
   if (n < 0 || n % 64 != 0) return fail(SMLA_EINVAL, "n must be a non-negative multiple of 64, got %lld", (long long)n);
   if (n == 0) return SMLA_OK;
   if (n / 512 + 1 > 0x7fffffff) return fail(SMLA_EINVAL, "n too large for one launch");
@@ -435,7 +463,7 @@ int sparse_mla_mxfp8(const float* y, int64_t n, void* codes, void* scales, void*
 
 int sparse_mla_decode_rows(const void* kv, int64_t n_kv, const int32_t* rows, int64_t n,
                            float* out, void* stream) {
-  g_err.clear();
+  clear_err();
   if (n < 0 || n_kv < 0) return fail(SMLA_EINVAL, "n and n_kv must be >= 0");
   if (n > 0x7fffffff) return fail(SMLA_EINVAL, "n too large for one launch");
   if (n == 0) return SMLA_OK;
@@ -450,7 +478,7 @@ int sparse_mla_cache_write(const void* latent, int64_t latent_stride,
                            const void* rope, int64_t rope_stride,
                            const int64_t* slots, int64_t n,
                            void* kv, int64_t n_kv, void* stream) {
-  g_err.clear();
+  clear_err();
   if (n < 0 || n_kv < 0) return fail(SMLA_EINVAL, "n and n_kv must be >= 0");
   if (n_kv > INT64_MAX / smla::kRecordBytes) return fail(SMLA_EINVAL, "n_kv out of range: %lld", (long long)n_kv);
   if (n > (int64_t)0x7fffffff * 4) return fail(SMLA_EINVAL, "n too large for one launch");
@@ -469,10 +497,10 @@ int sparse_mla_cache_write(const void* latent, int64_t latent_stride,
   return SMLA_OK;
 }
 
-const char* sparse_mla_last_error(void) { return g_err.c_str(); }
+const char* sparse_mla_last_error(void) { return g_err; }
 
 int sparse_mla_set_option(const char* name, int64_t value) {
-  g_err.clear();
+  clear_err();
   if (!name) return fail(SMLA_EINVAL, "null option name");
   if (!strcmp(name, "plan")) {
     if (value < 0 || value > 2) return fail(SMLA_EINVAL, "plan must be 0, 1 or 2");
@@ -488,7 +516,7 @@ int sparse_mla_set_option(const char* name, int64_t value) {
 }
 
 int sparse_mla_profile_begin(int32_t max_calls) {
-  g_err.clear();
+  clear_err();
   if (max_calls <= 0) return fail(SMLA_EINVAL, "max_calls must be > 0");
   std::lock_guard<std::mutex> lk(g_prof.mu);
   if (g_prof.active) return fail(SMLA_EINVAL, "profiling already active");
@@ -511,7 +539,7 @@ int sparse_mla_profile_begin(int32_t max_calls) {
 }
 
 int sparse_mla_profile_end(double* ms, int64_t* launches) {
-  g_err.clear();
+  clear_err();
   std::lock_guard<std::mutex> lk(g_prof.mu);
   if (!g_prof.active) return fail(SMLA_EINVAL, "profiling not active");
   double acc[SMLA_PROFILE_KINDS] = {};

@@ -128,6 +128,9 @@ hipError_t launch_fwd41(const FwdParams& p, Events ev, hipStream_t s);
 hipError_t launch_combine41(const Combine41Params& p, Events ev, hipStream_t s);
 // Test hook: MXFP8 of n f32 values (n a multiple of 64).
 hipError_t launch_mxfp8(const float* y, int64_t n, uint8_t* codes, uint8_t* scales, hipStream_t s);
+// Device address of the static scratch of sparse_mla_fwd_noalloc on device
+// dev (looked up once per device with that device current; smla_noalloc.hip).
+hipError_t noalloc_scratch(int dev, void** out);
 hipError_t launch_decode_rows(const uint8_t* kv, int64_t n_kv, const int32_t* rows, int64_t n,
                               float* out, hipStream_t s);
 
