@@ -53,11 +53,14 @@ typedef enum {
 #define SMLA_MAX_HEADS 128
 
 /*
- * sparse_mla_supported -- 1 if a forward with `num_heads` heads is implemented,
- * else 0.  The FlyDSL page rejects head counts outside [1, 16]
- * (build_sparse_mla_fp8ds_module); this library accepts [1, SMLA_MAX_HEADS].
+ * sparse_mla_supported -- 1 if a forward with `num_heads` heads, QK head
+ * dimension `head_dim_qk` and value dimension `dv` is implemented, else 0.
+ * The record fixes head_dim_qk = 576 (512 latent + 64 rope) and dv = 512
+ * (FlyDSL page, module docstring).  The FlyDSL page rejects head counts
+ * outside [1, 16] (build_sparse_mla_fp8ds_module); this library accepts
+ * [1, SMLA_MAX_HEADS].
  */
-int sparse_mla_supported(int32_t num_heads);
+int sparse_mla_supported(int32_t num_heads, int32_t head_dim_qk, int32_t dv);
 
 /*
  * sparse_mla_workspace_bytes -- device workspace a forward of T query rows,
@@ -105,8 +108,9 @@ int32_t sparse_mla_split_for(int32_t T, int32_t H, int64_t nnz, int32_t has_inva
  *              16-byte aligned, strides multiples of 8.
  *   lse        device, f32 [T, H] contiguous, or NULL to skip it.  Natural log;
  *              -inf for a row with no key (whose out is all zero).
- *   workspace  device, >= sparse_mla_workspace_bytes(T, H, nnz) bytes,
- *              256-byte aligned.
+ *   workspace  device, >= sparse_mla_workspace_bytes(T, H, nnz) bytes (asked
+ *              with the stream's device current: the split follows that
+ *              device's compute units), 256-byte aligned.
  *
  * Preconditions the library cannot check (undefined results if broken, as on
  * the FlyDSL page, section "Preconditions the host cannot check"):

@@ -33,7 +33,7 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 _vp, _i32, _i64, _f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
-_lib.sparse_mla_supported.argtypes = [_i32]
+_lib.sparse_mla_supported.argtypes = [_i32, _i32, _i32]
 _lib.sparse_mla_supported.restype = ctypes.c_int
 _lib.sparse_mla_workspace_bytes.argtypes = [_i32, _i32, _i64]
 _lib.sparse_mla_workspace_bytes.restype = _i64
@@ -132,8 +132,8 @@ def lib() -> ctypes.CDLL:
     return _lib
 
 
-def supported(num_heads: int) -> bool:
-    return bool(_lib.sparse_mla_supported(int(num_heads)))
+def supported(num_heads: int, head_dim_qk: int = 576, dv: int = 512) -> bool:
+    return bool(_lib.sparse_mla_supported(int(num_heads), int(head_dim_qk), int(dv)))
 
 
 def workspace_bytes(T: int, H: int, nnz: int) -> int:
@@ -170,7 +170,12 @@ def workspace(device: torch.device, nbytes: int) -> torch.Tensor:
     """A device workspace of at least nbytes, reused per device and stream (the
     current stream of `device`, the one the call is queued on): calls on one
     stream are ordered, so they can share it, and calls on other streams get
-    their own."""
+    their own.  While the stream is being captured into a HIP graph the call
+    gets a fresh workspace from the graph's own memory pool instead: graphs
+    captured on one capture stream may be replayed on different streams at
+    once, so they must not share a cached workspace."""
+    if torch.cuda.is_current_stream_capturing():
+        return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
     key = (device.type, device.index, torch.cuda.current_stream(device).cuda_stream)
     ws = _ws_cache.get(key)
     if ws is None or ws.numel() < nbytes:

@@ -38,8 +38,11 @@ int hip_fail(hipError_t e, const char* what) {
   return fail(SMLA_EHIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-int64_t g_split_override = 0;  // 0 = automatic
-int64_t g_plan_override = 0;   // 0 = automatic, 1 = never plan, 2 = always plan
+// Process-wide tuning knobs (sparse_mla_set_option; benchmarks and tests).
+// Atomic, so concurrent forwards read a consistent value; a forward reads
+// each once, so a change applies to the forwards that start after it.
+std::atomic<int64_t> g_split_override{0};  // 0 = automatic
+std::atomic<int64_t> g_plan_override{0};   // 0 = automatic, 1 = never plan, 2 = always plan
 
 // Index reads use 32-bit byte offsets; the kernels read up to a few tiles past
 // a row's end, so leave headroom below 2^32 bytes.
@@ -86,6 +89,9 @@ hipError_t zero_record(int dev, const uint8_t** out) {
 // Compute units of the current device (queried once per device).
 std::atomic<int> g_cus[64];
 
+// Head counts the forward implements (the QK and V dims are fixed by the record).
+bool heads_ok(int32_t H) { return H >= 1 && H <= SMLA_MAX_HEADS; }
+
 int device_cus(int dev = -1) {
   int cus = 0;
   if (dev < 0 && hipGetDevice(&dev) != hipSuccess) return 256;
@@ -101,12 +107,14 @@ int device_cus(int dev = -1) {
 // padded slices (has_invalid) the rows' real lengths differ, and a batch of
 // about one row per CU is bounded by its longest rows: two chunks per row,
 // queued longest first, let those rows use two CUs.
-int choose_split(int32_t T, int32_t H, int64_t nnz, bool has_invalid = true) {
-  if (g_split_override > 0) return (int)g_split_override;
+// `dev`: the device the forward runs on (-1: the current device).
+int choose_split(int32_t T, int32_t H, int64_t nnz, bool has_invalid, int dev) {
+  const int64_t forced = g_split_override.load(std::memory_order_relaxed);
+  if (forced > 0) return (int)forced;
   if (T <= 0) return 1;
   const int tile = smla::tile_tokens(H);
   const int64_t avg_tiles = (nnz / T + tile - 1) / tile;
-  const int cus = device_cus();
+  const int cus = device_cus(dev);
   const int64_t units = (int64_t)T * smla::head_groups(H);  // unsplit units
   if (units >= cus) return (has_invalid && 2 * units <= 3 * (int64_t)cus && avg_tiles >= 2) ? 2 : 1;
   int64_t s = (cus + units - 1) / units;
@@ -125,10 +133,10 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 // `partials`: the V4.1 path writes chunk partials for every row (its
 // epilogue runs in the combine), whatever the split.  The size is that of
 // the larger split (a padded batch's), so one workspace serves both.
-Layout layout(int32_t T, int32_t H, int64_t nnz, bool partials = false, bool has_invalid = true) {
+Layout layout(int32_t T, int32_t H, int64_t nnz, bool partials, bool has_invalid, int dev) {
   Layout L{};
-  const int s_max = choose_split(T, H, nnz, true);
-  L.S = choose_split(T, H, nnz, has_invalid);
+  const int s_max = choose_split(T, H, nnz, true, dev);
+  L.S = choose_split(T, H, nnz, has_invalid, dev);
   size_t off = 0;
   L.row_tiles = off;
   off = align256(off + sizeof(int32_t) * (size_t)T);
@@ -179,18 +187,20 @@ hipError_t timed(int kind, F&& launch) {
 
 extern "C" {
 
-int sparse_mla_supported(int32_t num_heads) { return num_heads >= 1 && num_heads <= SMLA_MAX_HEADS; }
+int sparse_mla_supported(int32_t num_heads, int32_t head_dim_qk, int32_t dv) {
+  return heads_ok(num_heads) && head_dim_qk == 576 && dv == 512;
+}
 
 int64_t sparse_mla_workspace_bytes(int32_t T, int32_t H, int64_t nnz) {
   if (T < 0 || nnz < 0) return fail(SMLA_EINVAL, "T and nnz must be >= 0 (T=%d nnz=%lld)", T, (long long)nnz);
-  if (!sparse_mla_supported(H)) return fail(SMLA_EUNSUPPORTED, "num_heads must be in [1, %d], got %d", SMLA_MAX_HEADS, H);
-  return (int64_t)layout(T, H, nnz).total;
+  if (!heads_ok(H)) return fail(SMLA_EUNSUPPORTED, "num_heads must be in [1, %d], got %d", SMLA_MAX_HEADS, H);
+  return (int64_t)layout(T, H, nnz, false, true, -1).total;
 }
 
 int32_t sparse_mla_split_for(int32_t T, int32_t H, int64_t nnz, int32_t has_invalid) {
   if (T < 0 || nnz < 0) return fail(SMLA_EINVAL, "T and nnz must be >= 0 (T=%d nnz=%lld)", T, (long long)nnz);
-  if (!sparse_mla_supported(H)) return fail(SMLA_EUNSUPPORTED, "num_heads must be in [1, %d], got %d", SMLA_MAX_HEADS, H);
-  return choose_split(T, H, nnz, has_invalid != 0);
+  if (!heads_ok(H)) return fail(SMLA_EUNSUPPORTED, "num_heads must be in [1, %d], got %d", SMLA_MAX_HEADS, H);
+  return choose_split(T, H, nnz, has_invalid != 0, -1);
 }
 
 }  // extern "C"
@@ -254,7 +264,7 @@ int fwd_impl(const void* q, int64_t q_stride_t, int64_t q_stride_h, const KeySou
              void* out, int64_t o_stride_t, int64_t o_stride_h, float* lse,
              void* workspace, int64_t workspace_bytes, void* stream, const V41Out* v41 = nullptr,
              bool noalloc = false) {
-  if (!sparse_mla_supported(H)) return fail(SMLA_EUNSUPPORTED, "num_heads must be in [1, %d], got %d", SMLA_MAX_HEADS, H);
+  if (!heads_ok(H)) return fail(SMLA_EUNSUPPORTED, "num_heads must be in [1, %d], got %d", SMLA_MAX_HEADS, H);
   if (v41 && H > 16) return fail(SMLA_EUNSUPPORTED, "the V4.1 record path implements 1 to 16 heads, got %d", H);
   if (T < 0) return fail(SMLA_EINVAL, "T must be >= 0, got %d", T);
   if (nnz < 0) return fail(SMLA_EINVAL, "nnz must be >= 0, got %lld", (long long)nnz);
@@ -271,16 +281,18 @@ int fwd_impl(const void* q, int64_t q_stride_t, int64_t q_stride_h, const KeySou
   if (q_stride_t < 0 || q_stride_h < 0 || o_stride_t < 0 || o_stride_h < 0 ||
       (q_stride_t | q_stride_h | o_stride_t | o_stride_h) % 8 != 0)
     return fail(SMLA_EINVAL, "strides must be non-negative multiples of 8 elements");
-  const Layout L = layout(T, H, nnz, v41 != nullptr, has_invalid != 0);
+  // the split and the workspace layout are those of the stream's device
+  // (a failed device lookup is reported after the argument checks)
+  hipStream_t s = (hipStream_t)stream;
+  int dev = -1;
+  hipError_t ez = stream_device(s, &dev);
+  const Layout L = layout(T, H, nnz, v41 != nullptr, has_invalid != 0, ez == hipSuccess ? dev : -1);
   if (noalloc && (int64_t)L.total > SMLA_NOALLOC_SCRATCH_BYTES)
     return fail(SMLA_EWORKSPACE, "this forward needs %lld bytes of scratch; the static scratch holds %lld "
                 "(call sparse_mla_fwd with a workspace)", (long long)L.total, (long long)SMLA_NOALLOC_SCRATCH_BYTES);
   if (!noalloc && workspace_bytes < (int64_t)L.total)
     return fail(SMLA_EWORKSPACE, "workspace has %lld bytes, needs %lld", (long long)workspace_bytes, (long long)L.total);
 
-  hipStream_t s = (hipStream_t)stream;
-  int dev = 0;
-  hipError_t ez = stream_device(s, &dev);
   if (ez != hipSuccess) return hip_fail(ez, "stream device");
   const uint8_t* zero = nullptr;
   ez = zero_record(dev, &zero);
@@ -299,9 +311,10 @@ int fwd_impl(const void* q, int64_t q_stride_t, int64_t q_stride_h, const KeySou
   // order cannot shorten the slowest.  Without an order there is nothing to
   // plan: each forward block takes its row's length from indptr and, with
   // has_invalid, trims the trailing masked entries by a scan of its own row.
-  const bool sort = g_plan_override == 1   ? false
-                    : g_plan_override == 2 ? true
-                                           : (int64_t)T * L.S * smla::head_groups(H) > device_cus(dev);
+  const int64_t plan_opt = g_plan_override.load(std::memory_order_relaxed);
+  const bool sort = plan_opt == 1   ? false
+                    : plan_opt == 2 ? true
+                                    : (int64_t)T * L.S * smla::head_groups(H) > device_cus(dev);
   hipError_t e = hipSuccess;
   if (sort) {
     smla::PlanParams pp{indptr, indices, idx_bytes, T, smla::tile_tokens(H), has_invalid ? 1 : 0,
@@ -424,7 +437,7 @@ int sparse_mla_fwd_paged(const void* q, int64_t q_stride_t, int64_t q_stride_h,
 int64_t sparse_mla_v41_workspace_bytes(int32_t T, int32_t H, int64_t nnz) {
   if (T < 0 || nnz < 0) return fail(SMLA_EINVAL, "T and nnz must be >= 0 (T=%d nnz=%lld)", T, (long long)nnz);
   if (H < 1 || H > 16) return fail(SMLA_EUNSUPPORTED, "the V4.1 record path implements 1 to 16 heads, got %d", H);
-  return (int64_t)layout(T, H, nnz, true).total;
+  return (int64_t)layout(T, H, nnz, true, true, -1).total;
 }
 
 int sparse_mla_fwd_v41(const void* q, int64_t q_stride_t, int64_t q_stride_h,
@@ -504,12 +517,12 @@ int sparse_mla_set_option(const char* name, int64_t value) {
   if (!name) return fail(SMLA_EINVAL, "null option name");
   if (!strcmp(name, "plan")) {
     if (value < 0 || value > 2) return fail(SMLA_EINVAL, "plan must be 0, 1 or 2");
-    g_plan_override = value;
+    g_plan_override.store(value, std::memory_order_relaxed);
     return SMLA_OK;
   }
   if (!strcmp(name, "split")) {
     if (value < 0 || value > SMLA_MAX_SPLIT) return fail(SMLA_EINVAL, "split must be in [0, %d]", SMLA_MAX_SPLIT);
-    g_split_override = value;
+    g_split_override.store(value, std::memory_order_relaxed);
     return SMLA_OK;
   }
   return fail(SMLA_EINVAL, "unknown option '%s'", name);

@@ -38,6 +38,9 @@ def test_supported_range(b):
     assert not b.supported(0)
     assert b.supported(1) and b.supported(16) and b.supported(64) and b.supported(128)
     assert not b.supported(129)
+    assert b.lib().sparse_mla_supported(16, 576, 512) == 1
+    assert b.lib().sparse_mla_supported(16, 512, 512) == 0   # the record's QK dim is 576
+    assert b.lib().sparse_mla_supported(16, 576, 576) == 0   # V is the 512 latent values
 
 
 def test_workspace_bytes(b):

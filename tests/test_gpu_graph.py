@@ -226,3 +226,50 @@ def test_concurrent_streams(smla):
     torch.cuda.synchronize()
     for name, (w, hi, o, l, ws) in outs.items():
         assert torch.equal(o, ref[name][0]) and torch.equal(l, ref[name][1]), f"problem {name} differs"
+
+
+def test_two_graphs_default_workspace_replayed_at_once(smla):
+    """Two graphs captured one after the other with the binding's default
+    workspace (both captures run on torch's one default capture stream), then
+    replayed at the same time on two streams: each capture got a workspace of
+    its own from its graph's memory pool, so each replay equals its eager
+    result bit for bit."""
+    T, H, N, k = 32, 16, 16384, 1024
+    ws_ = [synth.build_workload(f"graphs_{i}", T, H, N, lambda g, r, m: np.sort(synth.distinct_uniform(g, N, k)),
+                                seed=31 + i, device="cuda") for i in range(2)]
+    note(f"two graphs: {T} x {k} keys each, split {smla.split_for(T, H, T * k)}, replayed on two streams at once")
+    outs = [(torch.empty(T, H, 512, dtype=torch.bfloat16, device=DEV),
+             torch.empty(T, H, dtype=torch.float32, device=DEV)) for _ in ws_]
+    ref = []
+    for w, (o, l) in zip(ws_, outs):
+        smla.fwd(w.q, w.kv, w.indptr, w.indices, w.sm_scale, out=o, lse=l)
+        torch.cuda.synchronize()
+        ref.append((o.clone(), l.clone()))
+    graphs = []
+    for w, (o, l) in zip(ws_, outs):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            smla.fwd(w.q, w.kv, w.indptr, w.indices, w.sm_scale, out=o, lse=l)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(3):
+                smla.fwd(w.q, w.kv, w.indptr, w.indices, w.sm_scale, out=o, lse=l)
+        torch.cuda.synchronize()
+        graphs.append(g)
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for r in range(4):
+        for o, l in outs:
+            o.fill_(7)
+            l.fill_(7)
+        torch.cuda.synchronize()
+        for g, st in zip(graphs, streams):
+            st.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(st):
+                g.replay()
+        torch.cuda.synchronize()
+        for i, ((o, l), (ro, rl)) in enumerate(zip(outs, ref)):
+            assert torch.equal(o, ro) and torch.equal(l, rl), f"replay {r}: graph {i} differs from its eager call"
+    del graphs
