@@ -297,6 +297,27 @@ int sparse_mla_fwd_v41(const void* q, int64_t q_stride_t, int64_t q_stride_h,
 int sparse_mla_mxfp8(const float* y, int64_t n, void* codes, void* scales, void* stream);
 
 /*
+ * sparse_mla_qk_probe -- test hook: the QK dot products q . K (no sm_scale)
+ * of the n records kv[rows[i]] (n a multiple of 16) against the 16 heads of
+ * q (device bf16 [16, 576], contiguous), written to scores (device f32
+ * [n, 16]).  It measures the QK stage on its own:
+ *   mode 0  the forward's QK: K decoded exactly to bf16 with the record's
+ *           power-of-two scale, bf16 MFMA 16x16x32, f32 accumulation;
+ *   mode 1  the scaled fp8 MFMA 16x16x128 of the FlyDSL page (module
+ *           docstring, "QK:"): K's e4m3 codes with the record scale as the
+ *           E8M0 operand scale; q per head and 128-dim block split into an
+ *           e4m3 hi part under scale s (the smallest power of two with
+ *           amax / s <= 448) and an e4m3 lo part = 32 (q / s - hi) under s / 32;
+ *   mode 2  mode 1 without the lo part;
+ *   mode 3  mode 1 with lo = 16 (q / s - hi) under s / 16 (a top-binade hi's
+ *           residual reaches 16, and 32 x 16 is past e4m3's 448).
+ * Rope (64 dims) uses the bf16 MFMA in every mode.  Rows outside [0, n_kv)
+ * read record 0.  Returns SMLA_EINVAL on bad arguments.
+ */
+int sparse_mla_qk_probe(const void* q, const void* kv, int64_t n_kv, const int32_t* rows, int64_t n,
+                        int32_t mode, float* scores, void* stream);
+
+/*
  * sparse_mla_decode_rows -- test hook: decode records rows[0..n) of kv to f32
  * out[n, 576] (latent * scale, then rope) exactly as the forward's QK stage
  * sees them (scale applied through its exponent field), cross-checked on the

@@ -8,7 +8,7 @@ there is no fallback path.
 """
 
 _PUBLIC = (
-    "MAX_HEADS", "MAX_SPLIT", "KernelTimer", "KvPool", "SmlaError", "cache_write", "decode_rows", "fwd",
+    "MAX_HEADS", "MAX_SPLIT", "KernelTimer", "KvPool", "SmlaError", "cache_write", "decode_rows", "qk_probe", "fwd",
     "fwd_noalloc", "NOALLOC_SCRATCH_BYTES", "fwd_paged", "fwd_v41", "v41_workspace_bytes", "mxfp8",
     "set_option", "split_for", "supported", "workspace", "workspace_bytes", "LIB_PATH", "EXPORTED",
 )

@@ -97,6 +97,8 @@ _lib.sparse_mla_mxfp8.argtypes = [_vp, _i64, _vp, _vp, _vp]
 _lib.sparse_mla_mxfp8.restype = ctypes.c_int
 _lib.sparse_mla_cache_write.argtypes = [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp]
 _lib.sparse_mla_cache_write.restype = ctypes.c_int
+_lib.sparse_mla_qk_probe.argtypes = [_vp, _vp, _i64, _vp, _i64, _i32, _vp, _vp]
+_lib.sparse_mla_qk_probe.restype = ctypes.c_int
 _lib.sparse_mla_decode_rows.argtypes = [_vp, _i64, _vp, _i64, _vp, _vp]
 _lib.sparse_mla_decode_rows.restype = ctypes.c_int
 _lib.sparse_mla_last_error.argtypes = []
@@ -112,7 +114,7 @@ EXPORTED = (
     "sparse_mla_supported", "sparse_mla_workspace_bytes", "sparse_mla_split_for", "sparse_mla_fwd",
     "sparse_mla_fwd_noalloc",
     "sparse_mla_fwd_paged", "sparse_mla_v41_workspace_bytes", "sparse_mla_fwd_v41", "sparse_mla_mxfp8",
-    "sparse_mla_cache_write", "sparse_mla_decode_rows", "sparse_mla_last_error", "sparse_mla_set_option",
+    "sparse_mla_cache_write", "sparse_mla_decode_rows", "sparse_mla_qk_probe", "sparse_mla_last_error", "sparse_mla_set_option",
     "sparse_mla_profile_begin", "sparse_mla_profile_end",
 )
 
@@ -437,6 +439,22 @@ def decode_rows(kv: torch.Tensor, rows: torch.Tensor) -> torch.Tensor:
     out = torch.empty(rows.numel(), 576, dtype=torch.float32, device=kv.device)
     _check(_lib.sparse_mla_decode_rows(_ptr(kv), kv.shape[0], _ptr(rows), rows.numel(),
                                        _ptr(out), _stream(kv.device)))
+    return out
+
+
+def qk_probe(q16: torch.Tensor, kv: torch.Tensor, rows: torch.Tensor, mode: int) -> torch.Tensor:
+    """QK dot products (no sm_scale) of tokens kv[rows] against 16 heads of q
+    (bf16 [16, 576]) as f32 [n, 16] (test hook): mode 0 the forward's bf16
+    path, 1 the scaled fp8 MFMA with the q hi/lo split (lo = 32 x residual),
+    2 its hi part only, 3 the split with lo = 16 x residual."""
+    if q16.dtype != torch.bfloat16 or tuple(q16.shape) != (16, 576) or not q16.is_contiguous():
+        raise ValueError("q16 must be contiguous bf16 [16, 576]")
+    if kv.dtype != torch.uint8 or kv.dim() != 2 or kv.shape[1] != RECORD_BYTES or not kv.is_contiguous():
+        raise ValueError(f"kv must be contiguous uint8 [N, {RECORD_BYTES}]")
+    rows = rows.to(torch.int32).contiguous()
+    out = torch.empty(rows.numel(), 16, dtype=torch.float32, device=kv.device)
+    _check(_lib.sparse_mla_qk_probe(_ptr(q16), _ptr(kv), kv.shape[0], _ptr(rows), rows.numel(), int(mode),
+                                    _ptr(out), _stream(kv.device)))
     return out
 
 

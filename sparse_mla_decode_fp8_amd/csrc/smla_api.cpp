@@ -487,6 +487,22 @@ int sparse_mla_decode_rows(const void* kv, int64_t n_kv, const int32_t* rows, in
   return SMLA_OK;
 }
 
+int sparse_mla_qk_probe(const void* q, const void* kv, int64_t n_kv, const int32_t* rows, int64_t n,
+                        int32_t mode, float* scores, void* stream) {
+  clear_err();
+  if (n < 0 || n % 16 != 0) return fail(SMLA_EINVAL, "n must be a non-negative multiple of 16, got %lld", (long long)n);
+  if (mode < 0 || mode > 3) return fail(SMLA_EINVAL, "mode must be 0, 1, 2 or 3, got %d", mode);
+  if (n_kv < 1) return fail(SMLA_EINVAL, "n_kv must be >= 1");
+  if (n / 16 > 0x7fffffff) return fail(SMLA_EINVAL, "n too large for one launch");
+  if (n == 0) return SMLA_OK;
+  if (!q || !kv || !rows || !scores) return fail(SMLA_EINVAL, "null pointer");
+  if (!aligned(q, 16) || !aligned(kv, 16) || !aligned(scores, 4)) return fail(SMLA_EINVAL, "q and kv must be 16-byte aligned");
+  hipError_t e = smla::launch_qk_probe((const uint16_t*)q, (const uint8_t*)kv, n_kv, rows, n, mode, scores,
+                                       (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "qk probe kernel launch");
+  return SMLA_OK;
+}
+
 int sparse_mla_cache_write(const void* latent, int64_t latent_stride,
                            const void* rope, int64_t rope_stride,
                            const int64_t* slots, int64_t n,

@@ -131,6 +131,11 @@ hipError_t launch_mxfp8(const float* y, int64_t n, uint8_t* codes, uint8_t* scal
 // Device address of the static scratch of sparse_mla_fwd_noalloc on device
 // dev (looked up once per device with that device current; smla_noalloc.hip).
 hipError_t noalloc_scratch(int dev, void** out);
+// Test hook (smla_qk_probe.hip): QK scores of n tokens (n a multiple of 16)
+// against 16 heads, by the forward's bf16 path (mode 0) or the scaled fp8
+// MFMA with the q hi/lo split (mode 1; mode 2: hi only).
+hipError_t launch_qk_probe(const uint16_t* q, const uint8_t* kv, int64_t n_kv, const int32_t* rows, int64_t n,
+                           int mode, float* scores, hipStream_t s);
 hipError_t launch_decode_rows(const uint8_t* kv, int64_t n_kv, const int32_t* rows, int64_t n,
                               float* out, hipStream_t s);
 
