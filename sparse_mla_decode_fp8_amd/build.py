@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libsmla.so")
-SOURCES = ["smla_kernels.hip", "smla_wide.hip", "smla_v41.hip", "smla_noalloc.hip", "smla_qk_probe.hip", "smla_api.cpp"]
+SOURCES = ["smla_kernels.hip", "smla_wide.hip", "smla_wide64.hip", "smla_v41.hip", "smla_noalloc.hip", "smla_qk_probe.hip", "smla_api.cpp"]
 ARCH = "gfx950"
 
 

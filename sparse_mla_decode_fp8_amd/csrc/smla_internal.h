@@ -100,9 +100,9 @@ struct CacheWriteParams {
 };
 
 // Head tiling: tiles of 16 heads.  Tokens per tile: 128 for the H <= 16
-// kernel, 64 for the wide-head kernel.
+// kernel, 64 for the 17..32-head kernel, 32 for the kernel above 32 heads.
 inline int head_tiles(int H) { return (H + 15) / 16; }
-inline int tile_tokens(int H) { return head_tiles(H) == 1 ? 128 : 64; }
+inline int tile_tokens(int H) { return head_tiles(H) == 1 ? 128 : head_tiles(H) == 2 ? 64 : 32; }
 // Head groups of a row: the wide-head kernel takes at most 64 heads per unit.
 inline int head_groups(int H) { return (H + 63) / 64; }
 
@@ -117,8 +117,10 @@ struct Events {
 // (order, and row_tiles from indptr when there was no scan) when `sort`.
 hipError_t launch_plan(const PlanParams& p, bool sort, Events ev, hipStream_t s);
 hipError_t launch_fwd(const FwdParams& p, Events ev, hipStream_t s);
-// The wide-head forward (17 <= H <= 64), smla_wide.hip.
+// The wide-head forward: 17 <= H <= 32 (smla_wide.hip), above 32 heads the
+// kernel of smla_wide64.hip (launch_fwd_wide64).
 hipError_t launch_fwd_wide(const FwdParams& p, Events ev, hipStream_t s);
+hipError_t launch_fwd_wide64(const FwdParams& p, Events ev, hipStream_t s);
 // Device address of the library's zero record on the current device.
 hipError_t zero_record_address(const uint8_t** out);
 hipError_t launch_combine(const CombineParams& p, Events ev, hipStream_t s);

@@ -1,6 +1,6 @@
-// Wide-head forward: 17 <= H <= 128 heads (HT = 2 or 4 tiles of 16 heads;
-// above 64 heads a row's heads form groups of 64, each its own unit), the
-// prefill and wide decode shapes.  Same method as the H <= 16 kernel
+// Wide-head forward for 17 <= H <= 32 heads (HT = 2 tiles of 16 heads; the
+// kernel is written for HT tiles, and above 32 heads the forward uses the
+// kernel of smla_wide64.hip).  Same method as the H <= 16 kernel
 // (vLLM API page "vllm.models.kimi_k3.amd.ops.flydsl_sparse_mla_gfx950",
 // module docstring; split chunks merged as on the K2-back page,
 // stage_combine), laid out so that every record is converted once per head
@@ -419,7 +419,7 @@ static hipError_t launch_fwdw_t(const FwdParams& p, Events ev, hipStream_t s) {
 hipError_t launch_fwd_wide(const FwdParams& p, Events ev, hipStream_t s) {
   const int ht = head_tiles(p.H);
   if (ht == 2) return launch_fwdw_t<2>(p, ev, s);
-  if (ht >= 3 && ht <= 8) return launch_fwdw_t<4>(p, ev, s);  // above 64 heads: groups of 64
+  if (ht >= 3 && ht <= 8) return launch_fwd_wide64(p, ev, s);  // above 64 heads: groups of 64
   return hipErrorInvalidValue;
 }
 

@@ -1,0 +1,415 @@
+// Wide-head forward for 33 <= H <= 128 heads (up to 64 heads per unit; above
+// 64 a row's heads form groups of 64, each its own unit): the prefill and
+// wide decode shapes.  Same method as the other forward kernels (vLLM API
+// page "vllm.models.kimi_k3.amd.ops.flydsl_sparse_mla_gfx950", module
+// docstring; split chunks merged as on the K2-back page, stage_combine).
+//
+// The eight waves of a block have two roles.  Waves w and w + 4 of a block
+// run on the same SIMD, so every SIMD holds one wave of each role, and the
+// conversion-heavy score work of one overlaps the MFMA-heavy P.V work of the
+// other instead of both waves of a SIMD doing the same phase at once.
+//   QK waves 0..3: wave i scores head tile i (heads 16i .. 16i+15, q in
+//       registers) against every token of a 32-token tile, keeps the running
+//       maximum and sum of its heads, and writes the tile's P (f16, lazy
+//       reference per head) and each head's rescale factor to LDS.
+//   PV waves 4..7: wave 4 + j owns dims 128j .. 128j+127, one scale block,
+//       for all 64 heads, so the block's per-token V scale folds into P; it
+//       accumulates O over the tile the QK waves finished one step before.
+//       These waves also run the gather: index tiles into an LDS ring and
+//       the records (latent rows, scales and rope) of 8 tokens per tile.
+// One barrier per step: at step s the QK waves work on tile s while the PV
+// waves work on tile s - 1 and queue the records of tile s + 4 (four tiles
+// of records in flight, six LDS stages: s - 1, s, and four landing).  P,
+// the V scales and the rescale factors are double-buffered by tile parity.
+
+#include <hip/hip_ext.h>
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "smla_device.h"
+
+namespace smla {
+namespace w64 {
+
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kHeads = 64;
+constexpr int kTile = 32;                       // tokens per step
+constexpr int kAhead = 4;                       // tiles of records queued ahead of the QK tile
+constexpr int kStages = kAhead + 2;             // LDS record stages
+constexpr int kRing = 16;                       // index ring slots (tiles), >= 2 kAhead + 1
+constexpr int kPair = 2 * kLat + 16;            // two latent rows + 16-B pad
+constexpr int kLatStage = (kTile / 2) * kPair;  // 16,640 B
+constexpr int kSideStage = kTile * kSideTok;    // 4,608 B
+constexpr int kPitch = 96;                      // P and scale rows: 32 f16 + pad (no 128-bit read conflicts)
+// Vector-memory instructions a PV wave issues per tile: 4 latent DMAs (token
+// pairs) and 2 side DMAs (72 chunks of 16 B); one index DMA besides.
+constexpr int kTileVm = 6;
+constexpr int kQLoads = 18;                     // q loads per lane (16 latent + 2 rope)
+
+constexpr int kLatOff = 0;
+constexpr int kSideOff = kLatOff + kStages * kLatStage;
+constexpr int kPxOff = kSideOff + kStages * kSideStage;  // P f16 [buf 2][head 64][token], pitch kPitch
+constexpr int kPxBuf = kHeads * kPitch;
+constexpr int kSxOff = kPxOff + 2 * kPxBuf;               // V scales f16 [buf 2][block 4][token]
+constexpr int kSxBuf = 4 * kPitch;
+constexpr int kAxOff = kSxOff + 2 * kSxBuf;               // rescale factors f32 [buf 2][head t 16][tile 4]
+constexpr int kAxBuf = kHeads * 4;
+constexpr int kRingOff = kAxOff + 2 * kAxBuf;             // index entries [slot][32]
+constexpr int kTabOff = kRingOff + kRing * kTile * 4;     // record addresses [PV wave][8]
+constexpr int kKeyOff = kTabOff + 4 * 64;                 // key masks u32 [slot]: bit i = token i is a key
+constexpr int kRedOff = kKeyOff + kRing * 4;              // unit_tiles' reduction; later {l, m} per head
+constexpr int kBytes = kRedOff + kHeads * 8;
+static_assert(kBytes <= 160 * 1024, "LDS budget");
+static_assert(kStages >= kAhead + 2 && kRing >= 2 * kAhead + 1, "pipeline depth");
+
+// vmcnt <= n for a wave-uniform n in [0, 24]
+__device__ __forceinline__ void wait_vm_n(int n) {
+  switch (n) {
+#define SMLA_W(k) case k: wait_vm<k>(); break;
+    SMLA_W(0) SMLA_W(1) SMLA_W(2) SMLA_W(3) SMLA_W(4) SMLA_W(5) SMLA_W(6) SMLA_W(7) SMLA_W(8)
+    SMLA_W(9) SMLA_W(10) SMLA_W(11) SMLA_W(12) SMLA_W(13) SMLA_W(14) SMLA_W(15) SMLA_W(16)
+    SMLA_W(17) SMLA_W(18) SMLA_W(19) SMLA_W(20) SMLA_W(21) SMLA_W(22) SMLA_W(23)
+#undef SMLA_W
+    default: wait_vm<24>(); break;
+  }
+}
+
+__device__ __forceinline__ uint32_t row_off(int tau) { return (tau >> 1) * kPair + (tau & 1) * kLat; }
+
+}  // namespace w64
+
+__global__ __launch_bounds__(w64::kThreads, 1) void smla_fwdw64_kernel(FwdParams p) {
+  using namespace w64;
+  __shared__ __attribute__((aligned(1024))) uint8_t s_lds[kBytes];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int t = lane & 15;
+  const int g = lane >> 4;
+
+  int rank, sub;
+  if (p.hg == 1) fwd_unit(p.S, p.order == nullptr, rank, sub);  // one head group: sub is the chunk
+  else xcd_unit(p.S * p.hg, rank, sub);
+  if (rank >= p.T) return;
+  const int chunk = sub % p.S;
+  const int h0 = kHeads * (sub / p.S);  // first head of this unit's head group
+
+  const uint32_t base = lds_addr(s_lds);
+  const int row = p.order ? p.order[rank] : rank;
+  const int beg = p.indptr[row];
+  const int len = max(p.indptr[row + 1] - beg, 0);
+  const int tiles = unit_tiles<kThreads>(p, row, beg, len, kTile, (int*)(s_lds + kRedOff));
+  const int ct = (tiles + p.S - 1) / p.S;
+  const int t0 = min(chunk * ct, tiles);
+  const int t1 = min(t0 + ct, tiles);
+  const int unit = row * p.S + chunk;
+  const bool split = p.S > 1;
+  const int H = p.H;
+  const int Hl = min(H - h0, kHeads);  // heads of this group
+
+  if (t0 >= t1) {  // nothing to attend: zero output and the sink's lse, or an empty partial
+    if (split) {
+      for (int hh = h0 + tid; hh < h0 + Hl; hh += kThreads) p.part_lse[(int64_t)unit * H + hh] = -INFINITY;
+    } else {
+      for (int e = tid; e < Hl * (kLat / 8); e += kThreads) {
+        const int hh = h0 + e / (kLat / 8), d = (e % (kLat / 8)) * 8;
+        *(v4i*)(p.out + row * p.o_st + hh * p.o_sh + d) = v4i{0, 0, 0, 0};
+      }
+      if (p.lse)
+        for (int hh = h0 + tid; hh < h0 + Hl; hh += kThreads)
+          p.lse[(int64_t)row * H + hh] = p.sink ? p.sink[hh] : -INFINITY;
+    }
+    return;
+  }
+
+  const uint32_t px0 = base + kPxOff;
+  const uint32_t sx0 = base + kSxOff;
+  const uint32_t ax0 = base + kAxOff;
+  const uint32_t keys = base + kKeyOff;
+  const uint32_t lm = base + kRedOff;  // {l, m} of head h at lm + 8h (epilogue)
+  auto lat_at = [&](int st) -> uint32_t { return base + kLatOff + st * kLatStage; };
+  auto side_at = [&](int st) -> uint32_t { return base + kSideOff + st * kSideStage; };
+
+  if (w < 4) {
+    // ================================================================ QK waves
+    const int i = w;  // head tile
+    // q of head 16i + t (lane (t, g)): latent K-step 2m / 2m+1 = dims 64m +
+    // 16g + [0..7] / [8..15], rope K-step r = dims 512 + 32r + 8g + [0..7].
+    // Heads >= H load head 0 (every lane issues the same loads) and are zeroed.
+    const int hq = 16 * i + t;
+    const bool hq_ok = hq < Hl;
+    v4i qr[kQLoads];
+    {
+      const uint64_t qa = (uint64_t)(uintptr_t)(p.q + row * p.q_st + (int64_t)(h0 + (hq_ok ? hq : 0)) * p.q_sh);
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        gload16(qr[2 * m], qa + 2 * (64 * m + 16 * g));
+        gload16(qr[2 * m + 1], qa + 2 * (64 * m + 16 * g + 8));
+      }
+      gload16(qr[16], qa + 2 * (kLat + 8 * g));
+      gload16(qr[17], qa + 2 * (kLat + 32 + 8 * g));
+    }
+    wait_vm<0>();
+#pragma unroll
+    for (int k = 0; k < kQLoads; ++k) asm volatile("" : "+v"(qr[k]));
+    v8bf qlat[16], qrope[2];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) qlat[k] = __builtin_bit_cast(v8bf, hq_ok ? qr[k] : v4i{0, 0, 0, 0});
+#pragma unroll
+    for (int k = 0; k < 2; ++k) qrope[k] = __builtin_bit_cast(v8bf, hq_ok ? qr[16 + k] : v4i{0, 0, 0, 0});
+
+    float m_ref = -INFINITY;  // head 16i + t: reference max (log2 units)
+    float l_run = 0.0f;       // this lane's part of the head's sum of P
+    const v2h ones = v2h{(_Float16)1.0f, (_Float16)1.0f};
+    int st = 0;  // stage of tile s
+    for (int s = t0; s <= t1; ++s) {
+      // tile s's records have landed; the PV waves are done with tile s - 2
+      // (its P, scales and factors: this tile's buffers)
+      __syncthreads();
+      if (s < t1) {
+        const int b = s & 1;
+        const uint32_t lat = lat_at(st);
+        const uint32_t side = side_at(st);
+        const uint32_t kmask = *LDSP(uint32_t, keys + 4 * (s & (kRing - 1)));
+        // scores: lane (t, g) gets head 16i + t, tokens 16gi + 4g + r
+        float x[2][4];
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int gi = 0; gi < 2; ++gi) {
+          const int tok = 16 * gi + t;  // the token whose K row this lane feeds
+          const uint32_t qk_row = row_off(tok) + 16 * g;
+          const uint32_t qk_a = qk_row + ((t & 1) ? 128u : 0u);
+          const uint32_t qk_b = qk_row - ((t & 1) ? 128u : 0u);
+          v4i kr[8];
+#pragma unroll
+          for (int m = 0; m < 8; ++m) kr[m] = *LDSP(v4i, lat + ((m & 2) ? qk_b : qk_a) + 64 * m);
+          const v4f ksc = *LDSP(v4f, side + kSideTok * tok);
+          const v4i rp0 = *LDSP(v4i, side + kSideTok * tok + 16 + 16 * g);
+          const v4i rp1 = *LDSP(v4i, side + kSideTok * tok + 16 + 64 + 16 * g);
+          v4f acc0 = v4f{0, 0, 0, 0}, acc1 = v4f{0, 0, 0, 0};
+          acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, rp0), qrope[0], acc0, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, rp1), qrope[1], acc1, 0, 0, 0);
+#pragma unroll
+          for (int m = 0; m < 8; ++m) {
+            const float sc = ksc[m >> 1];
+            v2bf a0, a1, a2, a3, b0, b1, b2, b3;
+            cvt4_bf16(kr[m].x, sc, a0, a1);
+            cvt4_bf16(kr[m].y, sc, a2, a3);
+            cvt4_bf16(kr[m].z, sc, b0, b1);
+            cvt4_bf16(kr[m].w, sc, b2, b3);
+            const v8bf ka = {a0.x, a0.y, a1.x, a1.y, a2.x, a2.y, a3.x, a3.y};
+            const v8bf kb = {b0.x, b0.y, b1.x, b1.y, b2.x, b2.y, b3.x, b3.y};
+            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qlat[2 * m], acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qlat[2 * m + 1], acc1, 0, 0, 0);
+          }
+          const v4f S = acc0 + acc1;
+          const uint32_t kb = kmask >> (16 * gi + 4 * g);  // which of tokens 16gi + 4g + r are keys
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            x[gi][r] = ((kb >> r) & 1u) ? S[r] * p.c_log2 : -INFINITY;
+            tmax = fmax_(tmax, x[gi][r]);
+          }
+          // V scale of block g for token tok, clamped to 2^7, as f16 (one wave writes them)
+          if (i == 0)
+            *LDSP(_Float16, sx0 + b * kSxBuf + kPitch * g + 2 * tok) = (_Float16)__builtin_fminf(ksc[g], kScaleCap);
+        }
+        // the head's tile max; its reference moves only when the max exceeds
+        // it by more than kTau, and the factor tells the PV waves to rescale O
+        tmax = xor_max(tmax);
+        float alpha = 1.0f;
+        if (tmax > m_ref + kTau) {
+          alpha = m_ref == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_ref - tmax);
+          l_run *= alpha;
+          m_ref = tmax;
+        }
+        if (g == 0) *LDSP(float, ax0 + b * kAxBuf + 16 * t + 4 * i) = alpha;
+        const float mu = m_ref == -INFINITY ? 0.0f : m_ref;
+#pragma unroll
+        for (int gi = 0; gi < 2; ++gi) {
+          _Float16 ph[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) ph[r] = (_Float16)__builtin_amdgcn_exp2f(x[gi][r] - mu + kShift);
+          l_run = __builtin_amdgcn_fdot2(v2h{ph[0], ph[1]}, ones, l_run, false);
+          l_run = __builtin_amdgcn_fdot2(v2h{ph[2], ph[3]}, ones, l_run, false);
+          *LDSP(v2i, px0 + b * kPxBuf + kPitch * (16 * i + t) + 2 * (16 * gi + 4 * g)) =
+              __builtin_bit_cast(v2i, (v4h{ph[0], ph[1], ph[2], ph[3]}));
+        }
+        st = st == kStages - 1 ? 0 : st + 1;
+      }
+    }
+    // the head's sum and reference for the PV waves' normalisation
+    const float l = xor_sum(l_run);
+    if (g == 0) *LDSP(v2f, lm + 8 * (16 * i + t)) = v2f{l, m_ref};
+    __syncthreads();
+    return;
+  }
+
+  // ================================================================== PV waves
+  const int j = w - 4;  // scale block: dims 128j .. 128j+127; gather: tokens 8j .. 8j+7
+  const __amdgpu_buffer_rsrc_t irs = idx_rsrc(p.indices, p.idx_bytes);
+  const uint8_t* const zero = p.zero;
+  auto ring_at = [&](int n) -> uint32_t { return base + kRingOff + (n & (kRing - 1)) * kTile * 4; };
+  const uint32_t tab = base + kTabOff + 64 * j;  // this wave's 8 record addresses
+
+  // I: index DMA of this wave's 8 entries of tile n (bounded reads: positions
+  // past nnz read 0; positions past the row are masked where they are used).
+  auto issue_idx = [&](int n) {
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(ring_at(n) + 32 * j);
+    if (lane < 8) buf_dma4(irs, (uint32_t)(beg + n * kTile + 8 * j + lane) * 4u, dst);
+  };
+  // record addresses of this wave's 8 tokens of tile n (no key: the zero
+  // record), and their bits of the tile's key mask
+  auto fill_table = [&](int n) {
+    bool ok = false;
+    if (lane < 8) {
+      const int raw = *LDSP(int, ring_at(n) + 4 * (8 * j + lane));
+      ok = (n * kTile + 8 * j + lane < len) && p.km.valid(raw);
+      *LDSP(uint64_t, tab + 8 * lane) = (uint64_t)(uintptr_t)(ok ? key_addr(p, raw) : zero);
+    }
+    const uint32_t bits = (uint32_t)__ballot(ok) & 0xFFu;
+    if (lane == 0) *LDSP(uint8_t, keys + 4 * (n & (kRing - 1)) + j) = (uint8_t)bits;
+  };
+  // L: latent (4 token pairs; lanes 0..31 the even token, 32..63 the odd one,
+  // whose lane position q loads chunk q ^ 8) and side data (scales + rope,
+  // 9 chunks per token) of this wave's tokens into stage st.
+  const uint32_t src_chunk = 16u * (uint32_t)((lane & 31) ^ ((lane >> 5) << 3));
+  auto issue_tile = [&](int st) {
+    uint64_t a[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) a[k] = *LDSP(uint64_t, tab + 8 * (2 * k + (lane >> 5)));
+    const uint64_t s0 = *LDSP(uint64_t, tab + 8 * (lane / kSideChunks));
+    const uint64_t s1 = *LDSP(uint64_t, tab + 8 * 7);
+    const uint32_t dst = lat_at(st) + 4 * j * kPair;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      dma16((const uint8_t*)(uintptr_t)(a[k] + src_chunk), __builtin_amdgcn_readfirstlane(dst + k * kPair));
+    const uint32_t sd = side_at(st) + 8 * j * kSideTok;
+    dma16((const uint8_t*)(uintptr_t)(s0 + kScaleOff + 16 * (lane % kSideChunks)), __builtin_amdgcn_readfirstlane(sd));
+    // chunks 64 .. 71: token 7, pieces 1 .. 8
+    if (lane < 8) dma16((const uint8_t*)(uintptr_t)(s1 + kScaleOff + 16 * (lane + 1)),
+                        __builtin_amdgcn_readfirstlane(sd + 1024));
+  };
+
+  // ---- prologue: index tiles t0 .. t0+3, then records of tiles t0 .. t0+3,
+  // each followed by the index tile four ahead.  From here on the issue order
+  // is ... L(n) I(n+4) L(n+1) I(n+5) ..., so waiting for I(n+4) covers L(n).
+#pragma unroll
+  for (int k = 0; k < kAhead; ++k)
+    if (t0 + k < t1) issue_idx(t0 + k);
+#pragma unroll
+  for (int k = 0; k < kAhead; ++k) {
+    if (t0 + k < t1) {
+      // issued after I(t0+k): later index tiles, and L(t0+k') I(t0+k'+4) for k' < k
+      int after = 0;
+#pragma unroll
+      for (int k2 = k + 1; k2 < kAhead; ++k2) after += t0 + k2 < t1;
+#pragma unroll
+      for (int k2 = 0; k2 < k; ++k2) after += kTileVm + (t0 + k2 + kAhead < t1);
+      wait_vm_n(after);
+      fill_table(t0 + k);
+      issue_tile(k);
+      if (t0 + k + kAhead < t1) issue_idx(t0 + k + kAhead);
+    }
+  }
+
+  v4f O[4][8];  // O^T slices: dims 128j + 16dt + 4g + [0..3], head 16ht + t
+#pragma unroll
+  for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) O[ht][dt] = v4f{0, 0, 0, 0};
+
+  // transposed V reads: lane (t, g) loads token tv = 8g + t/2, bytes
+  // 8(t&1) .. +7 of chunk 8j + dt (stored at (8j + dt) ^ 8 in odd rows)
+  const int tv = 8 * g + (t >> 1);
+  const uint32_t pv_off = row_off(tv) + 128 * (j ^ (tv & 1)) + 8 * (t & 1);
+
+  int st_q = 0;  // stage of tile s (s - t0 mod kStages)
+  for (int s = t0; s <= t1; ++s) {
+    // this wave's records of tile s and index tile s+4 have landed: after
+    // I(s+4) it queued L(x) I(x+4) for x = s+1 .. s+3 (those that exist)
+    {
+      int after = 0;
+#pragma unroll
+      for (int x = 1; x < kAhead; ++x) after += (s + x < t1 ? kTileVm : 0) + (s + x + kAhead < t1);
+      wait_vm_n(after);
+    }
+    __syncthreads();
+    const int st_l = st_q + kAhead >= kStages ? st_q + kAhead - kStages : st_q + kAhead;  // tile s+4
+    if (s + kAhead < t1) {
+      fill_table(s + kAhead);
+      issue_tile(st_l);
+      if (s + 2 * kAhead < t1) issue_idx(s + 2 * kAhead);
+    }
+    if (s > t0) {
+      // ---- PV of tile s - 1: O^T[d, h] += V^T[d, tok] P'^T[tok, h]
+      const int n = s - 1;
+      const int b = n & 1;
+      const int st_p = st_q == 0 ? kStages - 1 : st_q - 1;
+      const uint32_t vaddr = lat_at(st_p) + pv_off;
+      v2i vr[8];
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) vr[dt] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(LDSP(v2i, vaddr + 16 * dt));
+      const v8h sr = *LDSP(v8h, sx0 + b * kSxBuf + kPitch * j + 16 * g);
+      const v4f al = *LDSP(v4f, ax0 + b * kAxBuf + 16 * t);
+      if (__builtin_amdgcn_ballot_w64(al.x != 1.0f || al.y != 1.0f || al.z != 1.0f || al.w != 1.0f)) {
+#pragma unroll
+        for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt) O[ht][dt] *= al[ht];
+      }
+      v8h vh[8];
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) vh[dt] = cvt8_f16(vr[dt]);
+#pragma unroll
+      for (int ht = 0; ht < 4; ++ht) {
+        const v8h pr = *LDSP(v8h, px0 + b * kPxBuf + kPitch * (16 * ht + t) + 16 * g);
+        const v8h pb = pr * sr;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) O[ht][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vh[dt], pb, O[ht][dt], 0, 0, 0);
+      }
+    }
+    st_q = st_q == kStages - 1 ? 0 : st_q + 1;
+  }
+  __syncthreads();  // every head's {l, m} is written
+
+  // ---- epilogue: this wave's 128 dims of every head (split: a partial
+  // without the sink, which the combine folds in)
+#pragma unroll
+  for (int ht = 0; ht < 4; ++ht) {
+    const int hl = 16 * ht + t;  // head of the group
+    const int h = h0 + hl;       // head of the row
+    const bool h_ok = hl < Hl;
+    const v2f lmv = *LDSP(v2f, lm + 8 * hl);
+    const Norm nm = finish_norm(lmv.x, lmv.y, (split || !h_ok) ? -INFINITY : sink_log2(p.sink, h));
+    if (j == 0 && g == 0 && h_ok) {
+      if (split) p.part_lse[(int64_t)unit * H + h] = nm.lse2;
+      else if (p.lse) p.lse[(int64_t)row * H + h] = nm.lse2 * kLn2;
+    }
+    if (h_ok) {
+      if (split) {
+        uint16_t* const po = p.part_o + ((int64_t)unit * H + h) * kLat + 128 * j;
+        st_part16(po, g, &O[ht][0], nm.scale);
+        st_part16(po + 64, g, &O[ht][4], nm.scale);
+      } else {
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+          const v4f acc = O[ht][dt] * nm.scale;
+          const int d = 128 * j + 16 * dt + 4 * g;
+          const uint32_t w0 = f32_to_bf16_rne(acc.x) | ((uint32_t)f32_to_bf16_rne(acc.y) << 16);
+          const uint32_t w1 = f32_to_bf16_rne(acc.z) | ((uint32_t)f32_to_bf16_rne(acc.w) << 16);
+          *(v2i*)(p.out + row * p.o_st + h * p.o_sh + d) = v2i{(int)w0, (int)w1};
+        }
+      }
+    }
+  }
+}
+
+hipError_t launch_fwd_wide64(const FwdParams& p, Events ev, hipStream_t s) {
+  const int64_t blocks = p.hg == 1 ? fwd_grid(p.T, p.S, p.order == nullptr) : xcd_grid(p.T, p.S * p.hg);
+  hipExtLaunchKernelGGL(smla_fwdw64_kernel, dim3((unsigned)blocks), dim3(w64::kThreads), 0, s, ev.start,
+                        ev.stop, 0, p);
+  return hipGetLastError();
+}
+
+}  // namespace smla
