@@ -55,7 +55,7 @@ HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 RECORD_BYTES = 656
 KERNEL_SRCS = [os.path.join(ROOT, "sparse_mla_decode_fp8_amd", "csrc", f)
-               for f in ("smla_kernels.hip", "smla_wide.hip", "smla_device.h", "smla_internal.h")]
+               for f in ("smla_kernels.hip", "smla_wide.hip", "smla_wide64.hip", "smla_device.h", "smla_internal.h")]
 COUNTERS = os.path.join(ROOT, "profiles", "fwd_decode_T64_H16_counters.txt")
 
 

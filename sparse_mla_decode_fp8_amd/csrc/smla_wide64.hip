@@ -18,9 +18,11 @@
 //       These waves also run the gather: index tiles into an LDS ring and
 //       the records (latent rows, scales and rope) of 8 tokens per tile.
 // One barrier per step: at step s the QK waves work on tile s while the PV
-// waves work on tile s - 1 and queue the records of tile s + 4 (four tiles
-// of records in flight, six LDS stages: s - 1, s, and four landing).  P,
+// waves work on tile s - 1 and queue the records of tile s + 3 (three tiles
+// of records in flight, five LDS stages: s - 1, s, and three landing).  P,
 // the V scales and the rescale factors are double-buffered by tile parity.
+// The PV waves queue the records at raised wave priority, ahead of the QK
+// wave's work on their SIMD.
 
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
@@ -35,7 +37,7 @@ constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kHeads = 64;
 constexpr int kTile = 32;                       // tokens per step
-constexpr int kAhead = 4;                       // tiles of records queued ahead of the QK tile
+constexpr int kAhead = 3;                       // tiles of records queued ahead of the QK tile
 constexpr int kStages = kAhead + 2;             // LDS record stages
 constexpr int kRing = 16;                       // index ring slots (tiles), >= 2 kAhead + 1
 constexpr int kPair = 2 * kLat + 16;            // two latent rows + 16-B pad
@@ -291,16 +293,16 @@ __global__ __launch_bounds__(w64::kThreads, 1) void smla_fwdw64_kernel(FwdParams
                         __builtin_amdgcn_readfirstlane(sd + 1024));
   };
 
-  // ---- prologue: index tiles t0 .. t0+3, then records of tiles t0 .. t0+3,
-  // each followed by the index tile four ahead.  From here on the issue order
-  // is ... L(n) I(n+4) L(n+1) I(n+5) ..., so waiting for I(n+4) covers L(n).
+  // ---- prologue: index tiles t0 .. t0+2, then records of tiles t0 .. t0+2,
+  // each followed by the index tile three ahead.  From here on the issue
+  // order is ... L(n) I(n+3) L(n+1) I(n+4) ..., so waiting for I(n+3) covers L(n).
 #pragma unroll
   for (int k = 0; k < kAhead; ++k)
     if (t0 + k < t1) issue_idx(t0 + k);
 #pragma unroll
   for (int k = 0; k < kAhead; ++k) {
     if (t0 + k < t1) {
-      // issued after I(t0+k): later index tiles, and L(t0+k') I(t0+k'+4) for k' < k
+      // issued after I(t0+k): later index tiles, and L(t0+k') I(t0+k'+3) for k' < k
       int after = 0;
 #pragma unroll
       for (int k2 = k + 1; k2 < kAhead; ++k2) after += t0 + k2 < t1;
@@ -326,8 +328,8 @@ __global__ __launch_bounds__(w64::kThreads, 1) void smla_fwdw64_kernel(FwdParams
 
   int st_q = 0;  // stage of tile s (s - t0 mod kStages)
   for (int s = t0; s <= t1; ++s) {
-    // this wave's records of tile s and index tile s+4 have landed: after
-    // I(s+4) it queued L(x) I(x+4) for x = s+1 .. s+3 (those that exist)
+    // this wave's records of tile s and index tile s+3 have landed: after
+    // I(s+3) it queued L(x) I(x+3) for x = s+1, s+2 (those that exist)
     {
       int after = 0;
 #pragma unroll
@@ -335,12 +337,14 @@ __global__ __launch_bounds__(w64::kThreads, 1) void smla_fwdw64_kernel(FwdParams
       wait_vm_n(after);
     }
     __syncthreads();
-    const int st_l = st_q + kAhead >= kStages ? st_q + kAhead - kStages : st_q + kAhead;  // tile s+4
+    const int st_l = st_q + kAhead >= kStages ? st_q + kAhead - kStages : st_q + kAhead;  // tile s+3
+    __builtin_amdgcn_s_setprio(2);
     if (s + kAhead < t1) {
       fill_table(s + kAhead);
       issue_tile(st_l);
       if (s + 2 * kAhead < t1) issue_idx(s + 2 * kAhead);
     }
+    __builtin_amdgcn_s_setprio(0);
     if (s > t0) {
       // ---- PV of tile s - 1: O^T[d, h] += V^T[d, tok] P'^T[tok, h]
       const int n = s - 1;
