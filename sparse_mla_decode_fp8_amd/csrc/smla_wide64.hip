@@ -8,21 +8,25 @@
 // run on the same SIMD, so every SIMD holds one wave of each role, and the
 // conversion-heavy score work of one overlaps the MFMA-heavy P.V work of the
 // other instead of both waves of a SIMD doing the same phase at once.
-//   QK waves 0..3: wave i scores head tile i (heads 16i .. 16i+15, q in
-//       registers) against every token of a 32-token tile, keeps the running
-//       maximum and sum of its heads, and writes the tile's P (f16, lazy
-//       reference per head) and each head's rescale factor to LDS.
+//   QK waves 0..3: wave (h, k) = (w & 1, w >> 1) scores heads 32h .. 32h+31
+//       (q in registers) against tokens 16k .. 16k+15 of each 32-token tile,
+//       so each K element is converted for 32 heads at once.  The two token
+//       halves are two softmax streams: each wave keeps its own running
+//       reference and sum per head, writes P relative to its reference and
+//       publishes the reference.  References are integers (log2 units), so
+//       every factor between them is an exact power of two.
 //   PV waves 4..7: wave 4 + j owns dims 128j .. 128j+127, one scale block,
 //       for all 64 heads, so the block's per-token V scale folds into P; it
-//       accumulates O over the tile the QK waves finished one step before.
-//       These waves also run the gather: index tiles into an LDS ring and
-//       the records (latent rows, scales and rope) of 8 tokens per tile.
+//       keeps O relative to the larger of the two streams' references,
+//       scales each stream's P to it, and accumulates O over the tile scored
+//       one step before.  These waves also run the gather: index tiles into
+//       an LDS ring and the records (latent rows, scales and rope) of 8
+//       tokens per tile.
 // One barrier per step: at step s the QK waves work on tile s while the PV
 // waves work on tile s - 1 and queue the records of tile s + 3 (three tiles
-// of records in flight, five LDS stages: s - 1, s, and three landing).  P,
-// the V scales and the rescale factors are double-buffered by tile parity.
-// The PV waves queue the records at raised wave priority, ahead of the QK
-// wave's work on their SIMD.
+// of records in flight, five LDS stages).  P, the V scales and the
+// references are double-buffered by tile parity.  The two streams are merged
+// like two chunks of a split row (K2-back page, stage_combine).
 
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
@@ -55,13 +59,13 @@ constexpr int kPxOff = kSideOff + kStages * kSideStage;  // P f16 [buf 2][head 6
 constexpr int kPxBuf = kHeads * kPitch;
 constexpr int kSxOff = kPxOff + 2 * kPxBuf;               // V scales f16 [buf 2][block 4][token]
 constexpr int kSxBuf = 4 * kPitch;
-constexpr int kAxOff = kSxOff + 2 * kSxBuf;               // rescale factors f32 [buf 2][head t 16][tile 4]
-constexpr int kAxBuf = kHeads * 4;
-constexpr int kRingOff = kAxOff + 2 * kAxBuf;             // index entries [slot][32]
+constexpr int kMxOff = kSxOff + 2 * kSxBuf;               // stream references f32 [buf 2][stream 2][head t 16][tile 4]
+constexpr int kMxBuf = 2 * kHeads * 4;
+constexpr int kRingOff = kMxOff + 2 * kMxBuf;             // index entries [slot][32]
 constexpr int kTabOff = kRingOff + kRing * kTile * 4;     // record addresses [PV wave][8]
 constexpr int kKeyOff = kTabOff + 4 * 64;                 // key masks u32 [slot]: bit i = token i is a key
-constexpr int kRedOff = kKeyOff + kRing * 4;              // unit_tiles' reduction; later {l, m} per head
-constexpr int kBytes = kRedOff + kHeads * 8;
+constexpr int kRedOff = kKeyOff + kRing * 4;              // unit_tiles' reduction; later {l, m} per head and stream
+constexpr int kBytes = kRedOff + kHeads * 16;
 static_assert(kBytes <= 160 * 1024, "LDS budget");
 static_assert(kStages >= kAhead + 2 && kRing >= 2 * kAhead + 1, "pipeline depth");
 
@@ -127,22 +131,26 @@ __global__ __launch_bounds__(w64::kThreads, 1) void smla_fwdw64_kernel(FwdParams
 
   const uint32_t px0 = base + kPxOff;
   const uint32_t sx0 = base + kSxOff;
-  const uint32_t ax0 = base + kAxOff;
+  const uint32_t mx0 = base + kMxOff;
   const uint32_t keys = base + kKeyOff;
-  const uint32_t lm = base + kRedOff;  // {l, m} of head h at lm + 8h (epilogue)
+  const uint32_t lm = base + kRedOff;  // {l, m} of head h, stream k at lm + 16h + 8k (epilogue)
   auto lat_at = [&](int st) -> uint32_t { return base + kLatOff + st * kLatStage; };
   auto side_at = [&](int st) -> uint32_t { return base + kSideOff + st * kSideStage; };
 
   if (w < 4) {
     // ================================================================ QK waves
-    const int i = w;  // head tile
-    // q of head 16i + t (lane (t, g)): latent K-step 2m / 2m+1 = dims 64m +
-    // 16g + [0..7] / [8..15], rope K-step r = dims 512 + 32r + 8g + [0..7].
-    // Heads >= H load head 0 (every lane issues the same loads) and are zeroed.
-    const int hq = 16 * i + t;
-    const bool hq_ok = hq < Hl;
-    v4i qr[kQLoads];
-    {
+    const int h = w & 1;   // head half: heads 32h .. 32h+31
+    const int kq = w >> 1; // token half (stream): tokens 16kq .. 16kq+15 of a tile
+    // q of heads 32h + 16u + t (lane (t, g), u = 0, 1): latent K-step 2m /
+    // 2m+1 = dims 64m + 16g + [0..7] / [8..15], rope K-step r = dims 512 +
+    // 32r + 8g + [0..7].  Heads >= H load head 0 (every lane issues the same
+    // loads) and are zeroed.
+    v8bf qlat[2][16], qrope[2][2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int hq = 32 * h + 16 * u + t;
+      const bool hq_ok = hq < Hl;
+      v4i qr[kQLoads];
       const uint64_t qa = (uint64_t)(uintptr_t)(p.q + row * p.q_st + (int64_t)(h0 + (hq_ok ? hq : 0)) * p.q_sh);
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
@@ -151,98 +159,104 @@ __global__ __launch_bounds__(w64::kThreads, 1) void smla_fwdw64_kernel(FwdParams
       }
       gload16(qr[16], qa + 2 * (kLat + 8 * g));
       gload16(qr[17], qa + 2 * (kLat + 32 + 8 * g));
+      wait_vm<0>();
+#pragma unroll
+      for (int k = 0; k < kQLoads; ++k) asm volatile("" : "+v"(qr[k]));
+#pragma unroll
+      for (int k = 0; k < 16; ++k) qlat[u][k] = __builtin_bit_cast(v8bf, hq_ok ? qr[k] : v4i{0, 0, 0, 0});
+#pragma unroll
+      for (int k = 0; k < 2; ++k) qrope[u][k] = __builtin_bit_cast(v8bf, hq_ok ? qr[16 + k] : v4i{0, 0, 0, 0});
     }
-    wait_vm<0>();
-#pragma unroll
-    for (int k = 0; k < kQLoads; ++k) asm volatile("" : "+v"(qr[k]));
-    v8bf qlat[16], qrope[2];
-#pragma unroll
-    for (int k = 0; k < 16; ++k) qlat[k] = __builtin_bit_cast(v8bf, hq_ok ? qr[k] : v4i{0, 0, 0, 0});
-#pragma unroll
-    for (int k = 0; k < 2; ++k) qrope[k] = __builtin_bit_cast(v8bf, hq_ok ? qr[16 + k] : v4i{0, 0, 0, 0});
 
-    float m_ref = -INFINITY;  // head 16i + t: reference max (log2 units)
-    float l_run = 0.0f;       // this lane's part of the head's sum of P
+    float m_ref[2] = {-INFINITY, -INFINITY};  // head 32h + 16u + t, this stream: reference (log2 units, integer)
+    float l_run[2] = {0.0f, 0.0f};            // this lane's part of the stream's sum of P
     const v2h ones = v2h{(_Float16)1.0f, (_Float16)1.0f};
+    const int tok = 16 * kq + t;  // the token whose K row this lane feeds
+    const uint32_t qk_row = row_off(tok) + 16 * g;
+    const uint32_t qk_a = qk_row + ((t & 1) ? 128u : 0u);
+    const uint32_t qk_b = qk_row - ((t & 1) ? 128u : 0u);
     int st = 0;  // stage of tile s
     for (int s = t0; s <= t1; ++s) {
       // tile s's records have landed; the PV waves are done with tile s - 2
-      // (its P, scales and factors: this tile's buffers)
+      // (its P, scales and references: this tile's buffers)
       __syncthreads();
       if (s < t1) {
         const int b = s & 1;
         const uint32_t lat = lat_at(st);
         const uint32_t side = side_at(st);
         const uint32_t kmask = *LDSP(uint32_t, keys + 4 * (s & (kRing - 1)));
-        // scores: lane (t, g) gets head 16i + t, tokens 16gi + 4g + r
-        float x[2][4];
-        float tmax = -INFINITY;
+        // scores: lane (t, g) gets heads 32h + 16u + t, tokens 16kq + 4g + r;
+        // each K element is converted once for both head tiles
+        v4i kr[8];
 #pragma unroll
-        for (int gi = 0; gi < 2; ++gi) {
-          const int tok = 16 * gi + t;  // the token whose K row this lane feeds
-          const uint32_t qk_row = row_off(tok) + 16 * g;
-          const uint32_t qk_a = qk_row + ((t & 1) ? 128u : 0u);
-          const uint32_t qk_b = qk_row - ((t & 1) ? 128u : 0u);
-          v4i kr[8];
+        for (int m = 0; m < 8; ++m) kr[m] = *LDSP(v4i, lat + ((m & 2) ? qk_b : qk_a) + 64 * m);
+        const v4f ksc = *LDSP(v4f, side + kSideTok * tok);
+        const v8bf rp0 = __builtin_bit_cast(v8bf, *LDSP(v4i, side + kSideTok * tok + 16 + 16 * g));
+        const v8bf rp1 = __builtin_bit_cast(v8bf, *LDSP(v4i, side + kSideTok * tok + 16 + 64 + 16 * g));
+        v4f acc[2][2];
 #pragma unroll
-          for (int m = 0; m < 8; ++m) kr[m] = *LDSP(v4i, lat + ((m & 2) ? qk_b : qk_a) + 64 * m);
-          const v4f ksc = *LDSP(v4f, side + kSideTok * tok);
-          const v4i rp0 = *LDSP(v4i, side + kSideTok * tok + 16 + 16 * g);
-          const v4i rp1 = *LDSP(v4i, side + kSideTok * tok + 16 + 64 + 16 * g);
-          v4f acc0 = v4f{0, 0, 0, 0}, acc1 = v4f{0, 0, 0, 0};
-          acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, rp0), qrope[0], acc0, 0, 0, 0);
-          acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, rp1), qrope[1], acc1, 0, 0, 0);
+        for (int u = 0; u < 2; ++u) {
+          acc[u][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rp0, qrope[u][0], v4f{0, 0, 0, 0}, 0, 0, 0);
+          acc[u][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rp1, qrope[u][1], v4f{0, 0, 0, 0}, 0, 0, 0);
+        }
 #pragma unroll
-          for (int m = 0; m < 8; ++m) {
-            const float sc = ksc[m >> 1];
-            v2bf a0, a1, a2, a3, b0, b1, b2, b3;
-            cvt4_bf16(kr[m].x, sc, a0, a1);
-            cvt4_bf16(kr[m].y, sc, a2, a3);
-            cvt4_bf16(kr[m].z, sc, b0, b1);
-            cvt4_bf16(kr[m].w, sc, b2, b3);
-            const v8bf ka = {a0.x, a0.y, a1.x, a1.y, a2.x, a2.y, a3.x, a3.y};
-            const v8bf kb = {b0.x, b0.y, b1.x, b1.y, b2.x, b2.y, b3.x, b3.y};
-            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qlat[2 * m], acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qlat[2 * m + 1], acc1, 0, 0, 0);
+        for (int m = 0; m < 8; ++m) {
+          const float sc = ksc[m >> 1];
+          v2bf a0, a1, a2, a3, b0, b1, b2, b3;
+          cvt4_bf16(kr[m].x, sc, a0, a1);
+          cvt4_bf16(kr[m].y, sc, a2, a3);
+          cvt4_bf16(kr[m].z, sc, b0, b1);
+          cvt4_bf16(kr[m].w, sc, b2, b3);
+          const v8bf ka = {a0.x, a0.y, a1.x, a1.y, a2.x, a2.y, a3.x, a3.y};
+          const v8bf kb = {b0.x, b0.y, b1.x, b1.y, b2.x, b2.y, b3.x, b3.y};
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            acc[u][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qlat[u][2 * m], acc[u][0], 0, 0, 0);
+            acc[u][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qlat[u][2 * m + 1], acc[u][1], 0, 0, 0);
           }
-          const v4f S = acc0 + acc1;
-          const uint32_t kb = kmask >> (16 * gi + 4 * g);  // which of tokens 16gi + 4g + r are keys
+        }
+        // V scale of block g for token tok, clamped to 2^7, as f16 (the waves of head half 0 write them)
+        if (h == 0) *LDSP(_Float16, sx0 + b * kSxBuf + kPitch * g + 2 * tok) = (_Float16)__builtin_fminf(ksc[g], kScaleCap);
+        const uint32_t kb = kmask >> (16 * kq + 4 * g);  // which of tokens 16kq + 4g + r are keys
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const v4f S = acc[u][0] + acc[u][1];
+          float x[4];
+          float tmax = -INFINITY;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            x[gi][r] = ((kb >> r) & 1u) ? S[r] * p.c_log2 : -INFINITY;
-            tmax = fmax_(tmax, x[gi][r]);
+            x[r] = ((kb >> r) & 1u) ? S[r] * p.c_log2 : -INFINITY;
+            tmax = fmax_(tmax, x[r]);
           }
-          // V scale of block g for token tok, clamped to 2^7, as f16 (one wave writes them)
-          if (i == 0)
-            *LDSP(_Float16, sx0 + b * kSxBuf + kPitch * g + 2 * tok) = (_Float16)__builtin_fminf(ksc[g], kScaleCap);
-        }
-        // the head's tile max; its reference moves only when the max exceeds
-        // it by more than kTau, and the factor tells the PV waves to rescale O
-        tmax = xor_max(tmax);
-        float alpha = 1.0f;
-        if (tmax > m_ref + kTau) {
-          alpha = m_ref == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_ref - tmax);
-          l_run *= alpha;
-          m_ref = tmax;
-        }
-        if (g == 0) *LDSP(float, ax0 + b * kAxBuf + 16 * t + 4 * i) = alpha;
-        const float mu = m_ref == -INFINITY ? 0.0f : m_ref;
-#pragma unroll
-        for (int gi = 0; gi < 2; ++gi) {
+          // the head's max over this tile's half; the stream's reference
+          // moves (to the max rounded up) only when the max exceeds it by
+          // more than kTau
+          tmax = xor_max(tmax);
+          if (tmax > m_ref[u] + kTau) {
+            const float m_new = __builtin_ceilf(tmax);
+            if (m_ref[u] != -INFINITY) l_run[u] *= __builtin_amdgcn_ldexpf(1.0f, (int)__builtin_fmaxf(m_ref[u] - m_new, -200.0f));
+            m_ref[u] = m_new;
+          }
+          const int hh = 32 * h + 16 * u + t;  // head of the group
+          if (g == 0) *LDSP(float, mx0 + b * kMxBuf + kq * (kHeads * 4) + 16 * t + 4 * (2 * h + u)) = m_ref[u];
+          const float mu = m_ref[u] == -INFINITY ? 0.0f : m_ref[u];
           _Float16 ph[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) ph[r] = (_Float16)__builtin_amdgcn_exp2f(x[gi][r] - mu + kShift);
-          l_run = __builtin_amdgcn_fdot2(v2h{ph[0], ph[1]}, ones, l_run, false);
-          l_run = __builtin_amdgcn_fdot2(v2h{ph[2], ph[3]}, ones, l_run, false);
-          *LDSP(v2i, px0 + b * kPxBuf + kPitch * (16 * i + t) + 2 * (16 * gi + 4 * g)) =
+          for (int r = 0; r < 4; ++r) ph[r] = (_Float16)__builtin_amdgcn_exp2f(x[r] - mu + kShift);
+          l_run[u] = __builtin_amdgcn_fdot2(v2h{ph[0], ph[1]}, ones, l_run[u], false);
+          l_run[u] = __builtin_amdgcn_fdot2(v2h{ph[2], ph[3]}, ones, l_run[u], false);
+          *LDSP(v2i, px0 + b * kPxBuf + kPitch * hh + 2 * (16 * kq + 4 * g)) =
               __builtin_bit_cast(v2i, (v4h{ph[0], ph[1], ph[2], ph[3]}));
         }
         st = st == kStages - 1 ? 0 : st + 1;
       }
     }
-    // the head's sum and reference for the PV waves' normalisation
-    const float l = xor_sum(l_run);
-    if (g == 0) *LDSP(v2f, lm + 8 * (16 * i + t)) = v2f{l, m_ref};
+    // each head's stream sum and reference for the PV waves' normalisation
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const float l = xor_sum(l_run[u]);
+      if (g == 0) *LDSP(v2f, lm + 16 * (32 * h + 16 * u + t) + 8 * kq) = v2f{l, m_ref[u]};
+    }
     __syncthreads();
     return;
   }
@@ -316,10 +330,15 @@ __global__ __launch_bounds__(w64::kThreads, 1) void smla_fwdw64_kernel(FwdParams
   }
 
   v4f O[4][8];  // O^T slices: dims 128j + 16dt + 4g + [0..3], head 16ht + t
+  float ref[2][4], M[4];  // heads 16ht + t: the streams' last references, O's reference (their max)
+  _Float16 fac[4];        // 2^(reference of this lane's stream - M), exact
 #pragma unroll
-  for (int ht = 0; ht < 4; ++ht)
+  for (int ht = 0; ht < 4; ++ht) {
+    ref[0][ht] = ref[1][ht] = M[ht] = -INFINITY;
+    fac[ht] = (_Float16)0.0f;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) O[ht][dt] = v4f{0, 0, 0, 0};
+  }
 
   // transposed V reads: lane (t, g) loads token tv = 8g + t/2, bytes
   // 8(t&1) .. +7 of chunk 8j + dt (stored at (8j + dt) ^ 8 in odd rows)
@@ -338,7 +357,7 @@ __global__ __launch_bounds__(w64::kThreads, 1) void smla_fwdw64_kernel(FwdParams
     }
     __syncthreads();
     const int st_l = st_q + kAhead >= kStages ? st_q + kAhead - kStages : st_q + kAhead;  // tile s+3
-    __builtin_amdgcn_s_setprio(2);
+    __builtin_amdgcn_s_setprio(2);  // the gather ahead of the other role's work on this SIMD
     if (s + kAhead < t1) {
       fill_table(s + kAhead);
       issue_tile(st_l);
@@ -355,12 +374,28 @@ __global__ __launch_bounds__(w64::kThreads, 1) void smla_fwdw64_kernel(FwdParams
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) vr[dt] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(LDSP(v2i, vaddr + 16 * dt));
       const v8h sr = *LDSP(v8h, sx0 + b * kSxBuf + kPitch * j + 16 * g);
-      const v4f al = *LDSP(v4f, ax0 + b * kAxBuf + 16 * t);
-      if (__builtin_amdgcn_ballot_w64(al.x != 1.0f || al.y != 1.0f || al.z != 1.0f || al.w != 1.0f)) {
+      // the streams' references of heads 16ht + t after tile n; when one
+      // moved, O's reference (their max) and the streams' factors follow
+      const v4f r0 = *LDSP(v4f, mx0 + b * kMxBuf + 16 * t);
+      const v4f r1 = *LDSP(v4f, mx0 + b * kMxBuf + kHeads * 4 + 16 * t);
+      if (__builtin_amdgcn_ballot_w64(r0.x != ref[0][0] || r0.y != ref[0][1] || r0.z != ref[0][2] || r0.w != ref[0][3] ||
+                                      r1.x != ref[1][0] || r1.y != ref[1][1] || r1.z != ref[1][2] || r1.w != ref[1][3])) {
 #pragma unroll
-        for (int ht = 0; ht < 4; ++ht)
+        for (int ht = 0; ht < 4; ++ht) {
+          ref[0][ht] = r0[ht];
+          ref[1][ht] = r1[ht];
+          const float mn = fmax_(M[ht], fmax_(r0[ht], r1[ht]));
+          if (M[ht] != -INFINITY && mn != M[ht]) {
+            const float al = __builtin_amdgcn_ldexpf(1.0f, (int)(M[ht] - mn));
 #pragma unroll
-          for (int dt = 0; dt < 8; ++dt) O[ht][dt] *= al[ht];
+            for (int dt = 0; dt < 8; ++dt) O[ht][dt] *= al;
+          }
+          M[ht] = mn;
+          // this lane's tokens 8g .. 8g+7 are stream g >> 1's
+          const float rs = g < 2 ? r0[ht] : r1[ht];
+          const float f = rs == -INFINITY ? 0.0f : __builtin_amdgcn_ldexpf(1.0f, (int)__builtin_fmaxf(rs - mn, -40.0f));
+          fac[ht] = (_Float16)f;
+        }
       }
       v8h vh[8];
 #pragma unroll
@@ -368,7 +403,7 @@ __global__ __launch_bounds__(w64::kThreads, 1) void smla_fwdw64_kernel(FwdParams
 #pragma unroll
       for (int ht = 0; ht < 4; ++ht) {
         const v8h pr = *LDSP(v8h, px0 + b * kPxBuf + kPitch * (16 * ht + t) + 16 * g);
-        const v8h pb = pr * sr;
+        const v8h pb = pr * (sr * fac[ht]);
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) O[ht][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vh[dt], pb, O[ht][dt], 0, 0, 0);
       }
@@ -384,8 +419,13 @@ __global__ __launch_bounds__(w64::kThreads, 1) void smla_fwdw64_kernel(FwdParams
     const int hl = 16 * ht + t;  // head of the group
     const int h = h0 + hl;       // head of the row
     const bool h_ok = hl < Hl;
-    const v2f lmv = *LDSP(v2f, lm + 8 * hl);
-    const Norm nm = finish_norm(lmv.x, lmv.y, (split || !h_ok) ? -INFINITY : sink_log2(p.sink, h));
+    // the two streams' sums, each relative to its own reference, at O's
+    // reference (their max; every factor is an exact power of two)
+    const v4f lmv = *LDSP(v4f, lm + 16 * hl);
+    const float mo = fmax_(lmv.y, lmv.w);
+    const float l = (lmv.y == -INFINITY ? 0.0f : lmv.x * __builtin_amdgcn_ldexpf(1.0f, (int)__builtin_fmaxf(lmv.y - mo, -200.0f))) +
+                    (lmv.w == -INFINITY ? 0.0f : lmv.z * __builtin_amdgcn_ldexpf(1.0f, (int)__builtin_fmaxf(lmv.w - mo, -200.0f)));
+    const Norm nm = finish_norm(l, mo, (split || !h_ok) ? -INFINITY : sink_log2(p.sink, h));
     if (j == 0 && g == 0 && h_ok) {
       if (split) p.part_lse[(int64_t)unit * H + h] = nm.lse2;
       else if (p.lse) p.lse[(int64_t)row * H + h] = nm.lse2 * kLn2;
