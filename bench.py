@@ -273,6 +273,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--config", type=int, default=2, help="workload number 1..5")
+    ap.add_argument("--heads", type=int, default=None,
+                    help="run the workload with this many heads instead of its own (e.g. 64 on the decode workload)")
     ap.add_argument("--cold-steps", type=int, default=50)
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -304,8 +306,10 @@ def main() -> int:
     if args.op == "fwd_v41":
         return bench_v41(args, torch, smla, dev)
     cfg = synth.make_config(args.config)
+    if args.heads is not None:
+        cfg["name"] = synth.heads_name(cfg["name"], args.heads)
     print(f"[bench] generating {cfg['name']}", file=sys.stderr, flush=True)
-    w = synth.make_workload(args.config, device="cuda")
+    w = synth.make_workload(args.config, device="cuda", H=args.heads)
     valid = w.valid_entries()
     gathered = RECORD_BYTES * valid
     flop = 2.0 * w.H * (576 + 512) * valid
@@ -621,7 +625,7 @@ def _fwd_kernel_name(H: int) -> str:
     """The forward kernel the library launches for H heads."""
     if H <= 16:
         return "smla_fwd16_kernel"
-    return "smla_fwdw_kernel<2>" if H <= 32 else "smla_fwdw_kernel<4>"
+    return "smla_fwdw_kernel<2>" if H <= 32 else "smla_fwdw64_kernel"
 
 
 def _split_of(smla, w) -> int:

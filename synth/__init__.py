@@ -14,6 +14,7 @@ from .workloads import (  # noqa: F401
     encode_records,
     make_config,
     make_workload,
+    heads_name,
     distinct_uniform,
     build_workload,
 )

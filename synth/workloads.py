@@ -22,6 +22,7 @@ Random streams (fixed order, so a seed fixes every byte):
 from __future__ import annotations
 
 import math
+import re
 from dataclasses import dataclass, field
 from typing import Callable, List, Optional
 
@@ -199,17 +200,25 @@ def make_config(cfg: int) -> dict:
     return dict(CONFIGS[cfg])
 
 
+def heads_name(name: str, H: int) -> str:
+    """A workload's name with its head count replaced by H."""
+    return re.sub(r"_H\d+_", f"_H{H}_", name, count=1)
+
+
 def make_workload(cfg: int, device="cpu", seed: Optional[int] = None,
-                  T: Optional[int] = None) -> Workload:
+                  T: Optional[int] = None, H: Optional[int] = None) -> Workload:
     """Build configuration ``cfg`` (1..5).  ``seed`` defaults to the config
     number.  ``T`` may shrink the number of query rows (rows keep the same
     recipe; for the causal config the row positions keep their full-size
-    meaning, i.e. row r is still row r of a 4096-row batch)."""
+    meaning, i.e. row r is still row r of a 4096-row batch).  ``H`` replaces
+    the configuration's head count (same records and slices; q has H heads)."""
     c = make_config(cfg)
     seed = cfg if seed is None else seed
-    Tf, H, N, k = c["T"], c["H"], c["N"], c["topk"]
+    Tf, Hc, N, k = c["T"], c["H"], c["N"], c["topk"]
+    H = Hc if H is None else H
     T = Tf if T is None else T
-    name = c["name"] if T == Tf else f"{c['name']}[T={T}]"
+    base = c["name"] if H == Hc else heads_name(c["name"], H)
+    name = base if T == Tf else f"{base}[T={T}]"
     if cfg == 1:
         return build_workload(name, T, H, N, lambda g, r, m: distinct_uniform(g, N, k), seed=seed,
                               device=device)
