@@ -161,6 +161,38 @@ def test_head_counts(smla, H):
     compare(out, lse, ro, rl, label=f"H{H}")
 
 
+@pytest.mark.parametrize("has_invalid,split,outliers", [(0, 1, 0), (1, 1, 0), (0, 3, 0), (1, 2, 1), (0, 1, 1)])
+def test_wide_stream_edges(smla, has_invalid, split, outliers):
+    """Above 32 heads each score wave takes one half of a 32-token tile, and
+    the two halves (tokens 0-15 and 16-31) are two softmax streams with their
+    own references, merged by powers of two.  Rows here end inside, on and
+    just past a half or a tile, have one half of every tile masked, or carry
+    outlier latents (large logits: the references move, O and the sums are
+    rescaled)."""
+    rng = np.random.default_rng(31 + 4 * has_invalid + split + 8 * outliers)
+    N = 4000
+    sl = [rng.integers(0, N, L) for L in (1, 5, 15, 16, 17, 31, 32, 33, 48, 63, 64, 65, 100, 700)]
+    pos = np.arange(160) % 32
+    x = rng.integers(0, N, 160)
+    x[pos >= 16] = -1  # the second half of every tile masked
+    y = rng.integers(0, N, 160)
+    y[pos < 16] = -1   # the first half masked
+    z = rng.integers(0, N, 160)
+    z[pos != 20] = -1  # one key per tile, in the second half
+    sl += [x, y, z]
+    kw = dict(latent_std=2.0, outlier_p=0.01, outlier_mag=1000.0) if outliers else {}
+    w = custom(f"streams_inv{has_invalid}_s{split}_o{outliers}", 64, N, sl, seed=50 + split, has_invalid=has_invalid, **kw)
+    smla.set_option("split", split)
+    note(f"wide stream edges has_invalid={has_invalid} split={split} outliers={outliers} T={w.T}")
+    out, lse = run_gpu(w)
+    if outliers:  # outputs near 10^3: the per-element bound of the ragged workload (reading c14)
+        ro, rl, ra = run_oracle(w, with_abs=True)
+        compare(out, lse, ro, rl, large_values=True, abs_ref=ra, label=f"streams inv{has_invalid} s{split} o1")
+    else:
+        ro, rl = run_oracle(w)
+        compare(out, lse, ro, rl, label=f"streams inv{has_invalid} s{split} o0")
+
+
 @pytest.mark.parametrize("split", [1, 2, 3, 7, 32])
 def test_forced_split(smla, split):
     rng = np.random.default_rng(7)
