@@ -193,11 +193,12 @@ __global__ __launch_bounds__(w64::kThreads, 1) void smla_fwdw64_kernel(FwdParams
         const v4f ksc = *LDSP(v4f, side + kSideTok * tok);
         const v8bf rp0 = __builtin_bit_cast(v8bf, *LDSP(v4i, side + kSideTok * tok + 16 + 16 * g));
         const v8bf rp1 = __builtin_bit_cast(v8bf, *LDSP(v4i, side + kSideTok * tok + 16 + 64 + 16 * g));
-        v4f acc[2][2];
+        // one accumulator chain per head tile (the two tiles' chains interleave)
+        v4f acc[2];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          acc[u][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rp0, qrope[u][0], v4f{0, 0, 0, 0}, 0, 0, 0);
-          acc[u][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rp1, qrope[u][1], v4f{0, 0, 0, 0}, 0, 0, 0);
+          acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rp0, qrope[u][0], v4f{0, 0, 0, 0}, 0, 0, 0);
+          acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rp1, qrope[u][1], acc[u], 0, 0, 0);
         }
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
@@ -210,17 +211,16 @@ __global__ __launch_bounds__(w64::kThreads, 1) void smla_fwdw64_kernel(FwdParams
           const v8bf ka = {a0.x, a0.y, a1.x, a1.y, a2.x, a2.y, a3.x, a3.y};
           const v8bf kb = {b0.x, b0.y, b1.x, b1.y, b2.x, b2.y, b3.x, b3.y};
 #pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            acc[u][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qlat[u][2 * m], acc[u][0], 0, 0, 0);
-            acc[u][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qlat[u][2 * m + 1], acc[u][1], 0, 0, 0);
-          }
+          for (int u = 0; u < 2; ++u) acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qlat[u][2 * m], acc[u], 0, 0, 0);
+#pragma unroll
+          for (int u = 0; u < 2; ++u) acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qlat[u][2 * m + 1], acc[u], 0, 0, 0);
         }
         // V scale of block g for token tok, clamped to 2^7, as f16 (the waves of head half 0 write them)
         if (h == 0) *LDSP(_Float16, sx0 + b * kSxBuf + kPitch * g + 2 * tok) = (_Float16)__builtin_fminf(ksc[g], kScaleCap);
         const uint32_t kb = kmask >> (16 * kq + 4 * g);  // which of tokens 16kq + 4g + r are keys
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          const v4f S = acc[u][0] + acc[u][1];
+          const v4f S = acc[u];
           float x[4];
           float tmax = -INFINITY;
 #pragma unroll
@@ -239,10 +239,10 @@ __global__ __launch_bounds__(w64::kThreads, 1) void smla_fwdw64_kernel(FwdParams
           }
           const int hh = 32 * h + 16 * u + t;  // head of the group
           if (g == 0) *LDSP(float, mx0 + b * kMxBuf + kq * (kHeads * 4) + 16 * t + 4 * (2 * h + u)) = m_ref[u];
-          const float mu = m_ref[u] == -INFINITY ? 0.0f : m_ref[u];
+          const float eo = kShift - (m_ref[u] == -INFINITY ? 0.0f : m_ref[u]);  // P = 2^(x - m + kShift)
           _Float16 ph[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) ph[r] = (_Float16)__builtin_amdgcn_exp2f(x[r] - mu + kShift);
+          for (int r = 0; r < 4; ++r) ph[r] = (_Float16)__builtin_amdgcn_exp2f(x[r] + eo);
           l_run[u] = __builtin_amdgcn_fdot2(v2h{ph[0], ph[1]}, ones, l_run[u], false);
           l_run[u] = __builtin_amdgcn_fdot2(v2h{ph[2], ph[3]}, ones, l_run[u], false);
           *LDSP(v2i, px0 + b * kPxBuf + kPitch * hh + 2 * (16 * kq + 4 * g)) =
@@ -349,7 +349,9 @@ __global__ __launch_bounds__(w64::kThreads, 1) void smla_fwdw64_kernel(FwdParams
   for (int s = t0; s <= t1; ++s) {
     // this wave's records of tile s and index tile s+3 have landed: after
     // I(s+3) it queued L(x) I(x+3) for x = s+1, s+2 (those that exist)
-    {
+    if (s + 2 * kAhead - 1 < t1) {
+      wait_vm<(kAhead - 1) * (kTileVm + 1)>();  // every later tile exists
+    } else {
       int after = 0;
 #pragma unroll
       for (int x = 1; x < kAhead; ++x) after += (s + x < t1 ? kTileVm : 0) + (s + x + kAhead < t1);
