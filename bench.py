@@ -625,7 +625,7 @@ def _fwd_kernel_name(H: int) -> str:
     """The forward kernel the library launches for H heads."""
     if H <= 16:
         return "smla_fwd16_kernel"
-    return "smla_fwdw_kernel<2>" if H <= 32 else "smla_fwdw64_kernel"
+    return "smla_fwdw_kernel<2>" if H <= 32 else "smla_fwdw64_kernel<false>"
 
 
 def _split_of(smla, w) -> int:

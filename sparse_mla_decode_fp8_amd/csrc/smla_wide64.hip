@@ -85,6 +85,9 @@ __device__ __forceinline__ uint32_t row_off(int tau) { return (tau >> 1) * kPair
 
 }  // namespace w64
 
+// PAGED: the keys live in paged pools (KeyMode, key_addr); otherwise in one
+// contiguous cache (entries >= 0 are keys), compiled without the pool logic.
+template <bool PAGED>
 __global__ __launch_bounds__(w64::kThreads, 1) void smla_fwdw64_kernel(FwdParams p) {
   using namespace w64;
   __shared__ __attribute__((aligned(1024))) uint8_t s_lds[kBytes];
@@ -280,8 +283,9 @@ __global__ __launch_bounds__(w64::kThreads, 1) void smla_fwdw64_kernel(FwdParams
     bool ok = false;
     if (lane < 8) {
       const int raw = *LDSP(int, ring_at(n) + 4 * (8 * j + lane));
-      ok = (n * kTile + 8 * j + lane < len) && p.km.valid(raw);
-      *LDSP(uint64_t, tab + 8 * lane) = (uint64_t)(uintptr_t)(ok ? key_addr(p, raw) : zero);
+      ok = (n * kTile + 8 * j + lane < len) && (PAGED ? p.km.valid(raw) : raw >= 0);
+      const uint8_t* const rec = PAGED ? key_addr(p, raw) : p.kv + (int64_t)raw * kRecordBytes;
+      *LDSP(uint64_t, tab + 8 * lane) = (uint64_t)(uintptr_t)(ok ? rec : zero);
     }
     const uint32_t bits = (uint32_t)__ballot(ok) & 0xFFu;
     if (lane == 0) *LDSP(uint8_t, keys + 4 * (n & (kRing - 1)) + j) = (uint8_t)bits;
@@ -453,8 +457,12 @@ __global__ __launch_bounds__(w64::kThreads, 1) void smla_fwdw64_kernel(FwdParams
 
 hipError_t launch_fwd_wide64(const FwdParams& p, Events ev, hipStream_t s) {
   const int64_t blocks = p.hg == 1 ? fwd_grid(p.T, p.S, p.order == nullptr) : xcd_grid(p.T, p.S * p.hg);
-  hipExtLaunchKernelGGL(smla_fwdw64_kernel, dim3((unsigned)blocks), dim3(w64::kThreads), 0, s, ev.start,
-                        ev.stop, 0, p);
+  if (p.km.paged)
+    hipExtLaunchKernelGGL(smla_fwdw64_kernel<true>, dim3((unsigned)blocks), dim3(w64::kThreads), 0, s, ev.start,
+                          ev.stop, 0, p);
+  else
+    hipExtLaunchKernelGGL(smla_fwdw64_kernel<false>, dim3((unsigned)blocks), dim3(w64::kThreads), 0, s, ev.start,
+                          ev.stop, 0, p);
   return hipGetLastError();
 }
 
