@@ -8,25 +8,30 @@
 // run on the same SIMD, so every SIMD holds one wave of each role, and the
 // conversion-heavy score work of one overlaps the MFMA-heavy P.V work of the
 // other instead of both waves of a SIMD doing the same phase at once.
-//   QK waves 0..3: wave (h, k) = (w & 1, w >> 1) scores heads 32h .. 32h+31
-//       (q in registers) against tokens 16k .. 16k+15 of each 32-token tile,
-//       so each K element is converted for 32 heads at once.  The two token
-//       halves are two softmax streams: each wave keeps its own running
-//       reference and sum per head, writes P relative to its reference and
-//       publishes the reference.  References are integers (log2 units), so
-//       every factor between them is an exact power of two.
+//   QK waves 0..3: wave (h, k) = (w & 1, w >> 1) computes the dim-half-h
+//       part of the scores (latent dims 256h .. 256h+255 and rope dims
+//       32h .. 32h+31) of all 64 heads against tokens 16k .. 16k+15 of each
+//       32-token tile, so each K element is converted once per tile.  The
+//       wave sends the other half's head tiles to it through LDS and, one
+//       step later, adds the half it receives and runs the softmax of heads
+//       32h .. 32h+31.  The two token halves are two softmax streams: each
+//       wave keeps its own running reference and sum per head, writes P
+//       relative to its reference and publishes the reference.  References
+//       are integers (log2 units), so every factor between them is an exact
+//       power of two.
 //   PV waves 4..7: wave 4 + j owns dims 128j .. 128j+127, one scale block,
 //       for all 64 heads, so the block's per-token V scale folds into P; it
 //       keeps O relative to the larger of the two streams' references,
-//       scales each stream's P to it, and accumulates O over the tile scored
-//       one step before.  These waves also run the gather: index tiles into
-//       an LDS ring and the records (latent rows, scales and rope) of 8
-//       tokens per tile.
-// One barrier per step: at step s the QK waves work on tile s while the PV
-// waves work on tile s - 1 and queue the records of tile s + 3 (three tiles
-// of records in flight, five LDS stages).  P, the V scales and the
-// references are double-buffered by tile parity.  The two streams are merged
-// like two chunks of a split row (K2-back page, stage_combine).
+//       scales each stream's P to it, and accumulates O over the tile whose
+//       softmax ran one step before.  These waves also run the gather: index
+//       tiles into an LDS ring and the records (latent rows, scales and
+//       rope) of 8 tokens per tile.
+// One barrier per step: at step s the QK waves score tile s and run the
+// softmax of tile s - 1 while the PV waves work on tile s - 2 and queue the
+// records of tile s + 3 (three tiles of records in flight, six LDS stages).
+// Halves of scores, P, the V scales and the references are double-buffered
+// by tile parity.  The two streams are merged like two chunks of a split row
+// (K2-back page, stage_combine).
 
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
@@ -42,7 +47,7 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kHeads = 64;
 constexpr int kTile = 32;                       // tokens per step
 constexpr int kAhead = 3;                       // tiles of records queued ahead of the QK tile
-constexpr int kStages = kAhead + 2;             // LDS record stages
+constexpr int kStages = kAhead + 3;             // LDS record stages
 constexpr int kRing = 16;                       // index ring slots (tiles), >= 2 kAhead + 1
 constexpr int kPair = 2 * kLat + 16;            // two latent rows + 16-B pad
 constexpr int kLatStage = (kTile / 2) * kPair;  // 16,640 B
@@ -61,13 +66,15 @@ constexpr int kSxOff = kPxOff + 2 * kPxBuf;               // V scales f16 [buf 2
 constexpr int kSxBuf = 4 * kPitch;
 constexpr int kMxOff = kSxOff + 2 * kSxBuf;               // stream references f32 [buf 2][stream 2][head t 16][tile 4]
 constexpr int kMxBuf = 2 * kHeads * 4;
-constexpr int kRingOff = kMxOff + 2 * kMxBuf;             // index entries [slot][32]
+constexpr int kSpOff = kMxOff + 2 * kMxBuf;               // halves of scores v4f [buf 2][stream 2][head tile 4][lane 64]
+constexpr int kSpBuf = 2 * 4 * 64 * 16;
+constexpr int kRingOff = kSpOff + 2 * kSpBuf;             // index entries [slot][32]
 constexpr int kTabOff = kRingOff + kRing * kTile * 4;     // record addresses [PV wave][8]
 constexpr int kKeyOff = kTabOff + 4 * 64;                 // key masks u32 [slot]: bit i = token i is a key
 constexpr int kRedOff = kKeyOff + kRing * 4;              // unit_tiles' reduction; later {l, m} per head and stream
 constexpr int kBytes = kRedOff + kHeads * 16;
 static_assert(kBytes <= 160 * 1024, "LDS budget");
-static_assert(kStages >= kAhead + 2 && kRing >= 2 * kAhead + 1, "pipeline depth");
+static_assert(kStages >= kAhead + 3 && kRing >= 2 * kAhead + 1, "pipeline depth");
 
 // vmcnt <= n for a wave-uniform n in [0, 24]
 __device__ __forceinline__ void wait_vm_n(int n) {
@@ -142,118 +149,156 @@ __global__ __launch_bounds__(w64::kThreads, 1) void smla_fwdw64_kernel(FwdParams
 
   if (w < 4) {
     // ================================================================ QK waves
-    const int h = w & 1;   // head half: heads 32h .. 32h+31
-    const int kq = w >> 1; // token half (stream): tokens 16kq .. 16kq+15 of a tile
-    // q of heads 32h + 16u + t (lane (t, g), u = 0, 1): latent K-step 2m /
-    // 2m+1 = dims 64m + 16g + [0..7] / [8..15], rope K-step r = dims 512 +
-    // 32r + 8g + [0..7].  Heads >= H load head 0 (every lane issues the same
-    // loads) and are zeroed.
-    v8bf qlat[2][16], qrope[2][2];
+    const int h = w & 1;    // dim half of the scores; softmax of heads 32h .. 32h+31
+    const int kq = w >> 1;  // token half (stream): tokens 16kq .. 16kq+15 of a tile
+    // q of head tile (2h + v) & 3 (heads 16((2h + v) & 3) + t, lane (t, g)),
+    // so tiles v = 0, 1 are this wave's softmax heads and v = 2, 3 the other
+    // wave's: latent K-step 2m / 2m+1 (m = 0..3) = dims 256h + 64m + 16g +
+    // [0..7] / [8..15], rope K-step = dims 512 + 32h + 8g + [0..7].  Heads >= H
+    // load head 0 (every lane issues the same loads) and are zeroed.
+    v8bf qlat[4][8], qrope[4];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int hq = 32 * h + 16 * u + t;
+    for (int v = 0; v < 4; ++v) {
+      const int hq = 16 * ((2 * h + v) & 3) + t;
       const bool hq_ok = hq < Hl;
-      v4i qr[kQLoads];
+      v4i qr[9];
       const uint64_t qa = (uint64_t)(uintptr_t)(p.q + row * p.q_st + (int64_t)(h0 + (hq_ok ? hq : 0)) * p.q_sh);
 #pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        gload16(qr[2 * m], qa + 2 * (64 * m + 16 * g));
-        gload16(qr[2 * m + 1], qa + 2 * (64 * m + 16 * g + 8));
+      for (int m = 0; m < 4; ++m) {
+        gload16(qr[2 * m], qa + 2 * (256 * h + 64 * m + 16 * g));
+        gload16(qr[2 * m + 1], qa + 2 * (256 * h + 64 * m + 16 * g + 8));
       }
-      gload16(qr[16], qa + 2 * (kLat + 8 * g));
-      gload16(qr[17], qa + 2 * (kLat + 32 + 8 * g));
+      gload16(qr[8], qa + 2 * (kLat + 32 * h + 8 * g));
       wait_vm<0>();
 #pragma unroll
-      for (int k = 0; k < kQLoads; ++k) asm volatile("" : "+v"(qr[k]));
+      for (int k = 0; k < 9; ++k) asm volatile("" : "+v"(qr[k]));
 #pragma unroll
-      for (int k = 0; k < 16; ++k) qlat[u][k] = __builtin_bit_cast(v8bf, hq_ok ? qr[k] : v4i{0, 0, 0, 0});
-#pragma unroll
-      for (int k = 0; k < 2; ++k) qrope[u][k] = __builtin_bit_cast(v8bf, hq_ok ? qr[16 + k] : v4i{0, 0, 0, 0});
+      for (int k = 0; k < 8; ++k) qlat[v][k] = __builtin_bit_cast(v8bf, hq_ok ? qr[k] : v4i{0, 0, 0, 0});
+      qrope[v] = __builtin_bit_cast(v8bf, hq_ok ? qr[8] : v4i{0, 0, 0, 0});
     }
 
     float m_ref[2] = {-INFINITY, -INFINITY};  // head 32h + 16u + t, this stream: reference (log2 units, integer)
     float l_run[2] = {0.0f, 0.0f};            // this lane's part of the stream's sum of P
+    v4f own[2];                               // this dim half's scores of the previous tile, heads 32h + 16u + t
     const v2h ones = v2h{(_Float16)1.0f, (_Float16)1.0f};
     const int tok = 16 * kq + t;  // the token whose K row this lane feeds
-    const uint32_t qk_row = row_off(tok) + 16 * g;
+    const uint32_t qk_row = row_off(tok) + 16 * g + 256 * h;
     const uint32_t qk_a = qk_row + ((t & 1) ? 128u : 0u);
     const uint32_t qk_b = qk_row - ((t & 1) ? 128u : 0u);
-    int st = 0;  // stage of tile s
-    for (int s = t0; s <= t1; ++s) {
-      // tile s's records have landed; the PV waves are done with tile s - 2
-      // (its P, scales and references: this tile's buffers)
-      __syncthreads();
-      if (s < t1) {
-        const int b = s & 1;
-        const uint32_t lat = lat_at(st);
-        const uint32_t side = side_at(st);
-        const uint32_t kmask = *LDSP(uint32_t, keys + 4 * (s & (kRing - 1)));
-        // scores: lane (t, g) gets heads 32h + 16u + t, tokens 16kq + 4g + r;
-        // each K element is converted once for both head tiles
-        v4i kr[8];
+    // halves of scores: [buffer 2][stream 2][head tile 4][lane] v4f; each
+    // wave writes the head tiles of the other dim half's wave and reads its own
+    const uint32_t sp_w = base + kSpOff + 16 * (64 * (4 * kq + 2 - 2 * h) + lane);
+    const uint32_t sp_r = base + kSpOff + 16 * (64 * (4 * kq + 2 * h) + lane);
+
+    // this dim half's scores of the tile in stage st: lane (t, g) gets heads
+    // 16((2h + v) & 3) + t, tokens 16kq + 4g + r; each K element is converted
+    // once for all 64 heads (one accumulator chain per head tile)
+    auto half_scores = [&](int st, v4f (&acc)[4]) {
+      const uint32_t lat = lat_at(st);
+      const uint32_t side = side_at(st) + kSideTok * tok;
+      const v8bf rp = __builtin_bit_cast(v8bf, *LDSP(v4i, side + 16 + 64 * h + 16 * g));
+      const v2f ksc = *LDSP(v2f, side + 8 * h);  // scales of blocks 2h, 2h+1
+      v4i kr[4];
 #pragma unroll
-        for (int m = 0; m < 8; ++m) kr[m] = *LDSP(v4i, lat + ((m & 2) ? qk_b : qk_a) + 64 * m);
-        const v4f ksc = *LDSP(v4f, side + kSideTok * tok);
-        const v8bf rp0 = __builtin_bit_cast(v8bf, *LDSP(v4i, side + kSideTok * tok + 16 + 16 * g));
-        const v8bf rp1 = __builtin_bit_cast(v8bf, *LDSP(v4i, side + kSideTok * tok + 16 + 64 + 16 * g));
-        // one accumulator chain per head tile (the two tiles' chains interleave)
-        v4f acc[2];
+      for (int m = 0; m < 4; ++m) kr[m] = *LDSP(v4i, lat + ((m & 2) ? qk_b : qk_a) + 64 * m);
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rp0, qrope[u][0], v4f{0, 0, 0, 0}, 0, 0, 0);
-          acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rp1, qrope[u][1], acc[u], 0, 0, 0);
-        }
+      for (int v = 0; v < 4; ++v) acc[v] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rp, qrope[v], v4f{0, 0, 0, 0}, 0, 0, 0);
 #pragma unroll
-        for (int m = 0; m < 8; ++m) {
-          const float sc = ksc[m >> 1];
-          v2bf a0, a1, a2, a3, b0, b1, b2, b3;
-          cvt4_bf16(kr[m].x, sc, a0, a1);
-          cvt4_bf16(kr[m].y, sc, a2, a3);
-          cvt4_bf16(kr[m].z, sc, b0, b1);
-          cvt4_bf16(kr[m].w, sc, b2, b3);
-          const v8bf ka = {a0.x, a0.y, a1.x, a1.y, a2.x, a2.y, a3.x, a3.y};
-          const v8bf kb = {b0.x, b0.y, b1.x, b1.y, b2.x, b2.y, b3.x, b3.y};
+      for (int m = 0; m < 4; ++m) {
+        const float sc = ksc[m >> 1];
+        v2bf a0, a1, a2, a3, b0, b1, b2, b3;
+        cvt4_bf16(kr[m].x, sc, a0, a1);
+        cvt4_bf16(kr[m].y, sc, a2, a3);
+        cvt4_bf16(kr[m].z, sc, b0, b1);
+        cvt4_bf16(kr[m].w, sc, b2, b3);
+        const v8bf ka = {a0.x, a0.y, a1.x, a1.y, a2.x, a2.y, a3.x, a3.y};
+        const v8bf kb = {b0.x, b0.y, b1.x, b1.y, b2.x, b2.y, b3.x, b3.y};
 #pragma unroll
-          for (int u = 0; u < 2; ++u) acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qlat[u][2 * m], acc[u], 0, 0, 0);
+        for (int v = 0; v < 4; ++v) acc[v] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qlat[v][2 * m], acc[v], 0, 0, 0);
 #pragma unroll
-          for (int u = 0; u < 2; ++u) acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qlat[u][2 * m + 1], acc[u], 0, 0, 0);
-        }
-        // V scale of block g for token tok, clamped to 2^7, as f16 (the waves of head half 0 write them)
-        if (h == 0) *LDSP(_Float16, sx0 + b * kSxBuf + kPitch * g + 2 * tok) = (_Float16)__builtin_fminf(ksc[g], kScaleCap);
-        const uint32_t kb = kmask >> (16 * kq + 4 * g);  // which of tokens 16kq + 4g + r are keys
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const v4f S = acc[u];
-          float x[4];
-          float tmax = -INFINITY;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            x[r] = ((kb >> r) & 1u) ? S[r] * p.c_log2 : -INFINITY;
-            tmax = fmax_(tmax, x[r]);
-          }
-          // the head's max over this tile's half; the stream's reference
-          // moves (to the max rounded up) only when the max exceeds it by
-          // more than kTau
-          tmax = xor_max(tmax);
-          if (tmax > m_ref[u] + kTau) {
-            const float m_new = __builtin_ceilf(tmax);
-            if (m_ref[u] != -INFINITY) l_run[u] *= __builtin_amdgcn_ldexpf(1.0f, (int)__builtin_fmaxf(m_ref[u] - m_new, -200.0f));
-            m_ref[u] = m_new;
-          }
-          const int hh = 32 * h + 16 * u + t;  // head of the group
-          if (g == 0) *LDSP(float, mx0 + b * kMxBuf + kq * (kHeads * 4) + 16 * t + 4 * (2 * h + u)) = m_ref[u];
-          const float eo = kShift - (m_ref[u] == -INFINITY ? 0.0f : m_ref[u]);  // P = 2^(x - m + kShift)
-          _Float16 ph[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) ph[r] = (_Float16)__builtin_amdgcn_exp2f(x[r] + eo);
-          l_run[u] = __builtin_amdgcn_fdot2(v2h{ph[0], ph[1]}, ones, l_run[u], false);
-          l_run[u] = __builtin_amdgcn_fdot2(v2h{ph[2], ph[3]}, ones, l_run[u], false);
-          *LDSP(v2i, px0 + b * kPxBuf + kPitch * hh + 2 * (16 * kq + 4 * g)) =
-              __builtin_bit_cast(v2i, (v4h{ph[0], ph[1], ph[2], ph[3]}));
-        }
-        st = st == kStages - 1 ? 0 : st + 1;
+        for (int v = 0; v < 4; ++v) acc[v] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qlat[v][2 * m + 1], acc[v], 0, 0, 0);
       }
+    };
+    // the other dim half's head tiles go to its wave through LDS
+    auto send_half = [&](int n, const v4f (&acc)[4]) {
+      const uint32_t a = sp_w + (n & 1) * kSpBuf;
+      *LDSP(v4f, a) = acc[2];
+      *LDSP(v4f, a + 64 * 16) = acc[3];
+    };
+    // softmax of tile n (stage st) for heads 32h + 16u + t: the scores are
+    // this wave's half plus the other wave's; P, the references and the V
+    // scales go to the buffers of tile parity n & 1
+    auto softmax = [&](int n, int st) {
+      const int b = n & 1;
+      const uint32_t kmask = *LDSP(uint32_t, keys + 4 * (n & (kRing - 1)));
+      const float vsc = *LDSP(float, side_at(st) + kSideTok * tok + 4 * g);
+      const v4f o0 = *LDSP(v4f, sp_r + b * kSpBuf);
+      const v4f o1 = *LDSP(v4f, sp_r + b * kSpBuf + 64 * 16);
+      // V scale of block g for token tok, clamped to 2^7, as f16 (both dim
+      // halves' waves write the same value)
+      *LDSP(_Float16, sx0 + b * kSxBuf + kPitch * g + 2 * tok) = (_Float16)__builtin_fminf(vsc, kScaleCap);
+      const uint32_t kb = kmask >> (16 * kq + 4 * g);  // which of tokens 16kq + 4g + r are keys
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const v4f S = own[u] + (u ? o1 : o0);
+        float x[4];
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          x[r] = ((kb >> r) & 1u) ? S[r] * p.c_log2 : -INFINITY;
+          tmax = fmax_(tmax, x[r]);
+        }
+        // the head's max over this tile's half; the stream's reference
+        // moves (to the max rounded up) only when the max exceeds it by
+        // more than kTau
+        tmax = xor_max(tmax);
+        if (tmax > m_ref[u] + kTau) {
+          const float m_new = __builtin_ceilf(tmax);
+          if (m_ref[u] != -INFINITY) l_run[u] *= __builtin_amdgcn_ldexpf(1.0f, (int)__builtin_fmaxf(m_ref[u] - m_new, -200.0f));
+          m_ref[u] = m_new;
+        }
+        const int hh = 32 * h + 16 * u + t;  // head of the group
+        // (the four lanes of a head write the same value)
+        *LDSP(float, mx0 + b * kMxBuf + kq * (kHeads * 4) + 16 * t + 4 * (2 * h + u)) = m_ref[u];
+        const float eo = kShift - (m_ref[u] == -INFINITY ? 0.0f : m_ref[u]);  // P = 2^(x - m + kShift)
+        _Float16 ph[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ph[r] = (_Float16)__builtin_amdgcn_exp2f(x[r] + eo);
+        l_run[u] = __builtin_amdgcn_fdot2(v2h{ph[0], ph[1]}, ones, l_run[u], false);
+        l_run[u] = __builtin_amdgcn_fdot2(v2h{ph[2], ph[3]}, ones, l_run[u], false);
+        *LDSP(v2i, px0 + b * kPxBuf + kPitch * hh + 2 * (16 * kq + 4 * g)) =
+            __builtin_bit_cast(v2i, (v4h{ph[0], ph[1], ph[2], ph[3]}));
+      }
+    };
+
+    // Step s (t0 <= s <= t1 + 1, one barrier each): this half of tile s's
+    // scores, and the softmax of tile s - 1, whose other half arrived over
+    // the barrier.  At the barrier of step s tile s's records have landed
+    // and the PV waves are done with tile s - 3, whose P, scale and
+    // reference buffers tile s - 1 takes.
+    __syncthreads();
+    {
+      v4f acc[4];
+      half_scores(0, acc);
+      send_half(t0, acc);
+      own[0] = acc[0];
+      own[1] = acc[1];
     }
+    int st = 1;  // stage of tile s
+    for (int s = t0 + 1; s < t1; ++s) {
+      __syncthreads();
+      const int st_prev = st == 0 ? kStages - 1 : st - 1;
+      v4f acc[4];
+      half_scores(st, acc);
+      softmax(s - 1, st_prev);
+      send_half(s, acc);
+      own[0] = acc[0];
+      own[1] = acc[1];
+      st = st == kStages - 1 ? 0 : st + 1;
+    }
+    __syncthreads();
+    softmax(t1 - 1, st == 0 ? kStages - 1 : st - 1);
+    __syncthreads();  // step t1 + 1: the PV waves' last tile
     // each head's stream sum and reference for the PV waves' normalisation
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -334,11 +379,12 @@ __global__ __launch_bounds__(w64::kThreads, 1) void smla_fwdw64_kernel(FwdParams
   }
 
   v4f O[4][8];  // O^T slices: dims 128j + 16dt + 4g + [0..3], head 16ht + t
-  float ref[2][4], M[4];  // heads 16ht + t: the streams' last references, O's reference (their max)
-  _Float16 fac[4];        // 2^(reference of this lane's stream - M), exact
+  // heads 16ht + t: the streams' last references; O's reference is their max
+  // (a stream's reference only rises, so that max is also O's running max)
+  v4f rf0 = v4f{-INFINITY, -INFINITY, -INFINITY, -INFINITY}, rf1 = rf0;
+  _Float16 fac[4];  // 2^(reference of this lane's stream - O's reference), exact
 #pragma unroll
   for (int ht = 0; ht < 4; ++ht) {
-    ref[0][ht] = ref[1][ht] = M[ht] = -INFINITY;
     fac[ht] = (_Float16)0.0f;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) O[ht][dt] = v4f{0, 0, 0, 0};
@@ -350,7 +396,7 @@ __global__ __launch_bounds__(w64::kThreads, 1) void smla_fwdw64_kernel(FwdParams
   const uint32_t pv_off = row_off(tv) + 128 * (j ^ (tv & 1)) + 8 * (t & 1);
 
   int st_q = 0;  // stage of tile s (s - t0 mod kStages)
-  for (int s = t0; s <= t1; ++s) {
+  for (int s = t0; s <= t1 + 1; ++s) {
     // this wave's records of tile s and index tile s+3 have landed: after
     // I(s+3) it queued L(x) I(x+3) for x = s+1, s+2 (those that exist)
     if (s + 2 * kAhead - 1 < t1) {
@@ -370,11 +416,11 @@ __global__ __launch_bounds__(w64::kThreads, 1) void smla_fwdw64_kernel(FwdParams
       if (s + 2 * kAhead < t1) issue_idx(s + 2 * kAhead);
     }
     __builtin_amdgcn_s_setprio(0);
-    if (s > t0) {
-      // ---- PV of tile s - 1: O^T[d, h] += V^T[d, tok] P'^T[tok, h]
-      const int n = s - 1;
+    if (s > t0 + 1) {
+      // ---- PV of tile s - 2: O^T[d, h] += V^T[d, tok] P'^T[tok, h]
+      const int n = s - 2;
       const int b = n & 1;
-      const int st_p = st_q == 0 ? kStages - 1 : st_q - 1;
+      const int st_p = st_q >= 2 ? st_q - 2 : st_q + kStages - 2;
       const uint32_t vaddr = lat_at(st_p) + pv_off;
       v2i vr[8];
 #pragma unroll
@@ -384,24 +430,24 @@ __global__ __launch_bounds__(w64::kThreads, 1) void smla_fwdw64_kernel(FwdParams
       // moved, O's reference (their max) and the streams' factors follow
       const v4f r0 = *LDSP(v4f, mx0 + b * kMxBuf + 16 * t);
       const v4f r1 = *LDSP(v4f, mx0 + b * kMxBuf + kHeads * 4 + 16 * t);
-      if (__builtin_amdgcn_ballot_w64(r0.x != ref[0][0] || r0.y != ref[0][1] || r0.z != ref[0][2] || r0.w != ref[0][3] ||
-                                      r1.x != ref[1][0] || r1.y != ref[1][1] || r1.z != ref[1][2] || r1.w != ref[1][3])) {
+      if (__builtin_amdgcn_ballot_w64(r0.x != rf0.x || r0.y != rf0.y || r0.z != rf0.z || r0.w != rf0.w ||
+                                      r1.x != rf1.x || r1.y != rf1.y || r1.z != rf1.z || r1.w != rf1.w)) {
 #pragma unroll
         for (int ht = 0; ht < 4; ++ht) {
-          ref[0][ht] = r0[ht];
-          ref[1][ht] = r1[ht];
-          const float mn = fmax_(M[ht], fmax_(r0[ht], r1[ht]));
-          if (M[ht] != -INFINITY && mn != M[ht]) {
-            const float al = __builtin_amdgcn_ldexpf(1.0f, (int)(M[ht] - mn));
+          const float mo = fmax_(rf0[ht], rf1[ht]);
+          const float mn = fmax_(r0[ht], r1[ht]);
+          if (mo != -INFINITY && mn != mo) {
+            const float al = __builtin_amdgcn_ldexpf(1.0f, (int)(mo - mn));
 #pragma unroll
             for (int dt = 0; dt < 8; ++dt) O[ht][dt] *= al;
           }
-          M[ht] = mn;
           // this lane's tokens 8g .. 8g+7 are stream g >> 1's
           const float rs = g < 2 ? r0[ht] : r1[ht];
           const float f = rs == -INFINITY ? 0.0f : __builtin_amdgcn_ldexpf(1.0f, (int)__builtin_fmaxf(rs - mn, -40.0f));
           fac[ht] = (_Float16)f;
         }
+        rf0 = r0;
+        rf1 = r1;
       }
       v8h vh[8];
 #pragma unroll
