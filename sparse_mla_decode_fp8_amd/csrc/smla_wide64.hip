@@ -37,6 +37,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "smla_device.h"
 
 namespace smla {
@@ -73,6 +75,14 @@ constexpr int kTabOff = kRingOff + kRing * kTile * 4;     // record addresses [P
 constexpr int kKeyOff = kTabOff + 4 * 64;                 // key masks u32 [slot]: bit i = token i is a key
 constexpr int kRedOff = kKeyOff + kRing * 4;              // unit_tiles' reduction; later {l, m} per head and stream
 constexpr int kBytes = kRedOff + kHeads * 16;
+// q exchange before the first tile (18 KB per score wave): waves 0, 1 in record
+// stages 3.. of the latent area, waves 2, 3 from record stage 3 of the side
+// area on (over P, scales, references and halves of scores); none of these is
+// written before the first tile's step.
+constexpr int kQxBytes = 18 * 64 * 16;
+constexpr int kQxA = kLatOff + 3 * kLatStage;
+constexpr int kQxB = kSideOff + 3 * kSideStage;
+static_assert(kQxA + 2 * kQxBytes <= kSideOff && kQxB + 2 * kQxBytes <= kRingOff, "q exchange areas");
 static_assert(kBytes <= 160 * 1024, "LDS budget");
 static_assert(kStages >= kAhead + 3 && kRing >= 2 * kAhead + 1, "pipeline depth");
 
@@ -105,13 +115,38 @@ __global__ __launch_bounds__(w64::kThreads, 1) void smla_fwdw64_kernel(FwdParams
   const int g = lane >> 4;
 
   int rank, sub;
-  if (p.hg == 1) fwd_unit(p.S, p.order == nullptr, rank, sub);  // one head group: sub is the chunk
-  else xcd_unit(p.S * p.hg, rank, sub);
+  // all chunks and head groups of a row on one XCD: the row's q is fetched
+  // into that XCD's L2 once
+  xcd_unit(p.S * p.hg, rank, sub);
   if (rank >= p.T) return;
   const int chunk = sub % p.S;
   const int h0 = kHeads * (sub / p.S);  // first head of this unit's head group
 
   const uint32_t base = lds_addr(s_lds);
+  const __amdgpu_buffer_rsrc_t irs = idx_rsrc(p.indices, p.idx_bytes);
+  auto ring_at = [&](int n) -> uint32_t { return base + kRingOff + (n & (kRing - 1)) * kTile * 4; };
+  // I: index DMA of PV wave j's 8 entries of tile n of the slice starting at
+  // b (bounded reads: positions past nnz read 0; positions past the row are
+  // masked where they are used).
+  auto issue_idx_at = [&](int b, int n) {
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(ring_at(n) + 32 * (w - 4));
+    if (lane < 8) buf_dma4(irs, (uint32_t)(b + n * kTile + 8 * (w - 4) + lane) * 4u, dst);
+  };
+  // Without a plan and with a uniform slice stride, the PV waves guess the
+  // slice start (rank * stride) and queue the unit's first index tiles before
+  // indptr arrives; they queue them again from the real start if the guess
+  // was wrong.
+  const int stride = p.stride;
+  const int ct_g = ((stride + kTile - 1) / kTile + p.S - 1) / p.S;
+  const int t0_g = min(chunk * ct_g, (stride + kTile - 1) / kTile);
+  const int t1_g = min(t0_g + ct_g, (stride + kTile - 1) / kTile);
+  const int beg_g = rank * stride;
+  const bool spec = stride > 0 && w >= 4;
+  if (spec) {
+#pragma unroll
+    for (int k = 0; k < kAhead; ++k)
+      if (t0_g + k < t1_g) issue_idx_at(beg_g, t0_g + k);
+  }
   const int row = p.order ? p.order[rank] : rank;
   const int beg = p.indptr[row];
   const int len = max(p.indptr[row + 1] - beg, 0);
@@ -125,6 +160,7 @@ __global__ __launch_bounds__(w64::kThreads, 1) void smla_fwdw64_kernel(FwdParams
   const int Hl = min(H - h0, kHeads);  // heads of this group
 
   if (t0 >= t1) {  // nothing to attend: zero output and the sink's lse, or an empty partial
+    if (spec) wait_vm<0>();  // the guessed index tiles land before the block ends
     if (split) {
       for (int hh = h0 + tid; hh < h0 + Hl; hh += kThreads) p.part_lse[(int64_t)unit * H + hh] = -INFINITY;
     } else {
@@ -156,26 +192,60 @@ __global__ __launch_bounds__(w64::kThreads, 1) void smla_fwdw64_kernel(FwdParams
     // wave's: latent K-step 2m / 2m+1 (m = 0..3) = dims 256h + 64m + 16g +
     // [0..7] / [8..15], rope K-step = dims 512 + 32h + 8g + [0..7].  Heads >= H
     // load head 0 (every lane issues the same loads) and are zeroed.
+    // The two waves of a dim half need the same q: wave (h, kq) loads head
+    // tiles v = 2kq, 2kq+1 (18 loads per lane), publishes them in LDS and,
+    // after a barrier, reads the other two that wave (h, 1 - kq) loaded.
     v8bf qlat[4][8], qrope[4];
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int hq = 16 * ((2 * h + v) & 3) + t;
-      const bool hq_ok = hq < Hl;
-      v4i qr[9];
-      const uint64_t qa = (uint64_t)(uintptr_t)(p.q + row * p.q_st + (int64_t)(h0 + (hq_ok ? hq : 0)) * p.q_sh);
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        gload16(qr[2 * m], qa + 2 * (256 * h + 64 * m + 16 * g));
-        gload16(qr[2 * m + 1], qa + 2 * (256 * h + 64 * m + 16 * g + 8));
-      }
-      gload16(qr[8], qa + 2 * (kLat + 32 * h + 8 * g));
-      wait_vm<0>();
-#pragma unroll
-      for (int k = 0; k < 9; ++k) asm volatile("" : "+v"(qr[k]));
+    auto qx_at = [&](int wave) -> uint32_t { return base + (wave < 2 ? kQxA : kQxB) + (wave & 1) * kQxBytes; };
+    auto take = [&](int v, const v4i (&qr)[9]) {
+      const bool hq_ok = 16 * ((2 * h + v) & 3) + t < Hl;
 #pragma unroll
       for (int k = 0; k < 8; ++k) qlat[v][k] = __builtin_bit_cast(v8bf, hq_ok ? qr[k] : v4i{0, 0, 0, 0});
       qrope[v] = __builtin_bit_cast(v8bf, hq_ok ? qr[8] : v4i{0, 0, 0, 0});
-    }
+    };
+    auto load_pair = [&](auto V0) {
+      constexpr int v0 = decltype(V0)::value;
+      v4i qr[2][9];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int hq = 16 * ((2 * h + v0 + i) & 3) + t;
+        const uint64_t qa = (uint64_t)(uintptr_t)(p.q + row * p.q_st + (int64_t)(h0 + (hq < Hl ? hq : 0)) * p.q_sh);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          gload16(qr[i][2 * m], qa + 2 * (256 * h + 64 * m + 16 * g));
+          gload16(qr[i][2 * m + 1], qa + 2 * (256 * h + 64 * m + 16 * g + 8));
+        }
+        gload16(qr[i][8], qa + 2 * (kLat + 32 * h + 8 * g));
+      }
+      wait_vm<0>();
+      const uint32_t dst = qx_at(w) + 16 * lane;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int k = 0; k < 9; ++k) {
+          asm volatile("" : "+v"(qr[i][k]));
+          *LDSP(v4i, dst + (9 * i + k) * 1024) = qr[i][k];
+        }
+      take(v0, qr[0]);
+      take(v0 + 1, qr[1]);
+    };
+    auto read_pair = [&](auto V0) {
+      constexpr int v0 = decltype(V0)::value;
+      const uint32_t src = qx_at(w ^ 2) + 16 * lane;
+      v4i qr[2][9];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int k = 0; k < 9; ++k) qr[i][k] = *LDSP(v4i, src + (9 * i + k) * 1024);
+      take(v0, qr[0]);
+      take(v0 + 1, qr[1]);
+    };
+    // wave (h, kq) loads tiles 2(h ^ kq), 2(h ^ kq) + 1: own tiles (v = 0, 1) when kq = 0
+    if (kq == 0) load_pair(std::integral_constant<int, 0>{});
+    else load_pair(std::integral_constant<int, 2>{});
+    __syncthreads();
+    if (kq == 0) read_pair(std::integral_constant<int, 2>{});
+    else read_pair(std::integral_constant<int, 0>{});
 
     float m_ref[2] = {-INFINITY, -INFINITY};  // head 32h + 16u + t, this stream: reference (log2 units, integer)
     float l_run[2] = {0.0f, 0.0f};            // this lane's part of the stream's sum of P
@@ -311,17 +381,11 @@ __global__ __launch_bounds__(w64::kThreads, 1) void smla_fwdw64_kernel(FwdParams
 
   // ================================================================== PV waves
   const int j = w - 4;  // scale block: dims 128j .. 128j+127; gather: tokens 8j .. 8j+7
-  const __amdgpu_buffer_rsrc_t irs = idx_rsrc(p.indices, p.idx_bytes);
   const uint8_t* const zero = p.zero;
-  auto ring_at = [&](int n) -> uint32_t { return base + kRingOff + (n & (kRing - 1)) * kTile * 4; };
   const uint32_t tab = base + kTabOff + 64 * j;  // this wave's 8 record addresses
 
-  // I: index DMA of this wave's 8 entries of tile n (bounded reads: positions
-  // past nnz read 0; positions past the row are masked where they are used).
-  auto issue_idx = [&](int n) {
-    const uint32_t dst = __builtin_amdgcn_readfirstlane(ring_at(n) + 32 * j);
-    if (lane < 8) buf_dma4(irs, (uint32_t)(beg + n * kTile + 8 * j + lane) * 4u, dst);
-  };
+  // I: index DMA of this wave's 8 entries of tile n of the row's slice
+  auto issue_idx = [&](int n) { issue_idx_at(beg, n); };
   // record addresses of this wave's 8 tokens of tile n (no key: the zero
   // record), and their bits of the tile's key mask
   auto fill_table = [&](int n) {
@@ -359,9 +423,13 @@ __global__ __launch_bounds__(w64::kThreads, 1) void smla_fwdw64_kernel(FwdParams
   // ---- prologue: index tiles t0 .. t0+2, then records of tiles t0 .. t0+2,
   // each followed by the index tile three ahead.  From here on the issue
   // order is ... L(n) I(n+3) L(n+1) I(n+4) ..., so waiting for I(n+3) covers L(n).
+  // index tiles t0 .. t0+2, unless the guessed ones are those
+  if (!(spec && beg == beg_g && t0 == t0_g && t1 == t1_g)) {
+    if (spec) wait_vm<0>();  // the guessed tiles land before the ring is refilled
 #pragma unroll
-  for (int k = 0; k < kAhead; ++k)
-    if (t0 + k < t1) issue_idx(t0 + k);
+    for (int k = 0; k < kAhead; ++k)
+      if (t0 + k < t1) issue_idx(t0 + k);
+  }
 #pragma unroll
   for (int k = 0; k < kAhead; ++k) {
     if (t0 + k < t1) {
@@ -378,6 +446,7 @@ __global__ __launch_bounds__(w64::kThreads, 1) void smla_fwdw64_kernel(FwdParams
     }
   }
 
+  __syncthreads();  // the score waves' q exchange
   v4f O[4][8];  // O^T slices: dims 128j + 16dt + 4g + [0..3], head 16ht + t
   // heads 16ht + t: the streams' last references; O's reference is their max
   // (a stream's reference only rises, so that max is also O's running max)
@@ -502,7 +571,7 @@ __global__ __launch_bounds__(w64::kThreads, 1) void smla_fwdw64_kernel(FwdParams
 }
 
 hipError_t launch_fwd_wide64(const FwdParams& p, Events ev, hipStream_t s) {
-  const int64_t blocks = p.hg == 1 ? fwd_grid(p.T, p.S, p.order == nullptr) : xcd_grid(p.T, p.S * p.hg);
+  const int64_t blocks = xcd_grid(p.T, p.S * p.hg);
   if (p.km.paged)
     hipExtLaunchKernelGGL(smla_fwdw64_kernel<true>, dim3((unsigned)blocks), dim3(w64::kThreads), 0, s, ev.start,
                           ev.stop, 0, p);

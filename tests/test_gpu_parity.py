@@ -193,6 +193,30 @@ def test_wide_stream_edges(smla, has_invalid, split, outliers):
         compare(out, lse, ro, rl, label=f"streams inv{has_invalid} s{split} o0")
 
 
+@pytest.mark.parametrize("H,split,has_invalid", [(16, 0, 0), (16, 2, 1), (64, 0, 0), (64, 3, 0), (64, 2, 1), (128, 2, 0)])
+def test_guessed_slice_starts(smla, H, split, has_invalid):
+    """Without a plan and with nnz a multiple of T, each unit guesses its slice
+    start (row x nnz/T) and queues its first index tiles before indptr
+    arrives.  The rows here make the guess right for some units and wrong for
+    others (the start, the length or a chunk's bounds differ; one row is
+    empty), so both the kept and the re-queued index tiles are checked."""
+    rng = np.random.default_rng(60 + H + split + has_invalid)
+    N = 5000
+    lengths = [300, 100, 200, 200, 0, 400, 200, 200]  # nnz = 1,600 = 8 x 200
+    sl = [rng.integers(0, N, L) for L in lengths]
+    if has_invalid:  # trailing and interior padding inside the same lengths
+        sl[2][150:] = -1
+        sl[3][::7] = -1
+        sl[6][:] = -1
+    w = custom(f"guess_H{H}_s{split}_inv{has_invalid}", H, N, sl, seed=61 + H, has_invalid=has_invalid)
+    assert w.nnz % w.T == 0
+    smla.set_option("split", split)
+    note(f"guessed slice starts H={H} split={split} has_invalid={has_invalid} T={w.T}")
+    out, lse = run_gpu(w)
+    ro, rl = run_oracle(w)
+    compare(out, lse, ro, rl, label=f"guess H{H} s{split} inv{has_invalid}")
+
+
 @pytest.mark.parametrize("split", [1, 2, 3, 7, 32])
 def test_forced_split(smla, split):
     rng = np.random.default_rng(7)
