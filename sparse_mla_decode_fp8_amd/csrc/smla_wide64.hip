@@ -44,6 +44,7 @@
 namespace smla {
 namespace w64 {
 
+typedef uint64_t v2u64 __attribute__((ext_vector_type(2)));
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kHeads = 64;
@@ -248,6 +249,7 @@ __global__ __launch_bounds__(w64::kThreads, 1) void smla_fwdw64_kernel(FwdParams
     else read_pair(std::integral_constant<int, 0>{});
 
     float m_ref[2] = {-INFINITY, -INFINITY};  // head 32h + 16u + t, this stream: reference (log2 units, integer)
+    float eo[2] = {kShift, kShift};           // kShift - m_ref (kShift while m_ref is -inf): P = 2^(x + eo)
     float l_run[2] = {0.0f, 0.0f};            // this lane's part of the stream's sum of P
     v4f own[2];                               // this dim half's scores of the previous tile, heads 32h + 16u + t
     const v2h ones = v2h{(_Float16)1.0f, (_Float16)1.0f};
@@ -304,36 +306,37 @@ __global__ __launch_bounds__(w64::kThreads, 1) void smla_fwdw64_kernel(FwdParams
       const float vsc = *LDSP(float, side_at(st) + kSideTok * tok + 4 * g);
       const v4f o0 = *LDSP(v4f, sp_r + b * kSpBuf);
       const v4f o1 = *LDSP(v4f, sp_r + b * kSpBuf + 64 * 16);
-      // V scale of block g for token tok, clamped to 2^7, as f16 (both dim
-      // halves' waves write the same value)
-      *LDSP(_Float16, sx0 + b * kSxBuf + kPitch * g + 2 * tok) = (_Float16)__builtin_fminf(vsc, kScaleCap);
+      // V scale of block g for token tok, clamped to 2^7, as f16 (the waves
+      // of dim half 0 write it)
+      if (h == 0) *LDSP(_Float16, sx0 + b * kSxBuf + kPitch * g + 2 * tok) = (_Float16)__builtin_fminf(vsc, kScaleCap);
       const uint32_t kb = kmask >> (16 * kq + 4 * g);  // which of tokens 16kq + 4g + r are keys
+      const float c = p.c_log2;  // > 0: the scaled max is the max of the scaled scores
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const v4f S = own[u] + (u ? o1 : o0);
-        float x[4];
-        float tmax = -INFINITY;
+        float y[4];  // the scores of keys, -inf elsewhere
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          x[r] = ((kb >> r) & 1u) ? S[r] * p.c_log2 : -INFINITY;
-          tmax = fmax_(tmax, x[r]);
-        }
+        for (int r = 0; r < 4; ++r) y[r] = ((kb >> r) & 1u) ? S[r] : -INFINITY;
+        float tmax = fmax_(fmax_(y[0], y[1]), fmax_(y[2], y[3])) * c;
         // the head's max over this tile's half; the stream's reference
         // moves (to the max rounded up) only when the max exceeds it by
-        // more than kTau
-        tmax = xor_max(tmax);
-        if (tmax > m_ref[u] + kTau) {
-          const float m_new = __builtin_ceilf(tmax);
-          if (m_ref[u] != -INFINITY) l_run[u] *= __builtin_amdgcn_ldexpf(1.0f, (int)__builtin_fmaxf(m_ref[u] - m_new, -200.0f));
-          m_ref[u] = m_new;
+        // more than kTau.  The lanes' maxima are reduced over the head's
+        // four lanes only when some lane's exceeds (a wave-wide ballot).
+        if (__builtin_amdgcn_ballot_w64(tmax > m_ref[u] + kTau)) {
+          tmax = xor_max(tmax);
+          if (tmax > m_ref[u] + kTau) {
+            const float m_new = __builtin_ceilf(tmax);
+            if (m_ref[u] != -INFINITY) l_run[u] *= __builtin_amdgcn_ldexpf(1.0f, (int)__builtin_fmaxf(m_ref[u] - m_new, -200.0f));
+            m_ref[u] = m_new;
+            eo[u] = kShift - m_new;
+          }
         }
         const int hh = 32 * h + 16 * u + t;  // head of the group
         // (the four lanes of a head write the same value)
         *LDSP(float, mx0 + b * kMxBuf + kq * (kHeads * 4) + 16 * t + 4 * (2 * h + u)) = m_ref[u];
-        const float eo = kShift - (m_ref[u] == -INFINITY ? 0.0f : m_ref[u]);  // P = 2^(x - m + kShift)
         _Float16 ph[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) ph[r] = (_Float16)__builtin_amdgcn_exp2f(x[r] + eo);
+        for (int r = 0; r < 4; ++r) ph[r] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(y[r], c, eo[u]));
         l_run[u] = __builtin_amdgcn_fdot2(v2h{ph[0], ph[1]}, ones, l_run[u], false);
         l_run[u] = __builtin_amdgcn_fdot2(v2h{ph[2], ph[3]}, ones, l_run[u], false);
         *LDSP(v2i, px0 + b * kPxBuf + kPitch * hh + 2 * (16 * kq + 4 * g)) =
@@ -499,8 +502,10 @@ __global__ __launch_bounds__(w64::kThreads, 1) void smla_fwdw64_kernel(FwdParams
       // moved, O's reference (their max) and the streams' factors follow
       const v4f r0 = *LDSP(v4f, mx0 + b * kMxBuf + 16 * t);
       const v4f r1 = *LDSP(v4f, mx0 + b * kMxBuf + kHeads * 4 + 16 * t);
-      if (__builtin_amdgcn_ballot_w64(r0.x != rf0.x || r0.y != rf0.y || r0.z != rf0.z || r0.w != rf0.w ||
-                                      r1.x != rf1.x || r1.y != rf1.y || r1.z != rf1.z || r1.w != rf1.w)) {
+      // (references are integers or -inf: bit equality is equality)
+      const v2u64 a0 = __builtin_bit_cast(v2u64, r0), a1 = __builtin_bit_cast(v2u64, r1);
+      const v2u64 c0 = __builtin_bit_cast(v2u64, rf0), c1 = __builtin_bit_cast(v2u64, rf1);
+      if (__builtin_amdgcn_ballot_w64(a0.x != c0.x || a0.y != c0.y || a1.x != c1.x || a1.y != c1.y)) {
 #pragma unroll
         for (int ht = 0; ht < 4; ++ht) {
           const float mo = fmax_(rf0[ht], rf1[ht]);
@@ -515,9 +520,9 @@ __global__ __launch_bounds__(w64::kThreads, 1) void smla_fwdw64_kernel(FwdParams
           const float f = rs == -INFINITY ? 0.0f : __builtin_amdgcn_ldexpf(1.0f, (int)__builtin_fmaxf(rs - mn, -40.0f));
           fac[ht] = (_Float16)f;
         }
-        rf0 = r0;
-        rf1 = r1;
       }
+      rf0 = r0;  // (unchanged unless a reference moved)
+      rf1 = r1;
       v8h vh[8];
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) vh[dt] = cvt8_f16(vr[dt]);
