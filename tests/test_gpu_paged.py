@@ -133,6 +133,27 @@ def test_paged_sink_matches_oracle(smla, H, split):
     np.testing.assert_allclose(l[0].cpu().numpy(), sink.astype(np.float32), rtol=2e-6, atol=0)
 
 
+@pytest.mark.parametrize("H,split", [(16, 0), (64, 0), (64, 3), (128, 2)])
+def test_paged_uniform_rows(smla, H, split):
+    """Rows of one length (so nnz is a multiple of T and every unit guesses
+    its slice start and queues its first index tiles before indptr arrives),
+    with -1 entries: through both pools, with sinks, against the oracle."""
+    w = ragged_workload(f"paged_uni_H{H}_S{split}", H, [700] * 6, 8000, seed=90 + H + split)
+    assert w.nnz % w.T == 0
+    rng = np.random.default_rng(91 + split)
+    pools, entry_of = paged_layout(rng, w.kv.numpy(), per_page=(16, 8), pad=(3 * 656 + 16, 0))
+    ent = entries(w, entry_of)
+    sink = sink_values(rng, H)
+    note(f"paged uniform rows H={H} split={split} T={w.T}")
+    smla.set_option("split", split)
+    try:
+        o, l = run_paged(smla, w, to_dev(pools), ent, sink=sink)
+    finally:
+        smla.set_option("split", 0)
+    ro, rl = run_oracle_paged(w, pools, ent, sink=sink)
+    compare(o, l, ro, rl, label=f"paged_uniform_H{H}_S{split}")
+
+
 def test_paged_absent_pool(smla):
     """With the compressed pool absent, its entries are not keys: the result
     equals the oracle's with those entries replaced by -1, with and without
