@@ -110,12 +110,15 @@ __device__ __forceinline__ float xor_sum(float v) {
   return b.x + b.y;
 }
 
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __builtin_bit_cast(uint32_t, f);
-  if ((u & 0x7f800000u) == 0x7f800000u) return (uint16_t)((u >> 16) | ((u & 0xffff) ? 0x40 : 0));
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+// Two f32 to two bf16, rounded to nearest even (one v_cvt_pk_bf16_f32; NaN
+// stays NaN, overflow rounds to infinity), packed lo | hi << 16.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f{lo, hi}), v2bf));
 }
+// Four f32 to four packed bf16 (two words).
+__device__ __forceinline__ v2i pack_bf16x4(v4f a) { return v2i{(int)pack_bf16x2(a.x, a.y), (int)pack_bf16x2(a.z, a.w)}; }
+// An f32 rounded to bf16 (nearest even) and widened back to f32.
+__device__ __forceinline__ float round_bf16(float f) { return __builtin_bit_cast(float, pack_bf16x2(f, 0.0f) << 16); }
 
 // 4 e4m3 codes (one word) x pow2 scale -> 4 bf16 (exact), as two v2bf.
 __device__ __forceinline__ void cvt4_bf16(int w, float sc, v2bf& lo, v2bf& hi) {

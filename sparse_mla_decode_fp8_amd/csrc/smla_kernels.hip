@@ -592,11 +592,8 @@ __global__ __launch_bounds__(n16::kThreads, 1) void smla_fwd16_kernel(
     } else {
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
-        const v4f acc = O[dt] * inv;
         const int d = 64 * w + 16 * dt + 4 * g;
-        const uint32_t w0 = f32_to_bf16_rne(acc.x) | ((uint32_t)f32_to_bf16_rne(acc.y) << 16);
-        const uint32_t w1 = f32_to_bf16_rne(acc.z) | ((uint32_t)f32_to_bf16_rne(acc.w) << 16);
-        *(v2i*)(p.out + row * p.o_st + h * p.o_sh + d) = v2i{(int)w0, (int)w1};
+        *(v2i*)(p.out + row * p.o_st + h * p.o_sh + d) = pack_bf16x4(O[dt] * inv);
       }
     }
   }
@@ -643,9 +640,7 @@ __device__ __forceinline__ void combine_row(const float* __restrict__ part_lse, 
   }
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
   const v4f o = acc * inv;
-  const uint32_t w0 = f32_to_bf16_rne(o.x) | ((uint32_t)f32_to_bf16_rne(o.y) << 16);
-  const uint32_t w1 = f32_to_bf16_rne(o.z) | ((uint32_t)f32_to_bf16_rne(o.w) << 16);
-  *(v2i*)(p.out + row * p.o_st + h * p.o_sh + part_dim(4 * threadIdx.x)) = v2i{(int)w0, (int)w1};
+  *(v2i*)(p.out + row * p.o_st + h * p.o_sh + part_dim(4 * threadIdx.x)) = pack_bf16x4(o);
   if (threadIdx.x == 0 && p.lse)
     p.lse[(int64_t)row * p.H + h] = L > 0.0f ? (M + __builtin_log2f(L)) * kLn2 : -INFINITY;
 }

@@ -596,7 +596,7 @@ __global__ __launch_bounds__(256) void smla_combine41_kernel(
   // bf16, then the inverse GPT-J rotation of the rope dims (448 ..)
   float y[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) y[i] = __builtin_bit_cast(float, (uint32_t)f32_to_bf16_rne(acc[i] * inv) << 16);
+  for (int i = 0; i < 8; ++i) y[i] = round_bf16(acc[i] * inv);
   if (rope) {
 #pragma unroll
     for (int half = 0; half < 2; ++half) {

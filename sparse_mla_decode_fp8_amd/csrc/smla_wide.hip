@@ -397,11 +397,8 @@ __global__ __launch_bounds__(nw::kThreads, 1) void smla_fwdw_kernel(FwdParams p)
       } else {
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
-          const v4f acc = O[j][dt] * nm.scale;
           const int d = 64 * w + 16 * dt + 4 * g;
-          const uint32_t w0 = f32_to_bf16_rne(acc.x) | ((uint32_t)f32_to_bf16_rne(acc.y) << 16);
-          const uint32_t w1 = f32_to_bf16_rne(acc.z) | ((uint32_t)f32_to_bf16_rne(acc.w) << 16);
-          *(v2i*)(p.out + row * p.o_st + h * p.o_sh + d) = v2i{(int)w0, (int)w1};
+          *(v2i*)(p.out + row * p.o_st + h * p.o_sh + d) = pack_bf16x4(O[j][dt] * nm.scale);
         }
       }
     }

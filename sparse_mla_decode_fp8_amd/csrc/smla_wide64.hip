@@ -564,11 +564,8 @@ __global__ __launch_bounds__(w64::kThreads, 1) void smla_fwdw64_kernel(FwdParams
       } else {
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
-          const v4f acc = O[ht][dt] * nm.scale;
           const int d = 128 * j + 16 * dt + 4 * g;
-          const uint32_t w0 = f32_to_bf16_rne(acc.x) | ((uint32_t)f32_to_bf16_rne(acc.y) << 16);
-          const uint32_t w1 = f32_to_bf16_rne(acc.z) | ((uint32_t)f32_to_bf16_rne(acc.w) << 16);
-          *(v2i*)(p.out + row * p.o_st + h * p.o_sh + d) = v2i{(int)w0, (int)w1};
+          *(v2i*)(p.out + row * p.o_st + h * p.o_sh + d) = pack_bf16x4(O[ht][dt] * nm.scale);
         }
       }
     }
