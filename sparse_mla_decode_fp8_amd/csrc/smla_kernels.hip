@@ -162,6 +162,8 @@ constexpr int kIdxRingOff = kMxOff + 16 * kWaves * 4;
 constexpr int kTabOff = kIdxRingOff + kIdxRing * kTile * 4;  // record addresses [2][token 128]
 constexpr int kBytes = kTabOff + 2 * kTile * 8;
 static_assert(kBytes <= 160 * 1024, "LDS budget");
+constexpr int kOutPitch = 2 * 64 + 16;            // epilogue staging row: 64 bf16 dims + pad
+static_assert(kWaves * 16 * kOutPitch <= 16 * kQRow, "epilogue staging fits the q area");
 // Vector-memory instructions one wave issues per tile: 8 latent DMAs (token
 // pairs) and 3 side loads; one index DMA per tile besides.
 constexpr int kTileVm = 8 + 3;
@@ -586,15 +588,22 @@ __global__ __launch_bounds__(n16::kThreads, 1) void smla_fwd16_kernel(
     if (split) p.part_lse[(int64_t)unit * H + h] = l2;
     else if (p.lse) p.lse[(int64_t)row * H + h] = l2 * kLn2;
   }
-  if (h_ok) {
-    if (split) {
-      st_part16(p.part_o + ((int64_t)unit * H + h) * kLat + 64 * w, g, O, inv);
-    } else {
+  if (split) {
+    if (h_ok) st_part16(p.part_o + ((int64_t)unit * H + h) * kLat + 64 * w, g, O, inv);
+  } else {
+    // bf16 rows staged in this wave's part of the q area (idle after the
+    // prologue), then read back 8 lanes per head, so that each store
+    // instruction writes eight heads' 128 contiguous bytes (the wave's own
+    // LDS writes, which LDS performs in order)
+    const uint32_t ob = base + kQOff + w * (16 * kOutPitch);
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        const int d = 64 * w + 16 * dt + 4 * g;
-        *(v2i*)(p.out + row * p.o_st + h * p.o_sh + d) = pack_bf16x4(O[dt] * inv);
-      }
+    for (int dt = 0; dt < 4; ++dt) *LDSP(v2i, ob + kOutPitch * t + 2 * (16 * dt + 4 * g)) = pack_bf16x4(O[dt] * inv);
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int hh = 8 * i + (lane >> 3);
+      const v4i v = *LDSP(v4i, ob + kOutPitch * hh + 16 * (lane & 7));
+      if (hh < H) *(v4i*)(p.out + row * p.o_st + hh * p.o_sh + 64 * w + 8 * (lane & 7)) = v;
     }
   }
 }

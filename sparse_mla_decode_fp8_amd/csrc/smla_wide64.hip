@@ -60,6 +60,7 @@ constexpr int kPitch = 96;                      // P and scale rows: 32 f16 + pa
 // pairs) and 2 side DMAs (72 chunks of 16 B); one index DMA besides.
 constexpr int kTileVm = 6;
 constexpr int kQLoads = 18;                     // q loads per lane (16 latent + 2 rope)
+constexpr int kOutPitch = 2 * 128 + 16;         // epilogue staging row: 128 bf16 dims + pad
 
 constexpr int kLatOff = 0;
 constexpr int kSideOff = kLatOff + kStages * kLatStage;
@@ -85,6 +86,7 @@ constexpr int kQxA = kLatOff + 3 * kLatStage;
 constexpr int kQxB = kSideOff + 3 * kSideStage;
 static_assert(kQxA + 2 * kQxBytes <= kSideOff && kQxB + 2 * kQxBytes <= kRingOff, "q exchange areas");
 static_assert(kBytes <= 160 * 1024, "LDS budget");
+static_assert(4 * kHeads * kOutPitch <= kStages * kLatStage, "epilogue staging fits the latent stages");
 static_assert(kStages >= kAhead + 3 && kRing >= 2 * kAhead + 1, "pipeline depth");
 
 // vmcnt <= n for a wave-uniform n in [0, 24]
@@ -539,7 +541,10 @@ __global__ __launch_bounds__(w64::kThreads, 1) void smla_fwdw64_kernel(FwdParams
   __syncthreads();  // every head's {l, m} is written
 
   // ---- epilogue: this wave's 128 dims of every head (split: a partial
-  // without the sink, which the combine folds in)
+  // without the sink, which the combine folds in).  An unsplit row's bf16
+  // output is staged in this wave's part of the (now idle) record stages, so
+  // that consecutive lanes store consecutive bytes of a head's row.
+  const uint32_t ob = lat_at(0) + j * (kHeads * kOutPitch);
 #pragma unroll
   for (int ht = 0; ht < 4; ++ht) {
     const int hl = 16 * ht + t;  // head of the group
@@ -556,18 +561,28 @@ __global__ __launch_bounds__(w64::kThreads, 1) void smla_fwdw64_kernel(FwdParams
       if (split) p.part_lse[(int64_t)unit * H + h] = nm.lse2;
       else if (p.lse) p.lse[(int64_t)row * H + h] = nm.lse2 * kLn2;
     }
-    if (h_ok) {
-      if (split) {
+    if (split) {
+      if (h_ok) {
         uint16_t* const po = p.part_o + ((int64_t)unit * H + h) * kLat + 128 * j;
         st_part16(po, g, &O[ht][0], nm.scale);
         st_part16(po + 64, g, &O[ht][4], nm.scale);
-      } else {
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-          const int d = 128 * j + 16 * dt + 4 * g;
-          *(v2i*)(p.out + row * p.o_st + h * p.o_sh + d) = pack_bf16x4(O[ht][dt] * nm.scale);
-        }
       }
+    } else {
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+        *LDSP(v2i, ob + kOutPitch * hl + 2 * (16 * dt + 4 * g)) = pack_bf16x4(O[ht][dt] * nm.scale);
+    }
+  }
+  if (!split) {
+    // this wave's rows back from LDS (the wave's own writes, which LDS
+    // performs in order): 16 lanes per head, so each store instruction writes
+    // four heads' 256 contiguous bytes
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < kHeads / 4; ++i) {
+      const int hl = 4 * i + (lane >> 4);
+      const v4i v = *LDSP(v4i, ob + kOutPitch * hl + 16 * (lane & 15));
+      if (hl < Hl) *(v4i*)(p.out + row * p.o_st + (h0 + hl) * p.o_sh + 128 * j + 8 * (lane & 15)) = v;
     }
   }
 }
