@@ -73,6 +73,26 @@ __global__ __launch_bounds__(256) void smla_plan_scan_kernel(
   if (tid == 0) p.row_tiles[row] = tiles_of(max(max(s_red[0], s_red[1]), max(s_red[2], s_red[3])), p.tile);
 }
 
+// Adds one per active lane to cnt[b] and returns each active lane's slot (the
+// old count plus its rank among the wave's lanes with the same b).  When every
+// active lane of the wave has the same b (equal-length rows) that is one LDS
+// atomic for the wave instead of one per lane on a single address; otherwise
+// one atomic per lane.  Wave-uniform control flow.
+__device__ __forceinline__ int wave_bucket_add(int* cnt, int b, bool active) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t act = __ballot(active);
+  if (!act) return 0;
+  const int leader = __builtin_ctzll(act);
+  const int lb = __shfl(b, leader);
+  if (__ballot(active && b == lb) == act) {
+    int base = 0;
+    if (lane == leader) base = atomicAdd(&cnt[lb], (int)__popcll(act));
+    base = __shfl(base, leader);
+    return base + (int)__popcll(act & ((1ull << lane) - 1));
+  }
+  return active ? atomicAdd(&cnt[b], 1) : 0;
+}
+
 // One block: tile counts of every row (from the scan, or from indptr) and a
 // counting sort of the rows by tile count, longest first (the FlyDSL page
 // issues long rows first so the long tail starts early).
@@ -85,15 +105,20 @@ __global__ __launch_bounds__(1024) void smla_plan_sort_kernel(
   const int tid = threadIdx.x;
   for (int i = tid; i < kPlanBuckets; i += blockDim.x) s_cnt[i] = 0;
   __syncthreads();
-  for (int r = tid; r < T; r += blockDim.x) {
-    int t;
-    if (has_invalid) {
-      t = row_tiles[r];
-    } else {
-      t = tiles_of(max(indptr[r + 1] - indptr[r], 0), p.tile);
-      row_tiles[r] = t;
+  // (every thread runs the same number of rounds: the wave-wide steps need
+  // whole waves)
+  for (int r0 = 0; r0 < T; r0 += blockDim.x) {
+    const int r = r0 + tid;
+    int t = 0;
+    if (r < T) {
+      if (has_invalid) {
+        t = row_tiles[r];
+      } else {
+        t = tiles_of(max(indptr[r + 1] - indptr[r], 0), p.tile);
+        row_tiles[r] = t;
+      }
     }
-    atomicAdd(&s_cnt[min(t, kPlanBuckets - 1)], 1);
+    wave_bucket_add(s_cnt, min(t, kPlanBuckets - 1), r < T);
   }
   __syncthreads();
   // exclusive prefix over buckets in descending order: start[b] = sum_{b' > b} cnt[b'].
@@ -117,9 +142,11 @@ __global__ __launch_bounds__(1024) void smla_plan_sort_kernel(
     s_cnt[b] = off + incl - c;
   }
   __syncthreads();
-  for (int r = tid; r < T; r += blockDim.x) {
-    const int t = row_tiles[r];
-    p.order[atomicAdd(&s_cnt[min(t, kPlanBuckets - 1)], 1)] = r;
+  for (int r0 = 0; r0 < T; r0 += blockDim.x) {
+    const int r = r0 + tid;
+    const int t = r < T ? row_tiles[r] : 0;
+    const int slot = wave_bucket_add(s_cnt, min(t, kPlanBuckets - 1), r < T);
+    if (r < T) p.order[slot] = r;
   }
 }
 
