@@ -193,6 +193,10 @@ CONFIGS = {
     3: dict(name="ragged_T256_H16_N262144_top2048_invalid", T=256, H=16, N=262144, topk=2048),
     4: dict(name="largecache_T128_H16_N8388608_top2048", T=128, H=16, N=8388608, topk=2048),
     5: dict(name="prefill_T4096_H64_N32768_top2048_causal", T=4096, H=64, N=32768, topk=2048),
+    # An additional workload (not one of the five): the causal prefill of one
+    # 2,048-token prompt, where row r attends to tokens 0 .. r (r + 1 keys, padded
+    # to 2,048 with -1): a wide-head batch of genuinely ragged rows.
+    6: dict(name="prefill_T2048_H64_N2048_top2048_causal_ragged", T=2048, H=64, N=2048, topk=2048),
 }
 
 
@@ -207,7 +211,8 @@ def heads_name(name: str, H: int) -> str:
 
 def make_workload(cfg: int, device="cpu", seed: Optional[int] = None,
                   T: Optional[int] = None, H: Optional[int] = None) -> Workload:
-    """Build configuration ``cfg`` (1..5).  ``seed`` defaults to the config
+    """Build configuration ``cfg`` (1..5, or 6: the additional ragged causal
+    prefill).  ``seed`` defaults to the config
     number.  ``T`` may shrink the number of query rows (rows keep the same
     recipe; for the causal config the row positions keep their full-size
     meaning, i.e. row r is still row r of a 4096-row batch).  ``H`` replaces
@@ -239,6 +244,11 @@ def make_workload(cfg: int, device="cpu", seed: Optional[int] = None,
     if cfg == 4:
         return build_workload(name, T, H, N, lambda g, r, m: distinct_uniform(g, N, k),
                               seed=seed, device=device)
+    if cfg == 6:
+        def rows(g, r, m):
+            take = min(r + 1, k)
+            return np.concatenate([np.arange(take, dtype=np.int64), -np.ones(k - take, np.int64)])
+        return build_workload(name, T, H, N, rows, seed=seed, has_invalid=1, device=device)
     if cfg == 5:
         def rows(g, r, m):
             avail = min(r + N - Tf + 1, N)

@@ -374,6 +374,19 @@ def test_causal_ragged_longest_first(smla, H):
     compare(out, lse, ro, rl, rows=rows, label=f"causal_H{H}")
 
 
+def test_ragged_causal_prefill_workload(smla):
+    """The additional workload: a 2,048-token causal prefill at 64 heads (row r
+    attends to tokens 0 .. r, padded to 2,048 with -1), every row computed and
+    sampled rows against the oracle, the first row (one key) and the last (all
+    2,048) among them."""
+    w = synth.make_workload(6, device="cuda")
+    note(f"ragged causal prefill {w.name}")
+    out, lse = run_gpu(w)
+    rows = sorted(set(sample_rows(w.T, 16, seed=6).tolist()) | {1, 31, 32, 33})
+    ro, rl = run_oracle(w, rows=rows)
+    compare(out, lse, ro, rl, rows=rows, label="ragged_causal_prefill")
+
+
 def test_repeat_calls_bitwise_identical(smla):
     w = synth.make_workload(2, device="cuda", T=16)
     note("repeat determinism")
