@@ -43,6 +43,7 @@ int hip_fail(hipError_t e, const char* what) {
 // each once, so a change applies to the forwards that start after it.
 std::atomic<int64_t> g_split_override{0};  // 0 = automatic
 std::atomic<int64_t> g_plan_override{0};   // 0 = automatic, 1 = never plan, 2 = always plan
+std::atomic<int64_t> g_persist_override{0};  // 0 = automatic, 1 = one unit per block always
 
 // Index reads use 32-bit byte offsets; the kernels read up to a few tiles past
 // a row's end, so leave headroom below 2^32 bytes.
@@ -356,6 +357,9 @@ int fwd_impl(const void* q, int64_t q_stride_t, int64_t q_stride_h, const KeySou
   }
   fp.sink = sink;
   fp.hg = smla::head_groups(H);
+  // with the plan (more units than CUs), kernels that can run several units
+  // per block get a persistent grid of one block per CU
+  fp.persist = (sort && g_persist_override.load(std::memory_order_relaxed) == 0) ? (device_cus(dev) / 8) * 8 : 0;
   if (v41) {
     fp.sink = nullptr;  // partials never hold the sink: the combine folds it in
     e = timed(1, [&](smla::Events ev) { return smla::launch_fwd41(fp, ev, s); });
@@ -534,6 +538,11 @@ int sparse_mla_set_option(const char* name, int64_t value) {
   if (!strcmp(name, "plan")) {
     if (value < 0 || value > 2) return fail(SMLA_EINVAL, "plan must be 0, 1 or 2");
     g_plan_override.store(value, std::memory_order_relaxed);
+    return SMLA_OK;
+  }
+  if (!strcmp(name, "persist")) {
+    if (value < 0 || value > 1) return fail(SMLA_EINVAL, "persist must be 0 or 1");
+    g_persist_override.store(value, std::memory_order_relaxed);
     return SMLA_OK;
   }
   if (!strcmp(name, "split")) {

@@ -171,12 +171,16 @@ __device__ __forceinline__ v4f half4_to_f32(v2i raw) {
 }
 
 // XCD-aware unit mapping: block b runs on XCD b % 8; rows of rank r go to XCD
-// r % 8 and the `per_row` blocks of a row are consecutive on that XCD.
-__device__ __forceinline__ void xcd_unit(int per_row, int& rank, int& sub) {
-  const int b = blockIdx.x;
+// r % 8 and the `per_row` blocks of a row are consecutive on that XCD.  A
+// persistent block maps the virtual blocks b it runs (b, b + grid, ..., with
+// the grid a multiple of 8, so all on its own XCD) the same way.
+__device__ __forceinline__ void xcd_unit_at(int b, int per_row, int& rank, int& sub) {
   const int i = b >> 3;
   rank = (b & 7) + 8 * (i / per_row);
   sub = i % per_row;
+}
+__device__ __forceinline__ void xcd_unit(int per_row, int& rank, int& sub) {
+  xcd_unit_at(blockIdx.x, per_row, rank, sub);
 }
 
 // Unit mapping of the split forward.  A row's keys in chunk order cover the

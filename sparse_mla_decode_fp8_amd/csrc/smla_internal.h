@@ -59,6 +59,8 @@ struct FwdParams {
   int32_t pool_shift[2];      // paged: log2 of the records per page
   const float* sink;          // nullable: per-head sink logit [H] (natural log); unsplit rows only
   int32_t hg;                 // head groups per row (units per row = S * hg)
+  int32_t persist;            // > 0: blocks of a persistent grid (a multiple of 8, one per CU), for
+                              // kernels that run several units per block; 0: one unit per block
 };
 
 struct CombineParams {

@@ -94,6 +94,9 @@ def test_options(b):
     for v in (1, 2, 0):
         assert b.lib().sparse_mla_set_option(b"plan", v) == 0
     assert b.lib().sparse_mla_set_option(b"plan", 3) == -1
+    for v in (1, 0):
+        assert b.lib().sparse_mla_set_option(b"persist", v) == 0
+    assert b.lib().sparse_mla_set_option(b"persist", 2) == -1
 
 
 def test_decode_rows_validation(b):

@@ -35,6 +35,7 @@ def smla():
     assert torch.cuda.is_available(), "GPU tests need a GPU"
     yield m
     m.set_option("split", 0)
+    m.set_option("persist", 0)
 
 
 def entries(w, entry_of):
@@ -152,6 +153,34 @@ def test_paged_uniform_rows(smla, H, split):
         smla.set_option("split", 0)
     ro, rl = run_oracle_paged(w, pools, ent, sink=sink)
     compare(o, l, ro, rl, label=f"paged_uniform_H{H}_S{split}")
+
+
+@pytest.mark.parametrize("H", [64, 128])
+def test_paged_persistent_grid(smla, H):
+    """Enough ragged rows that the kernel for more than 32 heads runs one
+    block per compute unit, each taking several units in turn, through both
+    pools with sinks (empty rows among them): bit-identical to one unit per
+    block, and the oracle's result on sampled rows."""
+    rng = np.random.default_rng(95 + H)
+    lens = rng.integers(0, 900, 400)
+    lens[::11] = 0
+    w = ragged_workload(f"paged_persist_H{H}", H, lens.tolist(), 12000, seed=96 + H, trailing=8)
+    pools, entry_of = paged_layout(rng, w.kv.numpy(), per_page=(16, 8), pad=(3 * 656 + 16, 0))
+    ent = entries(w, entry_of)
+    sink = sink_values(rng, H)
+    pools_d = to_dev(pools)
+    note(f"paged persistent grid H={H} T={w.T}")
+    o, l = run_paged(smla, w, pools_d, ent, sink=sink)
+    smla.set_option("persist", 1)
+    try:
+        o1, l1 = run_paged(smla, w, pools_d, ent, sink=sink)
+    finally:
+        smla.set_option("persist", 0)
+    assert torch.equal(o.view(torch.int16), o1.view(torch.int16))
+    assert torch.equal(l, l1)
+    rows = sorted(set(sample_rows(w.T, 8, seed=H).tolist()) | {0, 11, w.T - 1})
+    ro, rl = run_oracle_paged(w, pools, ent, sink=sink, rows=rows)
+    compare(o, l, ro, rl, rows=rows, label=f"paged_persist_H{H}")
 
 
 def test_paged_absent_pool(smla):

@@ -34,8 +34,10 @@ def smla():
 @pytest.fixture(autouse=True)
 def _reset_split(smla):
     smla.set_option("split", 0)
+    smla.set_option("persist", 0)
     yield
     smla.set_option("split", 0)
+    smla.set_option("persist", 0)
 
 
 def custom(name, H, N, slices, seed=11, device="cuda", **kw):
@@ -385,6 +387,35 @@ def test_ragged_causal_prefill_workload(smla):
     rows = sorted(set(sample_rows(w.T, 16, seed=6).tolist()) | {1, 31, 32, 33})
     ro, rl = run_oracle(w, rows=rows)
     compare(out, lse, ro, rl, rows=rows, label="ragged_causal_prefill")
+
+
+@pytest.mark.parametrize("H,split", [(64, 0), (128, 0), (40, 0), (64, 2)])
+def test_persistent_grid(smla, H, split):
+    """Ragged rows, many more units than compute units, so that the kernel for
+    more than 32 heads runs one block per compute unit, each block taking
+    several units in turn.  Empty rows and rows of every length sit between
+    long ones, so blocks pass from empty units to full ones and back.  The
+    result is bit-identical to one unit per block (each unit's arithmetic does
+    not depend on the block that runs it) and matches the oracle on sampled
+    rows, the empty ones among them."""
+    T, N = 700, 40000
+    rng = np.random.default_rng(20 + H + split)
+    lens = rng.integers(0, 1300, T)
+    lens[::9] = 0
+    lens[5::13] = 1
+    lens[7::31] = 2048
+    sl = [np.where(rng.random(L) < 0.03, -1, rng.integers(0, N, L)) for L in lens]
+    w = custom(f"persist_H{H}_S{split}", H, N, sl, seed=21, has_invalid=1)
+    note(f"persistent grid T={T} H={H} split={split}")
+    smla.set_option("split", split)
+    out, lse = run_gpu(w)
+    smla.set_option("persist", 1)
+    out1, lse1 = run_gpu(w)
+    assert torch.equal(out.view(torch.int16), out1.view(torch.int16))
+    assert torch.equal(lse, lse1)
+    rows = sorted(set(sample_rows(T, 10, seed=H).tolist()) | {0, 5, 7, 9, T - 1})
+    ro, rl = run_oracle(w, rows=rows)
+    compare(out, lse, ro, rl, rows=rows, label=f"persist_H{H}_S{split}")
 
 
 def test_repeat_calls_bitwise_identical(smla):
