@@ -418,7 +418,7 @@ def main() -> int:
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": read_traffic(cfg["name"]),
-            "kernel": _fwd_kernel_name(w.H),
+            "kernel": _fwd_kernel_name(w.H, w.T, _split_of(smla, w), kt.launches["plan"] > 0),
             "bytes_per_launch": gathered,
             "launch_ms": round(fwd_ms, 5),
         },
@@ -622,11 +622,18 @@ def bench_cache_write(args, torch, smla, dev) -> int:
     return 0
 
 
-def _fwd_kernel_name(H: int) -> str:
-    """The forward kernel the library launches for H heads."""
+def _fwd_kernel_name(H: int, T: int, S: int, planned: bool) -> str:
+    """The forward kernel the library launches for H heads (contiguous cache).
+    Above 32 heads, with the plan and more blocks than whole XCDs of compute
+    units, it is the persistent-grid instance."""
     if H <= 16:
         return "smla_fwd16_kernel"
-    return "smla_fwdw_kernel<2>" if H <= 32 else "smla_fwdw64_kernel<false>"
+    if H <= 32:
+        return "smla_fwdw_kernel<2>"
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    blocks = 8 * ((T + 7) // 8) * S * ((H + 63) // 64)
+    persistent = planned and blocks > (cus // 8) * 8
+    return f"smla_fwdw64_kernel<false, {'true' if persistent else 'false'}>"
 
 
 def _split_of(smla, w) -> int:
