@@ -125,7 +125,9 @@ int32_t sparse_mla_split_for(int32_t T, int32_t H, int64_t nnz, int32_t has_inva
  *     give unspecified rows).
  *
  * Returns SMLA_OK, or SMLA_EINVAL / SMLA_EUNSUPPORTED / SMLA_EWORKSPACE /
- * SMLA_EHIP with nothing queued.  Queues on `stream`: a plan when there are
+ * SMLA_EHIP with nothing queued (SMLA_EINVAL also when T is so large that a
+ * launch would need 2^31 or more blocks: T * max(S * head groups, H) rounded
+ * up, far beyond any q that fits in memory).  Queues on `stream`: a plan when there are
  * more (row, chunk, head group) units than compute units (a slice scan when has_invalid,
  * then a one-block longest-first sort of the rows; otherwise every unit
  * starts at once, rows run in their own order and each forward block scans

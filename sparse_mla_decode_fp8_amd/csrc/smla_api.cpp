@@ -4,12 +4,14 @@
 // path.
 
 #include <hip/hip_runtime.h>
+#include <limits.h>
 #include <math.h>
 #include <stdarg.h>
 #include <stdint.h>
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <atomic>
 #include <mutex>
 #include <string>
@@ -288,6 +290,10 @@ int fwd_impl(const void* q, int64_t q_stride_t, int64_t q_stride_h, const KeySou
   int dev = -1;
   hipError_t ez = stream_device(s, &dev);
   const Layout L = layout(T, H, nnz, v41 != nullptr, has_invalid != 0, ez == hipSuccess ? dev : -1);
+  // every grid of the call (forward units; the combine's one block per row
+  // and head) must fit a 32-bit launch dimension
+  if (8 * (((int64_t)T + 7) / 8) * std::max<int64_t>((int64_t)L.S * smla::head_groups(H), H) > INT32_MAX)
+    return fail(SMLA_EINVAL, "T = %d rows need more blocks than one launch holds", T);
   if (noalloc && (int64_t)L.total > SMLA_NOALLOC_SCRATCH_BYTES)
     return fail(SMLA_EWORKSPACE, "this forward needs %lld bytes of scratch; the static scratch holds %lld "
                 "(call sparse_mla_fwd with a workspace)", (long long)L.total, (long long)SMLA_NOALLOC_SCRATCH_BYTES);

@@ -76,6 +76,7 @@ def call(b, **over):
     (dict(ws=None), -1), (dict(indices=None), -1), (dict(q=FAKE + 8), -1),
     (dict(out=FAKE + 4), -1), (dict(kv=FAKE + 2), -1), (dict(ws=FAKE + 16), -1),
     (dict(qsh=577), -1), (dict(ost=-512), -1), (dict(wsb=100), -3),
+    (dict(T=(1 << 31) - 1), -1), (dict(T=1 << 24, H=128), -1),
 ])
 def test_host_validation(b, over, status):
     assert call(b, **over) == status
