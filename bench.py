@@ -630,6 +630,7 @@ def _fwd_kernel_name(H: int, T: int, S: int, planned: bool) -> str:
         return "smla_fwd16_kernel"
     if H <= 32:
         return "smla_fwdw_kernel<2>"
+    import torch
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     blocks = 8 * ((T + 7) // 8) * S * ((H + 63) // 64)
     persistent = planned and blocks > (cus // 8) * 8
