@@ -128,7 +128,7 @@ int choose_split(int32_t T, int32_t H, int64_t nnz, bool has_invalid, int dev) {
 
 struct Layout {
   int S;
-  size_t row_tiles, order, part_lse, part_o, total;
+  size_t row_tiles, order, desc, part_lse, part_o, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -145,6 +145,8 @@ Layout layout(int32_t T, int32_t H, int64_t nnz, bool partials, bool has_invalid
   off = align256(off + sizeof(int32_t) * (size_t)T);
   L.order = off;
   off = align256(off + sizeof(int32_t) * (size_t)T);
+  L.desc = off;
+  off = align256(off + 4 * sizeof(int32_t) * (size_t)T);
   L.part_lse = off;
   L.part_o = off;
   if (s_max > 1 || partials) {
@@ -311,6 +313,7 @@ int fwd_impl(const void* q, int64_t q_stride_t, int64_t q_stride_h, const KeySou
   uint8_t* ws = (uint8_t*)workspace;
   int32_t* row_tiles = (int32_t*)(ws + L.row_tiles);
   int32_t* order = (int32_t*)(ws + L.order);
+  int32_t* desc = (int32_t*)(ws + L.desc);
   const uint32_t idx_bytes = (uint32_t)(nnz * 4);
 
   // Longest-first order only pays when there are more units than CUs (one
@@ -325,7 +328,7 @@ int fwd_impl(const void* q, int64_t q_stride_t, int64_t q_stride_h, const KeySou
   hipError_t e = hipSuccess;
   if (sort) {
     smla::PlanParams pp{indptr, indices, idx_bytes, T, smla::tile_tokens(H), has_invalid ? 1 : 0,
-                        ks.km, row_tiles, order};
+                        ks.km, row_tiles, order, desc};
     e = timed(0, [&](smla::Events ev) { return smla::launch_plan(pp, sort, ev, s); });
     if (e != hipSuccess) return hip_fail(e, "plan kernel launch");
   }
@@ -353,6 +356,7 @@ int fwd_impl(const void* q, int64_t q_stride_t, int64_t q_stride_h, const KeySou
   // block start its index reads before indptr arrives
   fp.stride = (!sort && nnz % T == 0 && nnz / T > 0) ? (int32_t)(nnz / T) : 0;
   fp.order = sort ? order : nullptr;
+  fp.desc = sort ? desc : nullptr;
   fp.part_o = (uint16_t*)(ws + L.part_o);
   fp.part_lse = (float*)(ws + L.part_lse);
   fp.km = ks.km;

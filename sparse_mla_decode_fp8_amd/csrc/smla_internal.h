@@ -32,6 +32,7 @@ struct PlanParams {
   KeyMode km;
   int32_t* row_tiles;  // [T] out: tiles of each row
   int32_t* order;      // [T] out: rows, longest first
+  int32_t* desc;       // [T][4] out: slot r of the order as {row, slice start, length, tiles}
 };
 
 struct FwdParams {
@@ -51,6 +52,7 @@ struct FwdParams {
   int32_t scan;        // no plan and has_invalid: each block finds its row's last entry >= 0
   int32_t stride;      // > 0: no plan and every slice may start at row * stride (a guess the kernel checks)
   const int32_t* order;      // nullable: rows in their own order
+  const int32_t* desc;       // with order: {row, slice start, length, tiles} of each rank (one load)
   uint16_t* part_o;    // f16 bits [T*S, H, 512] when S > 1 (dims permuted in 64-dim blocks: part_dim)
   float* part_lse;     // [T*S, H]  (log2 units) when S > 1
   KeyMode km;

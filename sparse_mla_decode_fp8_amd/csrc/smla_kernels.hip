@@ -95,7 +95,9 @@ __device__ __forceinline__ int wave_bucket_add(int* cnt, int b, bool active) {
 
 // One block: tile counts of every row (from the scan, or from indptr) and a
 // counting sort of the rows by tile count, longest first (the FlyDSL page
-// issues long rows first so the long tail starts early).
+// issues long rows first so the long tail starts early).  Each slot of the
+// order also gets its row's {row, slice start, length, tiles}, so that a
+// forward block finds its unit with one load instead of two in a row.
 // (the row tiles, indptr, T and has_invalid are preloaded leading arguments)
 __global__ __launch_bounds__(1024) void smla_plan_sort_kernel(
     int32_t* __restrict__ row_tiles, const int32_t* __restrict__ indptr, int32_t T, int32_t has_invalid,
@@ -145,8 +147,14 @@ __global__ __launch_bounds__(1024) void smla_plan_sort_kernel(
   for (int r0 = 0; r0 < T; r0 += blockDim.x) {
     const int r = r0 + tid;
     const int t = r < T ? row_tiles[r] : 0;
+    const int beg = r < T ? indptr[r] : 0;
+    const int end = r < T ? indptr[r + 1] : 0;
     const int slot = wave_bucket_add(s_cnt, min(t, kPlanBuckets - 1), r < T);
-    if (r < T) p.order[slot] = r;
+    if (r < T) {
+      p.order[slot] = r;
+      // the forward blocks take their unit in one load
+      *(v4i*)(p.desc + 4 * slot) = v4i{r, beg, max(end - beg, 0), t};
+    }
   }
 }
 
@@ -225,7 +233,7 @@ __device__ __forceinline__ void pin(Side& s) { asm volatile("" : "+v"(s.ksc), "+
 // real start if the guess was wrong.
 __global__ __launch_bounds__(n16::kThreads, 1) void smla_fwd16_kernel(
     const int32_t* __restrict__ indptr, const int32_t* __restrict__ indices, const uint16_t* __restrict__ qbase,
-    const int32_t* __restrict__ order, int32_t T, int32_t S, uint32_t idx_bytes, int32_t stride, FwdParams p) {
+    const int32_t* __restrict__ desc, int32_t T, int32_t S, uint32_t idx_bytes, int32_t stride, FwdParams p) {
   using namespace n16;
   __shared__ __attribute__((aligned(1024))) uint8_t s_lds[kBytes];
 
@@ -236,7 +244,7 @@ __global__ __launch_bounds__(n16::kThreads, 1) void smla_fwd16_kernel(
   const int g = lane >> 4;
 
   int rank, chunk;
-  fwd_unit(S, order == nullptr, rank, chunk);
+  fwd_unit(S, desc == nullptr, rank, chunk);
   if (rank >= T) return;
 
   const uint32_t base = lds_addr(s_lds);
@@ -259,10 +267,19 @@ __global__ __launch_bounds__(n16::kThreads, 1) void smla_fwd16_kernel(
     issue_idx_at(beg_g, t0_g + 2);
   }
 
-  const int row = order ? order[rank] : rank;
-  const int beg = indptr[row];
-  const int len = max(indptr[row + 1] - beg, 0);
-  const int tiles = unit_tiles<kThreads>(p, row, beg, len, kTile, (int*)(s_lds + kMxOff));
+  int row, beg, len, tiles;
+  if (desc) {  // with the plan, the unit of rank `rank` in one load
+    const v4i ud = *(const v4i*)(desc + 4 * rank);
+    row = ud.x;
+    beg = ud.y;
+    len = ud.z;
+    tiles = ud.w;
+  } else {
+    row = rank;
+    beg = indptr[row];
+    len = max(indptr[row + 1] - beg, 0);
+    tiles = unit_tiles<kThreads>(p, row, beg, len, kTile, (int*)(s_lds + kMxOff));
+  }
   const int ct = (tiles + S - 1) / S;
   const int t0 = min(chunk * ct, tiles);
   const int t1 = min(t0 + ct, tiles);
@@ -825,7 +842,7 @@ hipError_t launch_fwd(const FwdParams& p, Events ev, hipStream_t s) {
     case 1: {
       const int64_t blocks = fwd_grid(p.T, p.S, p.order == nullptr);
       hipExtLaunchKernelGGL(smla_fwd16_kernel, dim3((unsigned)blocks), dim3(n16::kThreads), 0, s,
-                            ev.start, ev.stop, 0, p.indptr, p.indices, p.q, p.order, p.T, p.S, p.idx_bytes, p.stride, p);
+                            ev.start, ev.stop, 0, p.indptr, p.indices, p.q, p.desc, p.T, p.S, p.idx_bytes, p.stride, p);
       return hipGetLastError();
     }
     default: return launch_fwd_wide(p, ev, s);

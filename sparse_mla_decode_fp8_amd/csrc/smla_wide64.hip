@@ -115,7 +115,7 @@ __device__ __forceinline__ uint32_t row_off(int tau) { return (tau >> 1) * kPair
 // grid would use.  At a unit's last steps the score waves
 // load their q of the next unit and the P.V waves queue its first index tiles,
 // so the next unit starts with both at hand.  It runs with the plan
-// only (tile counts from row_tiles).
+// only (units from the plan's descriptors).
 template <bool PAGED, bool MULTI>
 __global__ __launch_bounds__(w64::kThreads, 1) void smla_fwdw64_kernel(FwdParams p) {
   using namespace w64;
@@ -178,14 +178,23 @@ __global__ __launch_bounds__(w64::kThreads, 1) void smla_fwdw64_kernel(FwdParams
   auto unit_at = [&](int r, int sb, Unit& uu) {
     const KArgs ka = args();
     const int S = SMLA_ARG(ka, S);
-    const int32_t* const order = SMLA_ARG(ka, order);
+    const int32_t* const desc = SMLA_ARG(ka, desc);
     const int32_t* const indptr = SMLA_ARG(ka, indptr);
     uu.chunk = sb % S;
     uu.h0 = kHeads * (sb / S);  // first head of the unit's head group
-    uu.row = order ? order[r] : r;
-    uu.beg = indptr[uu.row];
-    uu.len = max(indptr[uu.row + 1] - uu.beg, 0);
-    const int tiles = MULTI ? ka->row_tiles[uu.row] : unit_tiles<kThreads>(p, uu.row, uu.beg, uu.len, kTile, (int*)(s_lds + kRedOff));
+    int tiles;
+    if (MULTI || desc) {  // the plan's unit of rank r in one load
+      const v4i d = *(const v4i*)(desc + 4 * r);
+      uu.row = d.x;
+      uu.beg = d.y;
+      uu.len = d.z;
+      tiles = d.w;
+    } else {
+      uu.row = r;
+      uu.beg = indptr[r];
+      uu.len = max(indptr[r + 1] - uu.beg, 0);
+      tiles = unit_tiles<kThreads>(p, r, uu.beg, uu.len, kTile, (int*)(s_lds + kRedOff));
+    }
     const int ct = (tiles + S - 1) / S;
     uu.t0 = min(uu.chunk * ct, tiles);
     uu.t1 = min(uu.t0 + ct, tiles);
@@ -772,7 +781,7 @@ __global__ __launch_bounds__(w64::kThreads, 1) void smla_fwdw64_kernel(FwdParams
 // one per CU), the persistent kernel; otherwise one unit per block.
 hipError_t launch_fwd_wide64(const FwdParams& p, Events ev, hipStream_t s) {
   const int64_t blocks = xcd_grid(p.T, p.S * p.hg);
-  const bool multi = p.persist > 0 && p.row_tiles != nullptr && blocks > p.persist;
+  const bool multi = p.persist > 0 && p.desc != nullptr && blocks > p.persist;
   const dim3 grid((unsigned)(multi ? p.persist : blocks));
   auto go = [&](auto kernel) {
     hipExtLaunchKernelGGL(kernel, grid, dim3(w64::kThreads), 0, s, ev.start, ev.stop, 0, p);
