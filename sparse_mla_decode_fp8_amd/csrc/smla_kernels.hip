@@ -231,6 +231,15 @@ __device__ __forceinline__ void pin(Side& s) { asm volatile("" : "+v"(s.ksc), "+
 // evenly: each block then guesses its slice start (rank * stride) and queues
 // its first index tiles before indptr arrives, and queues them again from the
 // real start if the guess was wrong.
+// MULTI (with the plan only): a persistent grid of a multiple of 8 blocks, at
+// most one per CU.  In round k block b runs the unit of virtual block
+// k * grid + b of the one-unit-per-block grid, or in odd rounds that of b
+// mirrored among its XCD's blocks, so that in the longest-first order a
+// block's units pair long with short, each on the XCD the plain grid would
+// use.  A unit loads the next one's descriptor after its own first loads and
+// queues the next one's first index tiles after its last tile, so the next
+// unit starts with both at hand.
+template <bool MULTI>
 __global__ __launch_bounds__(n16::kThreads, 1) void smla_fwd16_kernel(
     const int32_t* __restrict__ indptr, const int32_t* __restrict__ indices, const uint16_t* __restrict__ qbase,
     const int32_t* __restrict__ desc, int32_t T, int32_t S, uint32_t idx_bytes, int32_t stride, FwdParams p) {
@@ -243,9 +252,47 @@ __global__ __launch_bounds__(n16::kThreads, 1) void smla_fwd16_kernel(
   const int t = lane & 15;
   const int g = lane >> 4;
 
+  // (persistent) the parameter block read at a unit's start and end comes
+  // through a pointer the compiler cannot see through (the kernel arguments in
+  // their segment: the leading scalars, then the block at its natural
+  // alignment), so its fields are loaded where they are used instead of being
+  // held in registers through every unit's tiles
+  struct KArgs {
+    const int32_t* indptr;
+    const int32_t* indices;
+    const uint16_t* qbase;
+    const int32_t* desc;
+    int32_t T, S;
+    uint32_t idx_bytes;
+    int32_t stride;
+    FwdParams p;
+  };
+  static_assert(offsetof(KArgs, p) == 48, "the parameter block follows the 48 bytes of leading arguments");
+  typedef const __attribute__((address_space(4))) KArgs* KArgsP;
+  auto pa = [&]() -> const __attribute__((address_space(4))) FwdParams* {
+    KArgsP a = (KArgsP)__builtin_amdgcn_kernarg_segment_ptr();
+    asm volatile("" : "+s"(a));
+    return &a->p;
+  };
+#define SMLA_P(f) (MULTI ? pa()->f : p.f)
+
   int rank, chunk;
   fwd_unit(S, desc == nullptr, rank, chunk);
-  if (rank >= T) return;
+  // (persistent) the block's first unit after round kr that holds a row
+  int kr = 0;
+  auto next_rank = [&](int& r, int& c) -> bool {
+    const int G = (int)gridDim.x, b = (int)blockIdx.x;
+    const int mirror = (b & 7) + 8 * (G / 8 - 1 - (b >> 3));
+    const int nvb = 8 * ((T + 7) / 8) * S;
+    for (++kr; kr * G < nvb; ++kr) {
+      const int v = kr * G + ((kr & 1) ? mirror : b);
+      if (v >= nvb) continue;
+      xcd_unit_at(v, S, r, c);
+      if (r < T) return true;
+    }
+    return false;
+  };
+  if (rank >= T && !(MULTI && next_rank(rank, chunk))) return;
 
   const uint32_t base = lds_addr(s_lds);
   const __amdgpu_buffer_rsrc_t irs = idx_rsrc(indices, idx_bytes);
@@ -267,8 +314,25 @@ __global__ __launch_bounds__(n16::kThreads, 1) void smla_fwd16_kernel(
     issue_idx_at(beg_g, t0_g + 2);
   }
 
+  // (persistent) the next unit, and its descriptor (lane i holds field i & 3;
+  // an ordinary load, whose wait the compiler places); have_ud: this unit's
+  // descriptor came from the unit before; pref: so did its first index tiles
+  int rank_n = 0, chunk_n = 0;
+  bool have_ud = false, pref = false;
+  int ud_n = 0;
+  for (;;) {
+  // (persistent) lane-derived values are formed anew in each unit, from an
+  // opaque copy of the lane index, instead of being held across units
+  int lane_u = lane;
+  if (MULTI) asm volatile("" : "+v"(lane_u));
+  const int lane = lane_u, t = lane & 15, g = lane >> 4;
   int row, beg, len, tiles;
-  if (desc) {  // with the plan, the unit of rank `rank` in one load
+  if (MULTI && have_ud) {
+    row = __builtin_amdgcn_readlane(ud_n, 0);
+    beg = __builtin_amdgcn_readlane(ud_n, 1);
+    len = __builtin_amdgcn_readlane(ud_n, 2);
+    tiles = __builtin_amdgcn_readlane(ud_n, 3);
+  } else if (desc) {  // with the plan, the unit of rank `rank` in one load
     const v4i ud = *(const v4i*)(desc + 4 * rank);
     row = ud.x;
     beg = ud.y;
@@ -285,24 +349,33 @@ __global__ __launch_bounds__(n16::kThreads, 1) void smla_fwd16_kernel(
   const int t1 = min(t0 + ct, tiles);
   const int unit = row * S + chunk;
   const bool split = S > 1;
-  const int H = p.H;
+  const int H = SMLA_P(H);
   const int h = t;  // head of this lane in QK (C column) and PV (B column)
   const bool h_ok = h < H;
+  const bool has_n = MULTI && next_rank(rank_n, chunk_n);
 
   if (t0 >= t1) {  // nothing to attend: zero output and the sink's lse, or an empty partial
-    if (stride > 0) wait_vm_all();  // the speculative index DMA must land before the block ends
+    if (stride > 0 || pref) wait_vm_all();  // the speculative or queued index DMAs land before the block ends
     if (split) {
-      for (int hh = tid; hh < H; hh += kThreads) p.part_lse[(int64_t)unit * H + hh] = -INFINITY;
+      for (int hh = tid; hh < H; hh += kThreads) SMLA_P(part_lse)[(int64_t)unit * H + hh] = -INFINITY;
     } else {
       for (int e = tid; e < H * (kLat / 8); e += kThreads) {
         const int hh = e / (kLat / 8), d = (e % (kLat / 8)) * 8;
-        *(v4i*)(p.out + row * p.o_st + hh * p.o_sh + d) = v4i{0, 0, 0, 0};
+        *(v4i*)(SMLA_P(out) + row * SMLA_P(o_st) + hh * SMLA_P(o_sh) + d) = v4i{0, 0, 0, 0};
       }
-      if (p.lse)  // a row with no key: lse is the sink (-inf without one)
+      float* const lse_o = SMLA_P(lse);
+      const float* const sink_o = SMLA_P(sink);
+      if (lse_o)  // a row with no key: lse is the sink (-inf without one)
         for (int hh = tid; hh < H; hh += kThreads)
-          p.lse[(int64_t)row * H + hh] = p.sink ? p.sink[hh] : -INFINITY;
+          lse_o[(int64_t)row * H + hh] = sink_o ? sink_o[hh] : -INFINITY;
     }
-    return;
+    if (!has_n) return;
+    ud_n = desc[4 * rank_n + (lane & 3)];
+    rank = rank_n;
+    chunk = chunk_n;
+    have_ud = true;
+    pref = false;
+    continue;
   }
 
   const uint8_t* const kv = p.kv;
@@ -377,7 +450,7 @@ __global__ __launch_bounds__(n16::kThreads, 1) void smla_fwd16_kernel(
   //   ... S(n) | I(n+3) | L(n+1) S(n+1) | I(n+4) ...
   // (L latent DMA, S side loads, I index DMA of a tile).
   // index tiles t0 .. t0+2, unless the speculative ones are those
-  if (!(stride > 0 && beg == beg_g && t0 == t0_g)) {
+  if (!pref && !(stride > 0 && beg == beg_g && t0 == t0_g)) {
     if (stride > 0) wait_vm_all();  // the guessed tiles land before the ring is refilled
     issue_idx(t0);
     issue_idx(t0 + 1);
@@ -388,12 +461,12 @@ __global__ __launch_bounds__(n16::kThreads, 1) void smla_fwd16_kernel(
   // use zeros).  nq: q DMA instructions this wave issues.
   const int nq = 2 * ((2 * w < H) + (2 * w + 1 < H));
   {
-    const uint16_t* qrow = qbase + row * p.q_st;
+    const uint16_t* qrow = qbase + row * SMLA_P(q_st);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int hh = 2 * w + j;
       if (hh < H) {
-        const uint16_t* qh = qrow + (int64_t)hh * p.q_sh;
+        const uint16_t* qh = qrow + (int64_t)hh * SMLA_P(q_sh);
         const uint32_t dst = base + kQOff + kQRow * hh;
         dma16((const uint8_t*)(qh + 8 * lane), __builtin_amdgcn_readfirstlane(dst));
         if (lane < 8) dma16((const uint8_t*)(qh + 8 * (64 + lane)), __builtin_amdgcn_readfirstlane(dst + 1024));
@@ -418,6 +491,8 @@ __global__ __launch_bounds__(n16::kThreads, 1) void smla_fwd16_kernel(
     wait_vm<kTileVm>();
   }
   __syncthreads();  // every wave's q chunks have landed
+  // (persistent) the next unit's descriptor, behind this unit's first loads
+  if (MULTI && has_n) ud_n = desc[4 * rank_n + (lane & 3)];
   // q as bf16 B operands (head = lane column t).  Latent K-step 2m / 2m+1: dims
   // 64m + 16g + [0..7] / [8..15]; rope K-step i: dims 512 + 32i + 8g + [0..7].
   v8bf qlat[16];
@@ -473,8 +548,14 @@ __global__ __launch_bounds__(n16::kThreads, 1) void smla_fwd16_kernel(
     // arrive as early as they can; tile t0+1 follows as soon as they have.
     const int left = t1 - n;  // tiles left, this one included
     if (n == t0) {
-      if (left >= 4) wait_vm<1>();
-      else wait_vm<0>();
+      // (after I(t0+3) if queued, and the next unit's descriptor if loaded)
+      if (MULTI && has_n) {
+        if (left >= 4) wait_vm<2>();
+        else wait_vm<1>();
+      } else {
+        if (left >= 4) wait_vm<1>();
+        else wait_vm<0>();
+      }
       if (left >= 2) {
         issue_latent(n + 1, st ^ 1);
         load_side(n + 1, sB);
@@ -620,20 +701,39 @@ __global__ __launch_bounds__(n16::kThreads, 1) void smla_fwd16_kernel(
     tile(n, 0, sA);
     if (n + 1 < t1) tile(n + 1, 1, sB);
   }
-  wait_vm_all();  // no DMA may still target LDS when the block ends
+  bool pref_n = false;
+  if (MULTI && has_n) {
+    // every load of this unit and the next unit's descriptor have landed (the
+    // last tile waited for all of them): queue the next unit's first index
+    // tiles, which land during this unit's epilogue
+    wait_vm_all();
+    const int beg_n = __builtin_amdgcn_readlane(ud_n, 1);
+    const int tiles_n = __builtin_amdgcn_readlane(ud_n, 3);
+    const int ct_n = (tiles_n + S - 1) / S;
+    const int t0_n = min(chunk_n * ct_n, tiles_n);
+    pref_n = t0_n < min(t0_n + ct_n, tiles_n);
+    if (pref_n) {
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // this unit's reads of the ring are done before it is refilled
+      issue_idx_at(beg_n, t0_n);
+      issue_idx_at(beg_n, t0_n + 1);
+      issue_idx_at(beg_n, t0_n + 2);
+    }
+  } else {
+    wait_vm_all();  // no DMA may still target LDS when the block ends
+  }
 
   // ---- epilogue: head t's sum over all tokens, then this wave's 64 dims
   // (split: a partial without the sink, which the combine folds in)
   l_run = xor_sum(l_run);
-  const Norm nm = finish_norm(l_run, m_ref, (split || !h_ok) ? -INFINITY : sink_log2(p.sink, h));
+  const Norm nm = finish_norm(l_run, m_ref, (split || !h_ok) ? -INFINITY : sink_log2(SMLA_P(sink), h));
   const float inv = nm.scale;
   const float l2 = nm.lse2;
   if (w == 0 && g == 0 && h_ok) {
-    if (split) p.part_lse[(int64_t)unit * H + h] = l2;
-    else if (p.lse) p.lse[(int64_t)row * H + h] = l2 * kLn2;
+    if (split) SMLA_P(part_lse)[(int64_t)unit * H + h] = l2;
+    else if (SMLA_P(lse)) SMLA_P(lse)[(int64_t)row * H + h] = l2 * kLn2;
   }
   if (split) {
-    if (h_ok) st_part16(p.part_o + ((int64_t)unit * H + h) * kLat + 64 * w, g, O, inv);
+    if (h_ok) st_part16(SMLA_P(part_o) + ((int64_t)unit * H + h) * kLat + 64 * w, g, O, inv);
   } else {
     // bf16 rows staged in this wave's part of the q area (idle after the
     // prologue), then read back 8 lanes per head, so that each store
@@ -647,9 +747,19 @@ __global__ __launch_bounds__(n16::kThreads, 1) void smla_fwd16_kernel(
     for (int i = 0; i < 2; ++i) {
       const int hh = 8 * i + (lane >> 3);
       const v4i v = *LDSP(v4i, ob + kOutPitch * hh + 16 * (lane & 7));
-      if (hh < H) *(v4i*)(p.out + row * p.o_st + hh * p.o_sh + 64 * w + 8 * (lane & 7)) = v;
+      if (hh < H) *(v4i*)(SMLA_P(out) + row * SMLA_P(o_st) + hh * SMLA_P(o_sh) + 64 * w + 8 * (lane & 7)) = v;
     }
   }
+  if (!MULTI || !has_n) return;
+  // every wave is past this unit (its stages, P buffers and the q area) before
+  // the next unit's loads land there
+  __syncthreads();
+  rank = rank_n;
+  chunk = chunk_n;
+  have_ud = true;
+  pref = pref_n;
+  }  // units
+#undef SMLA_P
 }
 
 // ---------------------------------------------------------------- combine
@@ -841,8 +951,14 @@ hipError_t launch_fwd(const FwdParams& p, Events ev, hipStream_t s) {
   switch (head_tiles(p.H)) {
     case 1: {
       const int64_t blocks = fwd_grid(p.T, p.S, p.order == nullptr);
-      hipExtLaunchKernelGGL(smla_fwd16_kernel, dim3((unsigned)blocks), dim3(n16::kThreads), 0, s,
-                            ev.start, ev.stop, 0, p.indptr, p.indices, p.q, p.desc, p.T, p.S, p.idx_bytes, p.stride, p);
+      // with the plan and more units than the persistent grid (p.persist
+      // blocks, one per CU), the persistent kernel; otherwise one unit per block
+      if (p.persist > 0 && p.desc != nullptr && blocks > p.persist)
+        hipExtLaunchKernelGGL(smla_fwd16_kernel<true>, dim3((unsigned)p.persist), dim3(n16::kThreads), 0, s,
+                              ev.start, ev.stop, 0, p.indptr, p.indices, p.q, p.desc, p.T, p.S, p.idx_bytes, p.stride, p);
+      else
+        hipExtLaunchKernelGGL(smla_fwd16_kernel<false>, dim3((unsigned)blocks), dim3(n16::kThreads), 0, s,
+                              ev.start, ev.stop, 0, p.indptr, p.indices, p.q, p.desc, p.T, p.S, p.idx_bytes, p.stride, p);
       return hipGetLastError();
     }
     default: return launch_fwd_wide(p, ev, s);

@@ -155,9 +155,9 @@ def test_paged_uniform_rows(smla, H, split):
     compare(o, l, ro, rl, label=f"paged_uniform_H{H}_S{split}")
 
 
-@pytest.mark.parametrize("H", [64, 128])
+@pytest.mark.parametrize("H", [16, 64, 128])
 def test_paged_persistent_grid(smla, H):
-    """Enough ragged rows that the kernel for more than 32 heads runs one
+    """Enough ragged rows that the 16-head and wide-head kernels run one
     block per compute unit, each taking several units in turn, through both
     pools with sinks (empty rows among them): bit-identical to one unit per
     block, and the oracle's result on sampled rows."""

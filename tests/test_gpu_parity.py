@@ -389,10 +389,10 @@ def test_ragged_causal_prefill_workload(smla):
     compare(out, lse, ro, rl, rows=rows, label="ragged_causal_prefill")
 
 
-@pytest.mark.parametrize("H,split", [(64, 0), (128, 0), (40, 0), (64, 2)])
+@pytest.mark.parametrize("H,split", [(64, 0), (128, 0), (40, 0), (64, 2), (16, 0), (16, 2), (5, 3)])
 def test_persistent_grid(smla, H, split):
-    """Ragged rows, many more units than compute units, so that the kernel for
-    more than 32 heads runs one block per compute unit, each block taking
+    """Ragged rows, many more units than compute units, so that the 16-head and
+    wide-head kernels run one block per compute unit, each block taking
     several units in turn.  Empty rows and rows of every length sit between
     long ones, so blocks pass from empty units to full ones and back.  The
     result is bit-identical to one unit per block (each unit's arithmetic does
