@@ -65,8 +65,8 @@ int sparse_mla_supported(int32_t num_heads, int32_t head_dim_qk, int32_t dv);
 /*
  * sparse_mla_workspace_bytes -- device workspace a forward of T query rows,
  * H heads and nnz CSR entries needs on the current device (per-row tile
- * counts, the longest-first row order and, when rows are split, chunk
- * partials).  Returns the byte count, or a negative smla_status for invalid
+ * counts, the longest-first row order with each slot's unit descriptor and,
+ * when rows are split, chunk partials).  Returns the byte count, or a negative smla_status for invalid
  * arguments; the size covers either has_invalid.  The workspace needs no
  * initialisation; it must not be shared by forwards that may run concurrently.
  */
