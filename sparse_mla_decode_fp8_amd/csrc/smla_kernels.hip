@@ -321,443 +321,443 @@ __global__ __launch_bounds__(n16::kThreads, 1) void smla_fwd16_kernel(
   bool have_ud = false, pref = false;
   int ud_n = 0;
   for (;;) {
-  // (persistent) lane-derived values are formed anew in each unit, from an
-  // opaque copy of the lane index, instead of being held across units
-  int lane_u = lane;
-  if (MULTI) asm volatile("" : "+v"(lane_u));
-  const int lane = lane_u, t = lane & 15, g = lane >> 4;
-  int row, beg, len, tiles;
-  if (MULTI && have_ud) {
-    row = __builtin_amdgcn_readlane(ud_n, 0);
-    beg = __builtin_amdgcn_readlane(ud_n, 1);
-    len = __builtin_amdgcn_readlane(ud_n, 2);
-    tiles = __builtin_amdgcn_readlane(ud_n, 3);
-  } else if (desc) {  // with the plan, the unit of rank `rank` in one load
-    const v4i ud = *(const v4i*)(desc + 4 * rank);
-    row = ud.x;
-    beg = ud.y;
-    len = ud.z;
-    tiles = ud.w;
-  } else {
-    row = rank;
-    beg = indptr[row];
-    len = max(indptr[row + 1] - beg, 0);
-    tiles = unit_tiles<kThreads>(p, row, beg, len, kTile, (int*)(s_lds + kMxOff));
-  }
-  const int ct = (tiles + S - 1) / S;
-  const int t0 = min(chunk * ct, tiles);
-  const int t1 = min(t0 + ct, tiles);
-  const int unit = row * S + chunk;
-  const bool split = S > 1;
-  const int H = SMLA_P(H);
-  const int h = t;  // head of this lane in QK (C column) and PV (B column)
-  const bool h_ok = h < H;
-  const bool has_n = MULTI && next_rank(rank_n, chunk_n);
-
-  if (t0 >= t1) {  // nothing to attend: zero output and the sink's lse, or an empty partial
-    if (stride > 0 || pref) wait_vm_all();  // the speculative or queued index DMAs land before the block ends
-    if (split) {
-      for (int hh = tid; hh < H; hh += kThreads) SMLA_P(part_lse)[(int64_t)unit * H + hh] = -INFINITY;
+    // (persistent) lane-derived values are formed anew in each unit, from an
+    // opaque copy of the lane index, instead of being held across units
+    int lane_u = lane;
+    if (MULTI) asm volatile("" : "+v"(lane_u));
+    const int lane = lane_u, t = lane & 15, g = lane >> 4;
+    int row, beg, len, tiles;
+    if (MULTI && have_ud) {
+      row = __builtin_amdgcn_readlane(ud_n, 0);
+      beg = __builtin_amdgcn_readlane(ud_n, 1);
+      len = __builtin_amdgcn_readlane(ud_n, 2);
+      tiles = __builtin_amdgcn_readlane(ud_n, 3);
+    } else if (desc) {  // with the plan, the unit of rank `rank` in one load
+      const v4i ud = *(const v4i*)(desc + 4 * rank);
+      row = ud.x;
+      beg = ud.y;
+      len = ud.z;
+      tiles = ud.w;
     } else {
-      for (int e = tid; e < H * (kLat / 8); e += kThreads) {
-        const int hh = e / (kLat / 8), d = (e % (kLat / 8)) * 8;
-        *(v4i*)(SMLA_P(out) + row * SMLA_P(o_st) + hh * SMLA_P(o_sh) + d) = v4i{0, 0, 0, 0};
-      }
-      float* const lse_o = SMLA_P(lse);
-      const float* const sink_o = SMLA_P(sink);
-      if (lse_o)  // a row with no key: lse is the sink (-inf without one)
-        for (int hh = tid; hh < H; hh += kThreads)
-          lse_o[(int64_t)row * H + hh] = sink_o ? sink_o[hh] : -INFINITY;
+      row = rank;
+      beg = indptr[row];
+      len = max(indptr[row + 1] - beg, 0);
+      tiles = unit_tiles<kThreads>(p, row, beg, len, kTile, (int*)(s_lds + kMxOff));
     }
-    if (!has_n) return;
-    ud_n = desc[4 * rank_n + (lane & 3)];
+    const int ct = (tiles + S - 1) / S;
+    const int t0 = min(chunk * ct, tiles);
+    const int t1 = min(t0 + ct, tiles);
+    const int unit = row * S + chunk;
+    const bool split = S > 1;
+    const int H = SMLA_P(H);
+    const int h = t;  // head of this lane in QK (C column) and PV (B column)
+    const bool h_ok = h < H;
+    const bool has_n = MULTI && next_rank(rank_n, chunk_n);
+
+    if (t0 >= t1) {  // nothing to attend: zero output and the sink's lse, or an empty partial
+      if (stride > 0 || pref) wait_vm_all();  // the speculative or queued index DMAs land before the block ends
+      if (split) {
+        for (int hh = tid; hh < H; hh += kThreads) SMLA_P(part_lse)[(int64_t)unit * H + hh] = -INFINITY;
+      } else {
+        for (int e = tid; e < H * (kLat / 8); e += kThreads) {
+          const int hh = e / (kLat / 8), d = (e % (kLat / 8)) * 8;
+          *(v4i*)(SMLA_P(out) + row * SMLA_P(o_st) + hh * SMLA_P(o_sh) + d) = v4i{0, 0, 0, 0};
+        }
+        float* const lse_o = SMLA_P(lse);
+        const float* const sink_o = SMLA_P(sink);
+        if (lse_o)  // a row with no key: lse is the sink (-inf without one)
+          for (int hh = tid; hh < H; hh += kThreads)
+            lse_o[(int64_t)row * H + hh] = sink_o ? sink_o[hh] : -INFINITY;
+      }
+      if (!has_n) return;
+      ud_n = desc[4 * rank_n + (lane & 3)];
+      rank = rank_n;
+      chunk = chunk_n;
+      have_ud = true;
+      pref = false;
+      continue;
+    }
+
+    const uint8_t* const kv = p.kv;
+    const uint8_t* const zero = p.zero;
+    auto lat_at = [&](int st) -> uint32_t { return base + kLatOff + st * kLatStage; };
+    auto tab_at = [&](int n) -> uint32_t { return base + kTabOff + (n & 1) * kTile * 8; };
+    // Every wave touches only its own 16 entries of the index ring and the
+    // address table, so those need no barrier.
+    auto issue_idx = [&](int n) { issue_idx_at(beg, n); };
+    // record addresses of this wave's tokens of tile n (masked ones: the zero
+    // record); returns the wave's valid-token mask
+    auto fill_table = [&](int n) -> uint32_t {
+      int ix = -1;
+      if (lane < 16) {
+        const int raw = *LDSP(int, ring_at(n) + 4 * (16 * w + lane));
+        ix = (n * kTile + 16 * w + lane < len) ? raw : -1;
+        *LDSP(uint64_t, tab_at(n) + 8 * (16 * w + lane)) =
+            (uint64_t)(uintptr_t)(p.km.valid(ix) ? key_addr(p, ix) : zero);
+      }
+      return (uint32_t)__ballot(lane < 16 && p.km.valid(ix)) & 0xFFFFu;
+    };
+    // latent DMA of this wave's 16 tokens of tile n into stage st: one
+    // instruction per token pair, lanes 0..31 the even token, 32..63 the odd one
+    // (lane position p of the odd row loads chunk p ^ 8).
+    const uint32_t src_chunk = 16u * (uint32_t)((lane & 31) ^ ((lane >> 5) << 3));
+    auto issue_latent = [&](int n, int st) {
+      const uint32_t tab = tab_at(n) + 8 * (16 * w + (lane >> 5));
+      uint64_t a[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) a[i] = *LDSP(uint64_t, tab + 16 * i);
+      const uint32_t dst = lat_at(st) + 8 * w * kPair;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        dma16((const uint8_t*)(uintptr_t)(a[i] + src_chunk), __builtin_amdgcn_readfirstlane(dst + i * kPair));
+    };
+    auto load_side = [&](int n, Side& s) {
+      const uint64_t rec = *LDSP(uint64_t, tab_at(n) + 8 * (16 * w + t));
+      gload16(s.ksc, rec + kScaleOff);
+      gload16(s.rp0, rec + kRopeOff + 16 * g);
+      gload16(s.rp1, rec + kRopeOff + 64 + 16 * g);
+    };
+    // Tile n's loads with every address already in registers: fill_table(n)
+    // and the table reads run while an earlier tile is processed, so that the
+    // refill after a tile only issues loads.
+    struct Next {
+      uint64_t lat[8];  // latent DMA source rows (issue_latent's a[])
+      uint64_t rec;     // the side loads' record (load_side's rec)
+      uint32_t vmask;
+    };
+    auto prep = [&](int n, Next& nx) {
+      nx.vmask = fill_table(n);
+      const uint32_t tab = tab_at(n) + 8 * (16 * w + (lane >> 5));
+#pragma unroll
+      for (int i = 0; i < 8; ++i) nx.lat[i] = *LDSP(uint64_t, tab + 16 * i);
+      nx.rec = *LDSP(uint64_t, tab_at(n) + 8 * (16 * w + t));
+    };
+    auto issue_next = [&](const Next& nx, int st, Side& s) {
+      const uint32_t dst = lat_at(st) + 8 * w * kPair;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        dma16((const uint8_t*)(uintptr_t)(nx.lat[i] + src_chunk), __builtin_amdgcn_readfirstlane(dst + i * kPair));
+      gload16(s.ksc, nx.rec + kScaleOff);
+      gload16(s.rp0, nx.rec + kRopeOff + 16 * g);
+      gload16(s.rp1, nx.rec + kRopeOff + 64 + 16 * g);
+      s.vmask = nx.vmask;
+    };
+
+    // ---- prologue.  q of the row into LDS (each wave an eighth, once per
+    // block) alongside the first three index tiles; then the first two tiles'
+    // records, with index tiles t0+3 and t0+4 queued as if by iterations
+    // t0-2 and t0-1, so every iteration sees the same order of loads:
+    //   ... S(n) | I(n+3) | L(n+1) S(n+1) | I(n+4) ...
+    // (L latent DMA, S side loads, I index DMA of a tile).
+    // index tiles t0 .. t0+2, unless the speculative ones are those
+    if (!pref && !(stride > 0 && beg == beg_g && t0 == t0_g)) {
+      if (stride > 0) wait_vm_all();  // the guessed tiles land before the ring is refilled
+      issue_idx(t0);
+      issue_idx(t0 + 1);
+      issue_idx(t0 + 2);
+    }
+    // wave w loads q heads 2w and 2w+1: chunk c (16 B, 72 per head) of head hh
+    // lands at q_lds + kQRow hh + 16 c; heads >= H are not loaded (their lanes
+    // use zeros).  nq: q DMA instructions this wave issues.
+    const int nq = 2 * ((2 * w < H) + (2 * w + 1 < H));
+    {
+      const uint16_t* qrow = qbase + row * SMLA_P(q_st);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int hh = 2 * w + j;
+        if (hh < H) {
+          const uint16_t* qh = qrow + (int64_t)hh * SMLA_P(q_sh);
+          const uint32_t dst = base + kQOff + kQRow * hh;
+          dma16((const uint8_t*)(qh + 8 * lane), __builtin_amdgcn_readfirstlane(dst));
+          if (lane < 8) dma16((const uint8_t*)(qh + 8 * (64 + lane)), __builtin_amdgcn_readfirstlane(dst + 1024));
+        }
+      }
+    }
+    // this wave's index tiles have landed (its q chunks may still be in flight)
+    if (nq == 4) wait_vm<4>();
+    else if (nq == 2) wait_vm<2>();
+    else wait_vm<0>();
+    Side sA, sB;    // tiles t0, t0+2, ... use sA; t0+1, t0+3, ... sB
+    sA.vmask = fill_table(t0);
+    sB.vmask = (t0 + 1 < t1) ? fill_table(t0 + 1) : 0u;
+    issue_latent(t0, 0);
+    load_side(t0, sA);
+    // Index tiles past the unit's end are never queued (from here on), so
+    // none is left in flight when the block ends.
+    if (t0 + 3 < t1) {
+      issue_idx(t0 + 3);
+      wait_vm<kTileVm + 1>();  // this wave's q chunks have landed (tile t0 and I(t0+3) may not)
+    } else {
+      wait_vm<kTileVm>();
+    }
+    __syncthreads();  // every wave's q chunks have landed
+    // (persistent) the next unit's descriptor, behind this unit's first loads
+    if (MULTI && has_n) ud_n = desc[4 * rank_n + (lane & 3)];
+    // q as bf16 B operands (head = lane column t).  Latent K-step 2m / 2m+1: dims
+    // 64m + 16g + [0..7] / [8..15]; rope K-step i: dims 512 + 32i + 8g + [0..7].
+    v8bf qlat[16];
+    v8bf qrope[2];
+    {
+      const uint32_t qr = base + kQOff + kQRow * t;
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        v4i a = *LDSP(v4i, qr + 2 * (64 * m + 16 * g));
+        v4i b = *LDSP(v4i, qr + 2 * (64 * m + 16 * g + 8));
+        if (!h_ok) a = b = v4i{0, 0, 0, 0};
+        qlat[2 * m] = __builtin_bit_cast(v8bf, a);
+        qlat[2 * m + 1] = __builtin_bit_cast(v8bf, b);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        v4i a = *LDSP(v4i, qr + 2 * (kLat + 32 * i + 8 * g));
+        if (!h_ok) a = v4i{0, 0, 0, 0};
+        qrope[i] = __builtin_bit_cast(v8bf, a);
+      }
+    }
+
+    float m_ref = -INFINITY;  // reference max (log2 units), the same in every wave
+    float l_run = 0.0f;       // head t's sum of P over this lane's tokens (PV side)
+    v4f O[4];                 // O^T slices: dims 64w + 16 dt + 4g + [0..3], head t
+#pragma unroll
+    for (int i = 0; i < 4; ++i) O[i] = v4f{0, 0, 0, 0};
+
+    // QK read addresses: token 16w + t, chunk 4m + g (stored at (4m + g) ^ 8 in odd rows,
+    // i.e. K-step m ^ 2): slices with m & 2 == 0 use qk_a, the others qk_b, + 64 m.
+    const uint32_t qk_row = row_off(16 * w + t) + 16 * g;
+    const uint32_t qk_a = qk_row + ((t & 1) ? 128u : 0u);
+    const uint32_t qk_b = qk_row - ((t & 1) ? 128u : 0u);
+    // PV transposed reads: lane (t, g) loads token 32 k + 8 g + t/2, bytes
+    // 8(t&1) .. +7 of chunk 4w + dt (stored at (4w + dt) ^ 8 in odd rows), so
+    // lane (i, g) receives dim i of tokens 8g .. 8g+7 of K-step k; dt and k are
+    // immediate offsets.
+    const int tv = 8 * g + (t >> 1);
+    const uint32_t pv_off = row_off(tv) + 64 * (w ^ (2 * (tv & 1))) + 8 * (t & 1);
+    const v2h ones = v2h{(_Float16)1.0f, (_Float16)1.0f};
+
+    const uint32_t mx = base + kMxOff;
+    const uint32_t px = base + kPxOff;
+    const uint32_t sx = base + kSxOff;
+    Next nx;
+
+    // One tile: n, its stage st (= (n - t0) & 1) and its side registers.
+    auto tile = [&](int n, int st, Side& sd) __attribute__((always_inline)) {
+      // this wave's records, scales and rope of tile n have landed; the loads
+      // queued after them (I(n+3), tile n+1's, I(n+4), each only if that tile
+      // exists) may still be in flight.  Tile t0 alone is queued by itself
+      // (followed by I(t0+3) only), so that the first records of every block
+      // arrive as early as they can; tile t0+1 follows as soon as they have.
+      const int left = t1 - n;  // tiles left, this one included
+      if (n == t0) {
+        // (after I(t0+3) if queued, and the next unit's descriptor if loaded)
+        if (MULTI && has_n) {
+          if (left >= 4) wait_vm<2>();
+          else wait_vm<1>();
+        } else {
+          if (left >= 4) wait_vm<1>();
+          else wait_vm<0>();
+        }
+        if (left >= 2) {
+          issue_latent(n + 1, st ^ 1);
+          load_side(n + 1, sB);
+        }
+        if (left >= 5) {
+          __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // ring slot t0 was read before I(t0+4) lands in it
+          issue_idx(n + 4);
+        }
+      } else if (left >= 5) {
+        wait_vm<2 + kTileVm>();
+      } else if (left == 4) {
+        wait_vm<1 + kTileVm>();
+      } else if (left >= 2) {
+        wait_vm<kTileVm>();
+      } else {
+        wait_vm<0>();
+      }
+      pin(sd);
+
+      // ---- QK: lane (t, g) gets head t, tokens 16w + 4g + r (own records only)
+      const uint32_t lat = lat_at(st);
+      v4f S;
+      {
+        v4i kr[8];
+#pragma unroll
+        for (int m = 0; m < 8; ++m) kr[m] = *LDSP(v4i, lat + ((m & 2) ? qk_b : qk_a) + 64 * m);
+        // all eight reads are issued before the first conversion waits for one
+        // (left to itself the scheduler issues them in pairs, each pair waited for)
+        __builtin_amdgcn_sched_barrier(0);
+        // two independent accumulation chains (K-steps 2m and 2m+1), summed at the end
+        v4f acc0 = v4f{0, 0, 0, 0}, acc1 = v4f{0, 0, 0, 0};
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, sd.rp0), qrope[0], acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, sd.rp1), qrope[1], acc1, 0, 0, 0);
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          const float sc = sd.ksc[m >> 1];
+          v2bf a0, a1, a2, a3, b0, b1, b2, b3;
+          cvt4_bf16(kr[m].x, sc, a0, a1);
+          cvt4_bf16(kr[m].y, sc, a2, a3);
+          cvt4_bf16(kr[m].z, sc, b0, b1);
+          cvt4_bf16(kr[m].w, sc, b2, b3);
+          const v8bf ka = {a0.x, a0.y, a1.x, a1.y, a2.x, a2.y, a3.x, a3.y};
+          const v8bf kb = {b0.x, b0.y, b1.x, b1.y, b2.x, b2.y, b3.x, b3.y};
+          acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qlat[2 * m], acc0, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qlat[2 * m + 1], acc1, 0, 0, 0);
+        }
+        S = acc0 + acc1;
+      }
+
+      // ---- softmax (log2 domain) of this wave's 16 tokens
+      float x[4];
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        x[r] = ((sd.vmask >> (4 * g + r)) & 1u) ? S[r] * p.c_log2 : -INFINITY;
+        tmax = fmax_(tmax, x[r]);
+      }
+      tmax = xor_max(tmax);
+      if (g == 0) *LDSP(float, mx + 4 * (8 * t + w)) = tmax;
+      // P with the current reference (valid unless some head's max moves it)
+      auto write_p = [&](float m_use) {
+        _Float16 ph[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ph[r] = (_Float16)__builtin_amdgcn_exp2f(x[r] - m_use + kShift);
+        *LDSP(v2i, px + kPRow * t + 2 * (16 * w + 4 * g)) =
+            __builtin_bit_cast(v2i, (v4h{ph[0], ph[1], ph[2], ph[3]}));
+      };
+      write_p(m_ref == -INFINITY ? 0.0f : m_ref);
+      // V scale of block g for token 16w + t, clamped to 2^7, as f16
+      *LDSP(_Float16, sx + kPRow * g + 2 * (16 * w + t)) = (_Float16)__builtin_fminf(sd.ksc[g], kScaleCap);
+      // tile n+2's addresses, while the other waves' records may still be
+      // landing: its index tile was queued before tile n's records (which have
+      // landed), table slot n & 1 was last read by tile n's own loads, and each
+      // wave touches only its own entries of the ring and the table
+      if (left >= 3) prep(n + 2, nx);
+      // every wave's records of tile n have landed (each waited for its own
+      // above) and its P, scales and maxima are written
+      __syncthreads();
+
+      // ---- tile max of head t over all waves (lane group g reads waves 2g, 2g+1);
+      // move the reference if it grew by more than kTau
+      {
+        const v2f mg = *LDSP(v2f, mx + 4 * (8 * t + 2 * g));
+        const float M = xor_max(fmax_(mg.x, mg.y));
+        if (__builtin_amdgcn_ballot_w64(M > m_ref + kTau)) {  // the same decision in every wave
+          const float m_new = fmax_(m_ref, M);
+          const float alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_ref - m_new);
+          if (__builtin_amdgcn_ballot_w64(m_ref != -INFINITY)) {  // O and l are still zero otherwise
+            l_run *= alpha;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) O[i] *= alpha;
+          }
+          m_ref = m_new;
+          write_p(m_ref == -INFINITY ? 0.0f : m_ref);
+          __syncthreads();
+        }
+      }
+
+      // ---- PV: O^T[d, h] += V^T[d, tok] P'^T[tok, h] over the tile's 128 tokens;
+      // l sums the same f16 P (so numerator and denominator share the rounding)
+      // K-step k's reads are issued before K-step k-1's conversions and MFMAs,
+      // so one K-step's LDS latency hides behind the previous one's work.
+      const uint32_t vaddr = lat + pv_off;
+      v8h pr[2], sr[2];
+      v2i vr[2][4];
+      auto pv_load = [&](int k) __attribute__((always_inline)) {
+        const int tok = 32 * k + 8 * g;
+        pr[k & 1] = *LDSP(v8h, px + kPRow * t + 2 * tok);
+        sr[k & 1] = *LDSP(v8h, sx + kPRow * (w >> 1) + 2 * tok);
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+          vr[k & 1][dt] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(LDSP(v2i, vaddr + 16 * kPair * k + 16 * dt));
+      };
+      pv_load(0);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        if (k < 3) pv_load(k + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        const v8h pk = pr[k & 1];
+        const v8h pb = pk * sr[k & 1];
+        l_run = __builtin_amdgcn_fdot2(v2h{pk[0], pk[1]}, ones, l_run, false);
+        l_run = __builtin_amdgcn_fdot2(v2h{pk[2], pk[3]}, ones, l_run, false);
+        l_run = __builtin_amdgcn_fdot2(v2h{pk[4], pk[5]}, ones, l_run, false);
+        l_run = __builtin_amdgcn_fdot2(v2h{pk[6], pk[7]}, ones, l_run, false);
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+          O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(cvt8_f16(vr[k & 1][dt]), pb, O[dt], 0, 0, 0);
+      }
+      if (left == 1) return;  // the last tile: nothing reuses the stage or P
+
+      // every wave is done with stage st, P, the scales and the maxima of tile n
+      __syncthreads();
+
+      // ---- tile n+2 into stage st and this side set, then index tile n+5
+      if (left >= 3) issue_next(nx, st, sd);
+      if (left >= 6) {
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // ring slot n+1 was read (fill_table) before its reload lands
+        issue_idx(n + 5);
+      }
+    };
+
+    for (int n = t0; n < t1; n += 2) {
+      tile(n, 0, sA);
+      if (n + 1 < t1) tile(n + 1, 1, sB);
+    }
+    bool pref_n = false;
+    if (MULTI && has_n) {
+      // every load of this unit and the next unit's descriptor have landed (the
+      // last tile waited for all of them): queue the next unit's first index
+      // tiles, which land during this unit's epilogue
+      wait_vm_all();
+      const int beg_n = __builtin_amdgcn_readlane(ud_n, 1);
+      const int tiles_n = __builtin_amdgcn_readlane(ud_n, 3);
+      const int ct_n = (tiles_n + S - 1) / S;
+      const int t0_n = min(chunk_n * ct_n, tiles_n);
+      pref_n = t0_n < min(t0_n + ct_n, tiles_n);
+      if (pref_n) {
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // this unit's reads of the ring are done before it is refilled
+        issue_idx_at(beg_n, t0_n);
+        issue_idx_at(beg_n, t0_n + 1);
+        issue_idx_at(beg_n, t0_n + 2);
+      }
+    } else {
+      wait_vm_all();  // no DMA may still target LDS when the block ends
+    }
+
+    // ---- epilogue: head t's sum over all tokens, then this wave's 64 dims
+    // (split: a partial without the sink, which the combine folds in)
+    l_run = xor_sum(l_run);
+    const Norm nm = finish_norm(l_run, m_ref, (split || !h_ok) ? -INFINITY : sink_log2(SMLA_P(sink), h));
+    const float inv = nm.scale;
+    const float l2 = nm.lse2;
+    if (w == 0 && g == 0 && h_ok) {
+      if (split) SMLA_P(part_lse)[(int64_t)unit * H + h] = l2;
+      else if (SMLA_P(lse)) SMLA_P(lse)[(int64_t)row * H + h] = l2 * kLn2;
+    }
+    if (split) {
+      if (h_ok) st_part16(SMLA_P(part_o) + ((int64_t)unit * H + h) * kLat + 64 * w, g, O, inv);
+    } else {
+      // bf16 rows staged in this wave's part of the q area (idle after the
+      // prologue), then read back 8 lanes per head, so that each store
+      // instruction writes eight heads' 128 contiguous bytes (the wave's own
+      // LDS writes, which LDS performs in order)
+      const uint32_t ob = base + kQOff + w * (16 * kOutPitch);
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) *LDSP(v2i, ob + kOutPitch * t + 2 * (16 * dt + 4 * g)) = pack_bf16x4(O[dt] * inv);
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int hh = 8 * i + (lane >> 3);
+        const v4i v = *LDSP(v4i, ob + kOutPitch * hh + 16 * (lane & 7));
+        if (hh < H) *(v4i*)(SMLA_P(out) + row * SMLA_P(o_st) + hh * SMLA_P(o_sh) + 64 * w + 8 * (lane & 7)) = v;
+      }
+    }
+    if (!MULTI || !has_n) return;
+    // every wave is past this unit (its stages, P buffers and the q area) before
+    // the next unit's loads land there
+    __syncthreads();
     rank = rank_n;
     chunk = chunk_n;
     have_ud = true;
-    pref = false;
-    continue;
-  }
-
-  const uint8_t* const kv = p.kv;
-  const uint8_t* const zero = p.zero;
-  auto lat_at = [&](int st) -> uint32_t { return base + kLatOff + st * kLatStage; };
-  auto tab_at = [&](int n) -> uint32_t { return base + kTabOff + (n & 1) * kTile * 8; };
-  // Every wave touches only its own 16 entries of the index ring and the
-  // address table, so those need no barrier.
-  auto issue_idx = [&](int n) { issue_idx_at(beg, n); };
-  // record addresses of this wave's tokens of tile n (masked ones: the zero
-  // record); returns the wave's valid-token mask
-  auto fill_table = [&](int n) -> uint32_t {
-    int ix = -1;
-    if (lane < 16) {
-      const int raw = *LDSP(int, ring_at(n) + 4 * (16 * w + lane));
-      ix = (n * kTile + 16 * w + lane < len) ? raw : -1;
-      *LDSP(uint64_t, tab_at(n) + 8 * (16 * w + lane)) =
-          (uint64_t)(uintptr_t)(p.km.valid(ix) ? key_addr(p, ix) : zero);
-    }
-    return (uint32_t)__ballot(lane < 16 && p.km.valid(ix)) & 0xFFFFu;
-  };
-  // latent DMA of this wave's 16 tokens of tile n into stage st: one
-  // instruction per token pair, lanes 0..31 the even token, 32..63 the odd one
-  // (lane position p of the odd row loads chunk p ^ 8).
-  const uint32_t src_chunk = 16u * (uint32_t)((lane & 31) ^ ((lane >> 5) << 3));
-  auto issue_latent = [&](int n, int st) {
-    const uint32_t tab = tab_at(n) + 8 * (16 * w + (lane >> 5));
-    uint64_t a[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) a[i] = *LDSP(uint64_t, tab + 16 * i);
-    const uint32_t dst = lat_at(st) + 8 * w * kPair;
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      dma16((const uint8_t*)(uintptr_t)(a[i] + src_chunk), __builtin_amdgcn_readfirstlane(dst + i * kPair));
-  };
-  auto load_side = [&](int n, Side& s) {
-    const uint64_t rec = *LDSP(uint64_t, tab_at(n) + 8 * (16 * w + t));
-    gload16(s.ksc, rec + kScaleOff);
-    gload16(s.rp0, rec + kRopeOff + 16 * g);
-    gload16(s.rp1, rec + kRopeOff + 64 + 16 * g);
-  };
-  // Tile n's loads with every address already in registers: fill_table(n)
-  // and the table reads run while an earlier tile is processed, so that the
-  // refill after a tile only issues loads.
-  struct Next {
-    uint64_t lat[8];  // latent DMA source rows (issue_latent's a[])
-    uint64_t rec;     // the side loads' record (load_side's rec)
-    uint32_t vmask;
-  };
-  auto prep = [&](int n, Next& nx) {
-    nx.vmask = fill_table(n);
-    const uint32_t tab = tab_at(n) + 8 * (16 * w + (lane >> 5));
-#pragma unroll
-    for (int i = 0; i < 8; ++i) nx.lat[i] = *LDSP(uint64_t, tab + 16 * i);
-    nx.rec = *LDSP(uint64_t, tab_at(n) + 8 * (16 * w + t));
-  };
-  auto issue_next = [&](const Next& nx, int st, Side& s) {
-    const uint32_t dst = lat_at(st) + 8 * w * kPair;
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      dma16((const uint8_t*)(uintptr_t)(nx.lat[i] + src_chunk), __builtin_amdgcn_readfirstlane(dst + i * kPair));
-    gload16(s.ksc, nx.rec + kScaleOff);
-    gload16(s.rp0, nx.rec + kRopeOff + 16 * g);
-    gload16(s.rp1, nx.rec + kRopeOff + 64 + 16 * g);
-    s.vmask = nx.vmask;
-  };
-
-  // ---- prologue.  q of the row into LDS (each wave an eighth, once per
-  // block) alongside the first three index tiles; then the first two tiles'
-  // records, with index tiles t0+3 and t0+4 queued as if by iterations
-  // t0-2 and t0-1, so every iteration sees the same order of loads:
-  //   ... S(n) | I(n+3) | L(n+1) S(n+1) | I(n+4) ...
-  // (L latent DMA, S side loads, I index DMA of a tile).
-  // index tiles t0 .. t0+2, unless the speculative ones are those
-  if (!pref && !(stride > 0 && beg == beg_g && t0 == t0_g)) {
-    if (stride > 0) wait_vm_all();  // the guessed tiles land before the ring is refilled
-    issue_idx(t0);
-    issue_idx(t0 + 1);
-    issue_idx(t0 + 2);
-  }
-  // wave w loads q heads 2w and 2w+1: chunk c (16 B, 72 per head) of head hh
-  // lands at q_lds + kQRow hh + 16 c; heads >= H are not loaded (their lanes
-  // use zeros).  nq: q DMA instructions this wave issues.
-  const int nq = 2 * ((2 * w < H) + (2 * w + 1 < H));
-  {
-    const uint16_t* qrow = qbase + row * SMLA_P(q_st);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int hh = 2 * w + j;
-      if (hh < H) {
-        const uint16_t* qh = qrow + (int64_t)hh * SMLA_P(q_sh);
-        const uint32_t dst = base + kQOff + kQRow * hh;
-        dma16((const uint8_t*)(qh + 8 * lane), __builtin_amdgcn_readfirstlane(dst));
-        if (lane < 8) dma16((const uint8_t*)(qh + 8 * (64 + lane)), __builtin_amdgcn_readfirstlane(dst + 1024));
-      }
-    }
-  }
-  // this wave's index tiles have landed (its q chunks may still be in flight)
-  if (nq == 4) wait_vm<4>();
-  else if (nq == 2) wait_vm<2>();
-  else wait_vm<0>();
-  Side sA, sB;    // tiles t0, t0+2, ... use sA; t0+1, t0+3, ... sB
-  sA.vmask = fill_table(t0);
-  sB.vmask = (t0 + 1 < t1) ? fill_table(t0 + 1) : 0u;
-  issue_latent(t0, 0);
-  load_side(t0, sA);
-  // Index tiles past the unit's end are never queued (from here on), so
-  // none is left in flight when the block ends.
-  if (t0 + 3 < t1) {
-    issue_idx(t0 + 3);
-    wait_vm<kTileVm + 1>();  // this wave's q chunks have landed (tile t0 and I(t0+3) may not)
-  } else {
-    wait_vm<kTileVm>();
-  }
-  __syncthreads();  // every wave's q chunks have landed
-  // (persistent) the next unit's descriptor, behind this unit's first loads
-  if (MULTI && has_n) ud_n = desc[4 * rank_n + (lane & 3)];
-  // q as bf16 B operands (head = lane column t).  Latent K-step 2m / 2m+1: dims
-  // 64m + 16g + [0..7] / [8..15]; rope K-step i: dims 512 + 32i + 8g + [0..7].
-  v8bf qlat[16];
-  v8bf qrope[2];
-  {
-    const uint32_t qr = base + kQOff + kQRow * t;
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      v4i a = *LDSP(v4i, qr + 2 * (64 * m + 16 * g));
-      v4i b = *LDSP(v4i, qr + 2 * (64 * m + 16 * g + 8));
-      if (!h_ok) a = b = v4i{0, 0, 0, 0};
-      qlat[2 * m] = __builtin_bit_cast(v8bf, a);
-      qlat[2 * m + 1] = __builtin_bit_cast(v8bf, b);
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      v4i a = *LDSP(v4i, qr + 2 * (kLat + 32 * i + 8 * g));
-      if (!h_ok) a = v4i{0, 0, 0, 0};
-      qrope[i] = __builtin_bit_cast(v8bf, a);
-    }
-  }
-
-  float m_ref = -INFINITY;  // reference max (log2 units), the same in every wave
-  float l_run = 0.0f;       // head t's sum of P over this lane's tokens (PV side)
-  v4f O[4];                 // O^T slices: dims 64w + 16 dt + 4g + [0..3], head t
-#pragma unroll
-  for (int i = 0; i < 4; ++i) O[i] = v4f{0, 0, 0, 0};
-
-  // QK read addresses: token 16w + t, chunk 4m + g (stored at (4m + g) ^ 8 in odd rows,
-  // i.e. K-step m ^ 2): slices with m & 2 == 0 use qk_a, the others qk_b, + 64 m.
-  const uint32_t qk_row = row_off(16 * w + t) + 16 * g;
-  const uint32_t qk_a = qk_row + ((t & 1) ? 128u : 0u);
-  const uint32_t qk_b = qk_row - ((t & 1) ? 128u : 0u);
-  // PV transposed reads: lane (t, g) loads token 32 k + 8 g + t/2, bytes
-  // 8(t&1) .. +7 of chunk 4w + dt (stored at (4w + dt) ^ 8 in odd rows), so
-  // lane (i, g) receives dim i of tokens 8g .. 8g+7 of K-step k; dt and k are
-  // immediate offsets.
-  const int tv = 8 * g + (t >> 1);
-  const uint32_t pv_off = row_off(tv) + 64 * (w ^ (2 * (tv & 1))) + 8 * (t & 1);
-  const v2h ones = v2h{(_Float16)1.0f, (_Float16)1.0f};
-
-  const uint32_t mx = base + kMxOff;
-  const uint32_t px = base + kPxOff;
-  const uint32_t sx = base + kSxOff;
-  Next nx;
-
-  // One tile: n, its stage st (= (n - t0) & 1) and its side registers.
-  auto tile = [&](int n, int st, Side& sd) __attribute__((always_inline)) {
-    // this wave's records, scales and rope of tile n have landed; the loads
-    // queued after them (I(n+3), tile n+1's, I(n+4), each only if that tile
-    // exists) may still be in flight.  Tile t0 alone is queued by itself
-    // (followed by I(t0+3) only), so that the first records of every block
-    // arrive as early as they can; tile t0+1 follows as soon as they have.
-    const int left = t1 - n;  // tiles left, this one included
-    if (n == t0) {
-      // (after I(t0+3) if queued, and the next unit's descriptor if loaded)
-      if (MULTI && has_n) {
-        if (left >= 4) wait_vm<2>();
-        else wait_vm<1>();
-      } else {
-        if (left >= 4) wait_vm<1>();
-        else wait_vm<0>();
-      }
-      if (left >= 2) {
-        issue_latent(n + 1, st ^ 1);
-        load_side(n + 1, sB);
-      }
-      if (left >= 5) {
-        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // ring slot t0 was read before I(t0+4) lands in it
-        issue_idx(n + 4);
-      }
-    } else if (left >= 5) {
-      wait_vm<2 + kTileVm>();
-    } else if (left == 4) {
-      wait_vm<1 + kTileVm>();
-    } else if (left >= 2) {
-      wait_vm<kTileVm>();
-    } else {
-      wait_vm<0>();
-    }
-    pin(sd);
-
-    // ---- QK: lane (t, g) gets head t, tokens 16w + 4g + r (own records only)
-    const uint32_t lat = lat_at(st);
-    v4f S;
-    {
-      v4i kr[8];
-#pragma unroll
-      for (int m = 0; m < 8; ++m) kr[m] = *LDSP(v4i, lat + ((m & 2) ? qk_b : qk_a) + 64 * m);
-      // all eight reads are issued before the first conversion waits for one
-      // (left to itself the scheduler issues them in pairs, each pair waited for)
-      __builtin_amdgcn_sched_barrier(0);
-      // two independent accumulation chains (K-steps 2m and 2m+1), summed at the end
-      v4f acc0 = v4f{0, 0, 0, 0}, acc1 = v4f{0, 0, 0, 0};
-      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, sd.rp0), qrope[0], acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, sd.rp1), qrope[1], acc1, 0, 0, 0);
-#pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        const float sc = sd.ksc[m >> 1];
-        v2bf a0, a1, a2, a3, b0, b1, b2, b3;
-        cvt4_bf16(kr[m].x, sc, a0, a1);
-        cvt4_bf16(kr[m].y, sc, a2, a3);
-        cvt4_bf16(kr[m].z, sc, b0, b1);
-        cvt4_bf16(kr[m].w, sc, b2, b3);
-        const v8bf ka = {a0.x, a0.y, a1.x, a1.y, a2.x, a2.y, a3.x, a3.y};
-        const v8bf kb = {b0.x, b0.y, b1.x, b1.y, b2.x, b2.y, b3.x, b3.y};
-        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qlat[2 * m], acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qlat[2 * m + 1], acc1, 0, 0, 0);
-      }
-      S = acc0 + acc1;
-    }
-
-    // ---- softmax (log2 domain) of this wave's 16 tokens
-    float x[4];
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      x[r] = ((sd.vmask >> (4 * g + r)) & 1u) ? S[r] * p.c_log2 : -INFINITY;
-      tmax = fmax_(tmax, x[r]);
-    }
-    tmax = xor_max(tmax);
-    if (g == 0) *LDSP(float, mx + 4 * (8 * t + w)) = tmax;
-    // P with the current reference (valid unless some head's max moves it)
-    auto write_p = [&](float m_use) {
-      _Float16 ph[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) ph[r] = (_Float16)__builtin_amdgcn_exp2f(x[r] - m_use + kShift);
-      *LDSP(v2i, px + kPRow * t + 2 * (16 * w + 4 * g)) =
-          __builtin_bit_cast(v2i, (v4h{ph[0], ph[1], ph[2], ph[3]}));
-    };
-    write_p(m_ref == -INFINITY ? 0.0f : m_ref);
-    // V scale of block g for token 16w + t, clamped to 2^7, as f16
-    *LDSP(_Float16, sx + kPRow * g + 2 * (16 * w + t)) = (_Float16)__builtin_fminf(sd.ksc[g], kScaleCap);
-    // tile n+2's addresses, while the other waves' records may still be
-    // landing: its index tile was queued before tile n's records (which have
-    // landed), table slot n & 1 was last read by tile n's own loads, and each
-    // wave touches only its own entries of the ring and the table
-    if (left >= 3) prep(n + 2, nx);
-    // every wave's records of tile n have landed (each waited for its own
-    // above) and its P, scales and maxima are written
-    __syncthreads();
-
-    // ---- tile max of head t over all waves (lane group g reads waves 2g, 2g+1);
-    // move the reference if it grew by more than kTau
-    {
-      const v2f mg = *LDSP(v2f, mx + 4 * (8 * t + 2 * g));
-      const float M = xor_max(fmax_(mg.x, mg.y));
-      if (__builtin_amdgcn_ballot_w64(M > m_ref + kTau)) {  // the same decision in every wave
-        const float m_new = fmax_(m_ref, M);
-        const float alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_ref - m_new);
-        if (__builtin_amdgcn_ballot_w64(m_ref != -INFINITY)) {  // O and l are still zero otherwise
-          l_run *= alpha;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) O[i] *= alpha;
-        }
-        m_ref = m_new;
-        write_p(m_ref == -INFINITY ? 0.0f : m_ref);
-        __syncthreads();
-      }
-    }
-
-    // ---- PV: O^T[d, h] += V^T[d, tok] P'^T[tok, h] over the tile's 128 tokens;
-    // l sums the same f16 P (so numerator and denominator share the rounding)
-    // K-step k's reads are issued before K-step k-1's conversions and MFMAs,
-    // so one K-step's LDS latency hides behind the previous one's work.
-    const uint32_t vaddr = lat + pv_off;
-    v8h pr[2], sr[2];
-    v2i vr[2][4];
-    auto pv_load = [&](int k) __attribute__((always_inline)) {
-      const int tok = 32 * k + 8 * g;
-      pr[k & 1] = *LDSP(v8h, px + kPRow * t + 2 * tok);
-      sr[k & 1] = *LDSP(v8h, sx + kPRow * (w >> 1) + 2 * tok);
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-        vr[k & 1][dt] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(LDSP(v2i, vaddr + 16 * kPair * k + 16 * dt));
-    };
-    pv_load(0);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      if (k < 3) pv_load(k + 1);
-      __builtin_amdgcn_sched_barrier(0);
-      const v8h pk = pr[k & 1];
-      const v8h pb = pk * sr[k & 1];
-      l_run = __builtin_amdgcn_fdot2(v2h{pk[0], pk[1]}, ones, l_run, false);
-      l_run = __builtin_amdgcn_fdot2(v2h{pk[2], pk[3]}, ones, l_run, false);
-      l_run = __builtin_amdgcn_fdot2(v2h{pk[4], pk[5]}, ones, l_run, false);
-      l_run = __builtin_amdgcn_fdot2(v2h{pk[6], pk[7]}, ones, l_run, false);
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-        O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(cvt8_f16(vr[k & 1][dt]), pb, O[dt], 0, 0, 0);
-    }
-    if (left == 1) return;  // the last tile: nothing reuses the stage or P
-
-    // every wave is done with stage st, P, the scales and the maxima of tile n
-    __syncthreads();
-
-    // ---- tile n+2 into stage st and this side set, then index tile n+5
-    if (left >= 3) issue_next(nx, st, sd);
-    if (left >= 6) {
-      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // ring slot n+1 was read (fill_table) before its reload lands
-      issue_idx(n + 5);
-    }
-  };
-
-  for (int n = t0; n < t1; n += 2) {
-    tile(n, 0, sA);
-    if (n + 1 < t1) tile(n + 1, 1, sB);
-  }
-  bool pref_n = false;
-  if (MULTI && has_n) {
-    // every load of this unit and the next unit's descriptor have landed (the
-    // last tile waited for all of them): queue the next unit's first index
-    // tiles, which land during this unit's epilogue
-    wait_vm_all();
-    const int beg_n = __builtin_amdgcn_readlane(ud_n, 1);
-    const int tiles_n = __builtin_amdgcn_readlane(ud_n, 3);
-    const int ct_n = (tiles_n + S - 1) / S;
-    const int t0_n = min(chunk_n * ct_n, tiles_n);
-    pref_n = t0_n < min(t0_n + ct_n, tiles_n);
-    if (pref_n) {
-      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // this unit's reads of the ring are done before it is refilled
-      issue_idx_at(beg_n, t0_n);
-      issue_idx_at(beg_n, t0_n + 1);
-      issue_idx_at(beg_n, t0_n + 2);
-    }
-  } else {
-    wait_vm_all();  // no DMA may still target LDS when the block ends
-  }
-
-  // ---- epilogue: head t's sum over all tokens, then this wave's 64 dims
-  // (split: a partial without the sink, which the combine folds in)
-  l_run = xor_sum(l_run);
-  const Norm nm = finish_norm(l_run, m_ref, (split || !h_ok) ? -INFINITY : sink_log2(SMLA_P(sink), h));
-  const float inv = nm.scale;
-  const float l2 = nm.lse2;
-  if (w == 0 && g == 0 && h_ok) {
-    if (split) SMLA_P(part_lse)[(int64_t)unit * H + h] = l2;
-    else if (SMLA_P(lse)) SMLA_P(lse)[(int64_t)row * H + h] = l2 * kLn2;
-  }
-  if (split) {
-    if (h_ok) st_part16(SMLA_P(part_o) + ((int64_t)unit * H + h) * kLat + 64 * w, g, O, inv);
-  } else {
-    // bf16 rows staged in this wave's part of the q area (idle after the
-    // prologue), then read back 8 lanes per head, so that each store
-    // instruction writes eight heads' 128 contiguous bytes (the wave's own
-    // LDS writes, which LDS performs in order)
-    const uint32_t ob = base + kQOff + w * (16 * kOutPitch);
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) *LDSP(v2i, ob + kOutPitch * t + 2 * (16 * dt + 4 * g)) = pack_bf16x4(O[dt] * inv);
-    asm volatile("" ::: "memory");
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int hh = 8 * i + (lane >> 3);
-      const v4i v = *LDSP(v4i, ob + kOutPitch * hh + 16 * (lane & 7));
-      if (hh < H) *(v4i*)(SMLA_P(out) + row * SMLA_P(o_st) + hh * SMLA_P(o_sh) + 64 * w + 8 * (lane & 7)) = v;
-    }
-  }
-  if (!MULTI || !has_n) return;
-  // every wave is past this unit (its stages, P buffers and the q area) before
-  // the next unit's loads land there
-  __syncthreads();
-  rank = rank_n;
-  chunk = chunk_n;
-  have_ud = true;
-  pref = pref_n;
+    pref = pref_n;
   }  // units
 #undef SMLA_P
 }
