@@ -625,13 +625,16 @@ def bench_cache_write(args, torch, smla, dev) -> int:
 def _fwd_kernel_name(H: int, T: int, S: int, planned: bool) -> str:
     """The forward kernel the library launches for H heads (contiguous cache).
     With the plan and more blocks than whole XCDs of compute units, the 16-head
-    and wide-head kernels run their persistent-grid instances."""
+    (up to two blocks per CU) and wide-head kernels run their persistent-grid
+    instances."""
     if 16 < H <= 32:
         return "smla_fwdw_kernel<2>"
     import torch
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     blocks = 8 * ((T + 7) // 8) * S * ((H + 63) // 64)
-    persistent = "true" if planned and blocks > (cus // 8) * 8 else "false"
+    grid = (cus // 8) * 8
+    # (the 16-head kernel takes the persistent grid only up to two units per CU)
+    persistent = "true" if planned and blocks > grid and (H > 16 or blocks <= 2 * grid) else "false"
     if H <= 16:
         return f"smla_fwd16_kernel<{persistent}>"
     return f"smla_fwdw64_kernel<false, {persistent}>"

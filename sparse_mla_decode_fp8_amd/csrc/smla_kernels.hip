@@ -952,8 +952,10 @@ hipError_t launch_fwd(const FwdParams& p, Events ev, hipStream_t s) {
     case 1: {
       const int64_t blocks = fwd_grid(p.T, p.S, p.order == nullptr);
       // with the plan and more units than the persistent grid (p.persist
-      // blocks, one per CU), the persistent kernel; otherwise one unit per block
-      if (p.persist > 0 && p.desc != nullptr && blocks > p.persist)
+      // blocks, one per CU) but at most two per block, the persistent kernel;
+      // otherwise one unit per block (with more units per CU the hardware's
+      // dispatch of blocks as CUs free up balances ragged rows better)
+      if (p.persist > 0 && p.desc != nullptr && blocks > p.persist && blocks <= 2 * (int64_t)p.persist)
         hipExtLaunchKernelGGL(smla_fwd16_kernel<true>, dim3((unsigned)p.persist), dim3(n16::kThreads), 0, s,
                               ev.start, ev.stop, 0, p.indptr, p.indices, p.q, p.desc, p.T, p.S, p.idx_bytes, p.stride, p);
       else
