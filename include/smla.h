@@ -372,9 +372,10 @@ const char* sparse_mla_last_error(void);
  *   "plan"   the plan kernels (has_invalid scan, longest-first order):
  *            0 = automatic (when units outnumber compute units), 1 = never
  *            (each forward block scans its own slice), 2 = always.
- *   "persist" with the plan and more units than compute units, the kernels
- *            for up to 16 and for 33 to 128 heads run a grid of one block per
- *            compute unit, each block taking several units in turn:
+ *   "persist" with the plan and more units than compute units (for up to 16
+ *            heads, at most twice as many), the kernels for up to 16 and for
+ *            33 to 128 heads run a grid of one block per compute unit, each
+ *            block taking several units in turn:
  *            0 = automatic, 1 = one unit per block always.  Results are the
  *            same either way.
  * Returns SMLA_OK or SMLA_EINVAL for an unknown name or value.
